@@ -1,0 +1,206 @@
+"""Sequence splits, the causal work model, the ring loops and the Ulysses
+all-to-all, restated on P virtual ranks in one process (numpy, float64).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Sources, all on the handbook page "上下文并行：Ring Attention 与 Ulysses"
+(Context parallelism: Ring Attention and Ulysses):
+
+* section "Ring Attention：KV 沿环传一圈": rank r owns rows
+  [r*C, (r+1)*C) with C = S/P; at step t it holds the KV block of rank
+  src = (r - t) mod P, computes only when src <= r, merges with the
+  log-sum-exp rule and passes the block to rank r+1;
+* section "之字形切分" (zigzag split): the sequence is cut into 2P chunks,
+  rank r takes chunks r and 2P-1-r; the contiguous split of the same
+  snippet gives rank r chunks 2r and 2r+1; the work of a query chunk q is
+  q + 1/2 KV chunks (the diagonal chunk counts half);
+* section "Ulysses：在序列和头之间转置": seq_to_head and head_to_seq are
+  a reshape/transpose followed by ``all_to_all_single``.
+
+Readings where the page is silent (the page has no zigzag ring code):
+
+* zigzag ring -- rank r's local rows are [chunk r, chunk 2P-1-r] in that
+  order, its KV block is the same two chunks, src = (r - t) mod P as in
+  the contiguous ring, and every (query chunk, key chunk) pair is
+  skipped when the key chunk comes after the query chunk, computed with
+  the causal mask when they are the same chunk, and computed in full
+  when the key chunk comes first.
+* plan order -- for each rank, each step, each query chunk in local
+  order, each key chunk in local order.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import attention, lse_merge
+
+CONTIGUOUS, ZIGZAG = 0, 1
+SKIP, FULL, DIAG = 0, 1, 2
+
+
+# ----------------------------------------------------------------- splits
+def split_contiguous(P: int) -> dict[int, list[int]]:
+    """Zigzag-section snippet: contiguous split in 2P chunks, rank r gets [2r, 2r+1]."""
+    return {r: [2 * r, 2 * r + 1] for r in range(P)}
+
+
+def split_zigzag(P: int) -> dict[int, list[int]]:
+    """Zigzag-section snippet: rank r gets chunk r and chunk 2P-1-r."""
+    return {r: [r, 2 * P - 1 - r] for r in range(P)}
+
+
+def work(query_chunks) -> float:
+    """Zigzag-section work model: a query chunk with index q needs q full KV
+    chunks plus the diagonal one, which counts half."""
+    return sum(q + 0.5 for q in query_chunks)
+
+
+def layout_index(layout: int, S: int, P: int, rank: int) -> np.ndarray:
+    """Natural sequence position of each local row of ``rank``.
+
+    Contiguous: the ring section's ``slice(rank*C, (rank+1)*C)``.
+    Zigzag: the 2P-chunk split, chunks concatenated in the order listed.
+    """
+    if layout == CONTIGUOUS:
+        C = S // P
+        return np.arange(rank * C, (rank + 1) * C, dtype=np.int64)
+    C = S // (2 * P)
+    return np.concatenate([np.arange(c * C, (c + 1) * C, dtype=np.int64)
+                           for c in split_zigzag(P)[rank]])
+
+
+def _chunks(layout: int, S: int, P: int, rank: int):
+    """(chunk ids, chunk length) of ``rank`` for the ring schedule."""
+    if layout == CONTIGUOUS:
+        return [rank], S // P
+    return split_zigzag(P)[rank], S // (2 * P)
+
+
+def ring_plan(S: int, P: int, layout: int, rank: int, causal: bool = True):
+    """Every (rank, step, q_chunk, k_chunk) pair of the ring, classified.
+
+    Returns a list of tuples (rank, step, q_chunk, k_chunk, q_offset,
+    k_offset, len_q, len_k, kind) with kind SKIP / FULL / DIAG.  rank=-1
+    lists all ranks.
+    """
+    ranks = range(P) if rank < 0 else [rank]
+    pairs = []
+    for r in ranks:
+        q_chunks, C = _chunks(layout, S, P, r)
+        for t in range(P):
+            src = (r - t) % P
+            k_chunks, _ = _chunks(layout, S, P, src)
+            for qc in q_chunks:
+                for kc in k_chunks:
+                    if not causal or kc < qc:
+                        kind = FULL
+                    elif kc == qc:
+                        kind = DIAG
+                    else:
+                        kind = SKIP
+                    pairs.append((r, t, qc, kc, qc * C, kc * C, C, C, kind))
+    return pairs
+
+
+# ---------------------------------------------------------------- the ring
+def ring_contiguous(q, k, v, P: int, causal: bool = True):
+    """The ring section's loop, run for every virtual rank in turn.
+
+    Returns (outs, lses, computed): per rank its local out [C, Hq, D],
+    lse [Hq, C] and the number of KV blocks it actually computed.
+    """
+    S = q.shape[0]
+    C = S // P
+    outs, lses, computed = [], [], []
+    blocks = [(k[r * C:(r + 1) * C], v[r * C:(r + 1) * C]) for r in range(P)]
+    for rank in range(P):
+        q_l = q[rank * C:(rank + 1) * C]
+        out = lse = None
+        n = 0
+        src = rank
+        for step in range(P):
+            if src <= rank or not causal:
+                kb, vb = blocks[src]          # the block that arrived this step
+                o, l = attention(q_l, kb, vb, causal=causal,
+                                 q_offset=rank * C, k_offset=src * C)
+                if out is None:
+                    out, lse = o, l
+                else:
+                    out, lse = lse_merge(out, lse, o, l)
+                n += 1
+            src = (src - 1) % P               # receive from the left
+        outs.append(out)
+        lses.append(lse)
+        computed.append(n)
+    return outs, lses, computed
+
+
+def ring_zigzag(q, k, v, P: int, causal: bool = True):
+    """Zigzag ring (reading stated in the module docstring).
+
+    Returns (outs, lses, units): per rank its local out [2C, Hq, D] in the
+    order [chunk r, chunk 2P-1-r], lse [Hq, 2C], and the work units it
+    computed at each step (full pair = 1, diagonal pair = 1/2).
+    """
+    S, Hq, D = q.shape
+    C = S // (2 * P)
+    split = split_zigzag(P)
+    outs, lses, units = [], [], []
+    for rank in range(P):
+        state = {}
+        per_step = []
+        for step in range(P):
+            src = (rank - step) % P
+            u = 0.0
+            for qc in split[rank]:
+                for kc in split[src]:
+                    if causal and kc > qc:
+                        continue
+                    o, l = attention(q[qc * C:(qc + 1) * C], k[kc * C:(kc + 1) * C],
+                                     v[kc * C:(kc + 1) * C], causal=causal,
+                                     q_offset=qc * C, k_offset=kc * C)
+                    state[qc] = (o, l) if qc not in state else lse_merge(*state[qc], o, l)
+                    u += 0.5 if (causal and kc == qc) else 1.0
+            per_step.append(u)
+        outs.append(np.concatenate([state[c][0] for c in split[rank]], axis=0))
+        lses.append(np.concatenate([state[c][1] for c in split[rank]], axis=1))
+        units.append(per_step)
+    return outs, lses, units
+
+
+# ---------------------------------------------------------------- Ulysses
+def all_to_all(sendbufs):
+    """``all_to_all_single`` over P virtual ranks: block p of rank r's send
+    buffer becomes block r of rank p's receive buffer."""
+    P = len(sendbufs)
+    return [np.stack([sendbufs[r][p] for r in range(P)]) for p in range(P)]
+
+
+def seq_to_head(local_x, P: int):
+    """Ulysses section: every rank's [S/P, H, D] -> every rank's [S, H/P, D]."""
+    Sl, H, D = local_x[0].shape
+    sends = [x.reshape(Sl, P, H // P, D).transpose(1, 0, 2, 3) for x in local_x]
+    return [r.reshape(P * Sl, H // P, D) for r in all_to_all(sends)]
+
+
+def head_to_seq(head_x, P: int):
+    """Ulysses section: every rank's [S, H/P, D] -> every rank's [S/P, H, D]."""
+    S, Hp, D = head_x[0].shape
+    sends = [y.reshape(P, S // P, Hp, D) for y in head_x]
+    return [r.transpose(1, 0, 2, 3).reshape(S // P, P * Hp, D) for r in all_to_all(sends)]
+
+
+def ulysses_attention(q, k, v, P: int, causal: bool = True):
+    """Ulysses on P virtual ranks: split rows, seq_to_head q, k, v, local
+    full-sequence attention on each rank's head share, head_to_seq.
+    Returns (per-rank local outputs, per-rank attention-time q shapes)."""
+    q, k, v = (np.asarray(x, dtype=np.float64) if not hasattr(x, "detach")
+               else x.detach().double().numpy() for x in (q, k, v))
+    S = q.shape[0]
+    C = S // P
+    rows = [slice(r * C, (r + 1) * C) for r in range(P)]
+    ql = seq_to_head([q[s] for s in rows], P)
+    kl = seq_to_head([k[s] for s in rows], P)
+    vl = seq_to_head([v[s] for s in rows], P)
+    out_heads = [attention(ql[p], kl[p], vl[p], causal=causal)[0] for p in range(P)]
+    return head_to_seq(out_heads, P), [x.shape for x in ql]

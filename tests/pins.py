@@ -1,0 +1,205 @@
+"""Pins: checks that tie the oracle to facts other than itself.
+
+Each function takes the implementation under test (so that the mutation
+tests can hand in deliberately broken copies) and raises AssertionError
+when a fact fails.  Facts used:
+
+* brute force over pure-Python loops, normalising exp(s_j) by their plain
+  sum (no max shift, no log-sum-exp route);
+* closed forms: with q = 0 every visible score is 0, so lse = ln(n) and
+  out is the mean of the visible v rows; with one key, out = v_0 and
+  lse = q.k/sqrt(D); with v = 1 every non-empty row's out is 1;
+* a library special case: ``torch.nn.functional.scaled_dot_product_attention``
+  (float64, CPU) for offsets 0, causal or not, with GQA heads;
+* the merge identity over disjoint key sets and the global-max route of
+  the "Sequence Parallel vs Context Parallel" blog, section 3.2;
+* the values fixed by the handbook page "上下文并行：Ring Attention 与
+  Ulysses": work per rank, KV blocks per rank, Ulysses shapes (text
+  fixtures under tests/golden with their citations).
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name: str) -> dict[str, list[float]]:
+    vals = {}
+    with open(os.path.join(GOLDEN, name), encoding="utf-8") as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *nums = line.split()
+            vals[key] = [float(x) for x in nums]
+    return vals
+
+
+# Set to np.float32 to round every random input to float32 first, so that an
+# implementation that reads float32 inputs sees exactly the pins' numbers.
+ROUND_INPUTS = None
+
+
+def rand(shape, seed):
+    x = np.random.default_rng(seed).standard_normal(shape)
+    return x if ROUND_INPUTS is None else x.astype(ROUND_INPUTS).astype(np.float64)
+
+
+# ----------------------------------------------------------- brute force
+def brute_force(q, k, v, causal, q_offset, k_offset):
+    """Pure-Python loops: p_j = exp(s_j) / sum_j exp(s_j) over visible j."""
+    Sq, Hq, D = q.shape
+    Sk, Hkv, _ = k.shape
+    group = Hq // Hkv
+    out = [[[0.0] * D for _ in range(Hq)] for _ in range(Sq)]
+    lse = [[-math.inf] * Sq for _ in range(Hq)]
+    for h in range(Hq):
+        g = h // group
+        for i in range(Sq):
+            e = []
+            for j in range(Sk):
+                if causal and k_offset + j > q_offset + i:
+                    continue
+                s = sum(float(q[i, h, d]) * float(k[j, g, d]) for d in range(D)) / math.sqrt(D)
+                e.append((j, math.exp(s)))
+            if not e:
+                continue
+            z = math.fsum(w for _, w in e)
+            lse[h][i] = math.log(z)
+            for d in range(D):
+                out[i][h][d] = math.fsum(w / z * float(v[j, g, d]) for j, w in e)
+    return np.array(out), np.array(lse)
+
+
+def pin_brute_force(attn, cases=None):
+    cases = cases or [
+        # Sq, Sk, Hq, Hkv, D, causal, q_offset, k_offset
+        (5, 7, 2, 1, 3, True, 4, 0),
+        (6, 6, 2, 2, 4, True, 0, 0),
+        (4, 9, 4, 2, 2, True, 3, 5),
+        (3, 5, 1, 1, 5, False, 0, 0),
+        (4, 4, 2, 1, 3, True, 0, 2),     # first rows see no key
+    ]
+    for n, (Sq, Sk, Hq, Hkv, D, causal, qo, ko) in enumerate(cases):
+        q, k, v = rand((Sq, Hq, D), 3 * n), rand((Sk, Hkv, D), 3 * n + 1), rand((Sk, Hkv, D), 3 * n + 2)
+        o, l = attn(q, k, v, causal=causal, q_offset=qo, k_offset=ko)
+        ob, lb = brute_force(q, k, v, causal, qo, ko)
+        np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+        assert np.array_equal(np.isinf(l), np.isinf(lb))
+        np.testing.assert_allclose(np.where(np.isinf(lb), 0, l), np.where(np.isinf(lb), 0, lb),
+                                   rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------- closed forms
+def pin_zero_query(attn):
+    """q = 0: lse_i = ln n_i, out_i = mean of visible v_j, n_i = number visible."""
+    for (Sq, Sk, qo, ko, Hq, Hkv) in [(6, 9, 3, 1, 2, 1), (8, 8, 0, 0, 4, 2), (5, 4, 0, 3, 2, 2)]:
+        D = 3
+        q = np.zeros((Sq, Hq, D))
+        k, v = rand((Sk, Hkv, D), 11), rand((Sk, Hkv, D), 12)
+        o, l = attn(q, k, v, causal=True, q_offset=qo, k_offset=ko)
+        group = Hq // Hkv
+        for i in range(Sq):
+            n = min(max(qo + i - ko + 1, 0), Sk)
+            for h in range(Hq):
+                if n == 0:
+                    assert l[h, i] == -np.inf and np.all(o[i, h] == 0)
+                else:
+                    assert abs(l[h, i] - math.log(n)) < 1e-12
+                    np.testing.assert_allclose(o[i, h], v[:n, h // group].mean(axis=0), atol=1e-12)
+
+
+def pin_ones_value(attn):
+    Sq, Sk, D = 7, 10, 4
+    q, k = rand((Sq, 2, D), 21), rand((Sk, 2, D), 22)
+    o, l = attn(q, k, np.ones((Sk, 2, D)), causal=True, q_offset=2, k_offset=0)
+    np.testing.assert_allclose(o, 1.0, atol=1e-12)
+
+
+def pin_single_key(attn):
+    D = 5
+    q, k, v = rand((3, 2, D), 31), rand((1, 2, D), 32), rand((1, 2, D), 33)
+    o, l = attn(q, k, v, causal=True, q_offset=7, k_offset=7)
+    for h in range(2):
+        for i in range(3):
+            np.testing.assert_allclose(o[i, h], v[0, h], atol=1e-12)
+            assert abs(l[h, i] - float(q[i, h] @ k[0, h]) / math.sqrt(D)) < 1e-12
+
+
+def pin_sdpa(attn):
+    """Offsets 0: torch's scaled_dot_product_attention in float64 on the CPU
+    (its is_causal mask is the lower triangle including the diagonal; its
+    enable_gqa maps query head h to KV head h // (Hq/Hkv))."""
+    import torch.nn.functional as F
+    for causal in (True, False):
+        for (S, Hq, Hkv, D) in [(9, 4, 2, 8), (16, 2, 2, 16)]:
+            q, k, v = rand((S, Hq, D), 41), rand((S, Hkv, D), 42), rand((S, Hkv, D), 43)
+            o, _ = attn(q, k, v, causal=causal)
+            tq, tk, tv = (torch.from_numpy(x).permute(1, 0, 2).unsqueeze(0) for x in (q, k, v))
+            ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                 enable_gqa=(Hq != Hkv))
+            np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+# ----------------------------------------------------------------- merge
+def pin_merge_identity(attn, merge):
+    """attn over K1 u K2 == merge(attn over K1, attn over K2), both orders,
+    and associativity over three parts; -inf parts are the identity."""
+    Sq, Sk, H, D, qo = 6, 12, 2, 4, 8
+    q, k, v = rand((Sq, H, D), 51), rand((Sk, H, D), 52), rand((Sk, H, D), 53)
+    full = attn(q, k, v, causal=True, q_offset=qo, k_offset=0)
+    cuts = [0, 4, 9, Sk]
+    parts = [attn(q, k[a:b], v[a:b], causal=True, q_offset=qo, k_offset=a)
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    for (x, y) in [(0, 1), (1, 0)]:
+        m = merge(*parts[x], *parts[y])
+        ref = attn(q, k[:9], v[:9], causal=True, q_offset=qo, k_offset=0)
+        np.testing.assert_allclose(m[0], ref[0], atol=1e-12)
+        np.testing.assert_allclose(m[1], ref[1], atol=1e-12)
+    left = merge(*merge(*parts[0], *parts[1]), *parts[2])
+    right = merge(*parts[0], *merge(*parts[1], *parts[2]))
+    for res in (left, right):
+        np.testing.assert_allclose(res[0], full[0], atol=1e-12)
+        np.testing.assert_allclose(res[1], full[1], atol=1e-12)
+    # a part whose keys all lie after every query: lse = -inf, identity of the merge
+    empty = attn(q, k[:3], v[:3], causal=True, q_offset=0, k_offset=100)
+    assert np.all(np.isneginf(empty[1])) and np.all(empty[0] == 0)
+    res = merge(*empty, *full)
+    np.testing.assert_allclose(res[0], full[0], atol=0)
+    np.testing.assert_allclose(res[1], full[1], atol=0)
+    both = merge(*empty, *empty)
+    assert np.all(np.isneginf(both[1])) and np.all(both[0] == 0)
+
+
+def pin_global_max_route(attn, global_max_attn):
+    Sq, Sk, H, D = 7, 11, 2, 3
+    q, k, v = rand((Sq, H, D), 61), rand((Sk, H, D), 62), rand((Sk, H, D), 63)
+    parts = [np.arange(0, 3), np.arange(3, 8), np.arange(8, 11)]
+    a = attn(q, k, v, causal=True, q_offset=4, k_offset=0)
+    b = global_max_attn(q, k, v, parts, causal=True, q_offset=4, k_offset=0)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-12)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-12)
+
+
+# ----------------------------------------------------------- schedules
+def pin_work(split_contiguous, split_zigzag, work):
+    g = load_golden("work_p4.txt")
+    P = 4
+    assert [work(split_contiguous(P)[r]) for r in range(P)] == g["contiguous"]
+    assert [work(split_zigzag(P)[r]) for r in range(P)] == g["zigzag"]
+    # every chunk owned exactly once by the splits
+    for split in (split_contiguous, split_zigzag):
+        for PP in (2, 4, 8):
+            owned = sorted(c for r in range(PP) for c in split(PP)[r])
+            assert owned == list(range(2 * PP))
+
+
+def make_qkv_page():
+    """The handbook's make_qkv(): manual_seed(0), then randn(32, 8, 16) x3."""
+    torch.manual_seed(0)
+    return torch.randn(32, 8, 16), torch.randn(32, 8, 16), torch.randn(32, 8, 16)

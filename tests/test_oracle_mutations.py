@@ -1,0 +1,215 @@
+"""Planted mistakes: every plausible slip in the oracle must fail a pin.
+
+Each case rewrites one spot of the oracle's own source (a dropped term, a
+wrong sign or index, a swapped operand, a shifted mask), loads the mutated
+copy on the CPU and runs the pins against it.  The test passes when at
+least one pin rejects the mutant; a mutant that every pin accepts would
+mean the pins cannot tell that mistake from the real definition.
+"""
+import os
+import sys
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import pins
+from oracle import native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _load_mutant(relpath, old, new, modname):
+    src = open(os.path.join(ROOT, relpath), encoding="utf-8").read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    src = src.replace(old, new, 1)
+    pkg = types.ModuleType("oracle_mutant")
+    pkg.__path__ = []
+    sys.modules["oracle_mutant"] = pkg
+    # the schedules module imports the attention module relatively
+    att_src = open(os.path.join(ROOT, "oracle/attention.py"), encoding="utf-8").read()
+    if relpath == "oracle/attention.py":
+        att_src = src
+    att = types.ModuleType("oracle_mutant.attention")
+    exec(compile(att_src, "mutant_attention", "exec"), att.__dict__)
+    sys.modules["oracle_mutant.attention"] = att
+    if relpath == "oracle/attention.py":
+        return att
+    mod = types.ModuleType("oracle_mutant." + modname)
+    mod.__package__ = "oracle_mutant"
+    exec(compile(src, "mutant_" + modname, "exec"), mod.__dict__)
+    return mod
+
+
+def _attention_pins_fail(att):
+    checks = [
+        lambda: pins.pin_brute_force(att.attention),
+        lambda: pins.pin_zero_query(att.attention),
+        lambda: pins.pin_ones_value(att.attention),
+        lambda: pins.pin_single_key(att.attention),
+        lambda: pins.pin_sdpa(att.attention),
+        lambda: pins.pin_merge_identity(att.attention, att.lse_merge),
+        lambda: pins.pin_global_max_route(att.attention, att.attention_global_max),
+    ]
+    failed = 0
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failed += 1
+    return failed
+
+
+ATTENTION_MUTANTS = [
+    ("diagonal masked", "kpos <= qpos", "kpos < qpos"),
+    ("query offset dropped", "np.arange(Sq)[:, None] + q_offset", "np.arange(Sq)[:, None]"),
+    ("key offset sign", "np.arange(Sk)[None, :] + k_offset", "np.arange(Sk)[None, :] - k_offset"),
+    ("scale 1/D", "k[:, g, :].T) / np.sqrt(D)", "k[:, g, :].T) / D"),
+    ("max term dropped from lse", "lse[h, i] = m + np.log", "lse[h, i] = np.log"),
+    ("sum replaced by max", "np.exp(row - m).sum()", "np.exp(row - m).max()"),
+    ("GQA head index", "        g = h // group\n        scores", "        g = h % Hkv\n        scores"),
+    ("value operand swapped for key", "out[:, h, :] = w @ v[:, g, :]", "out[:, h, :] = w @ k[:, g, :]"),
+    ("merge weight sign", "w1 = np.where(finite, np.exp(lse1 - safe)", "w1 = np.where(finite, np.exp(safe - lse1)"),
+    ("merge uses one weight twice", "return o1 * w1 + o2 * w2", "return o1 * w1 + o2 * w1"),
+    ("merge lse as max", "lse = np.logaddexp(lse1, lse2)", "lse = np.maximum(lse1, lse2)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", ATTENTION_MUTANTS, ids=[m[0] for m in ATTENTION_MUTANTS])
+def test_attention_mutant_is_caught(name, old, new):
+    att = _load_mutant("oracle/attention.py", old, new, "attention")
+    with np.errstate(all="ignore"):
+        assert _attention_pins_fail(att) >= 1, f"no pin catches: {name}"
+
+
+def _schedule_pins_fail(sch, att):
+    import oracle.schedules as real
+    failed = 0
+    checks = []
+    checks.append(lambda: pins.pin_work(sch.split_contiguous, sch.split_zigzag, sch.work))
+
+    def ring_checks():
+        from oracle.attention import attention
+        q, k, v = pins.make_qkv_page()
+        ref, _ = attention(q, k, v)
+        outs, _, computed = sch.ring_contiguous(q, k, v, P=4)
+        assert computed == pins.load_golden("ring_counts_p4.txt")["counts"]
+        for r in range(4):
+            np.testing.assert_allclose(outs[r], ref[r * 8:(r + 1) * 8], atol=1e-12)
+        outs, _, units = sch.ring_zigzag(q, k, v, P=4)
+        for r in range(4):
+            np.testing.assert_allclose(outs[r], ref[sch.layout_index(sch.ZIGZAG, 32, 4, r)],
+                                       atol=1e-12)
+            assert units[r] == [2.0] * 4
+    checks.append(ring_checks)
+
+    def plan_checks():
+        for P in (4, 8):
+            S = 16 * P
+            mine = sch.ring_plan(S, P, sch.ZIGZAG, -1)
+            ref = real.ring_plan(S, P, real.ZIGZAG, -1)
+            # counts and coverage facts (not the reference plan itself)
+            for r in range(P):
+                comp = sorted((p[2], p[3]) for p in mine if p[0] == r and p[8] != sch.SKIP)
+                want = sorted((qc, kc) for qc in pins_split_zigzag(P)[r] for kc in range(qc + 1))
+                assert comp == want
+            assert len(mine) == len(ref)
+    checks.append(plan_checks)
+
+    def ulysses_checks():
+        S, H, D, P = 24, 8, 3, 4
+        x = np.arange(S * H * D, dtype=np.float64).reshape(S, H, D)
+        heads = sch.seq_to_head([x[r * 6:(r + 1) * 6] for r in range(P)], P)
+        for p in range(P):
+            assert np.array_equal(heads[p], x[:, 2 * p:2 * p + 2, :])
+        assert np.array_equal(np.concatenate(sch.head_to_seq(heads, P)), x)
+        g = pins.load_golden("ulysses_shapes_p4.txt")
+        q, k, v = pins.make_qkv_page()
+        outs, shapes = sch.ulysses_attention(q, k, v, P=4)
+        assert all(list(s) == g["attention"] for s in shapes)
+    checks.append(ulysses_checks)
+
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError, KeyError):
+            failed += 1
+    return failed
+
+
+def pins_split_zigzag(P):
+    """The zigzag split as the page's prose states it: rank r takes the r-th
+    chunk and the (r+1)-th chunk from the end."""
+    return {r: [r, 2 * P - (r + 1)] for r in range(P)}
+
+
+SCHEDULE_MUTANTS = [
+    ("zigzag second chunk", "return {r: [r, 2 * P - 1 - r] for r in range(P)}",
+     "return {r: [r, 2 * P - 2 - r] for r in range(P)}"),
+    ("contiguous split", "return {r: [2 * r, 2 * r + 1] for r in range(P)}",
+     "return {r: [r, r + 1] for r in range(P)}"),
+    ("work counts diagonal fully", "return sum(q + 0.5 for q in query_chunks)",
+     "return sum(q + 1.0 for q in query_chunks)"),
+    ("ring skip rule", "if src <= rank or not causal:", "if src < rank or not causal:"),
+    ("ring key offset", "q_offset=rank * C, k_offset=src * C)", "q_offset=rank * C, k_offset=rank * C)"),
+    ("zigzag skip rule", "if causal and kc > qc:", "if causal and kc >= qc:"),
+    ("plan classification", "elif kc == qc:\n                        kind = DIAG",
+     "elif kc == qc + 1:\n                        kind = DIAG"),
+    ("seq_to_head transpose dropped", "x.reshape(Sl, P, H // P, D).transpose(1, 0, 2, 3)",
+     "x.reshape(P, Sl, H // P, D)"),
+    ("all_to_all block index", "np.stack([sendbufs[r][p] for r in range(P)])",
+     "np.stack([sendbufs[p][r] for r in range(P)])"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", SCHEDULE_MUTANTS, ids=[m[0] for m in SCHEDULE_MUTANTS])
+def test_schedule_mutant_is_caught(name, old, new):
+    sch = _load_mutant("oracle/schedules.py", old, new, "schedules")
+    assert _schedule_pins_fail(sch, None) >= 1, f"no pin catches: {name}"
+
+
+C_MUTANTS = [
+    ("diagonal masked", "k_offset + j > pos_q", "k_offset + j >= pos_q"),
+    ("scale 1/D", "1.0 / sqrt((double)D)", "1.0 / (double)D"),
+    ("max term dropped", "const double l = m + log(sum);", "const double l = log(sum);"),
+    ("GQA head index", "const int g = h / group;", "const int g = h % Hkv;"),
+    ("weights not normalised", "const double w = exp(s[j] - l);", "const double w = exp(s[j] - m);"),
+    ("bf16 widening shift", "<< 16;", "<< 15;"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", C_MUTANTS, ids=[m[0] for m in C_MUTANTS])
+def test_c_oracle_mutant_is_caught(name, old, new, tmp_path):
+    src = open(os.path.join(ROOT, "oracle/cp_oracle.c"), encoding="utf-8").read()
+    assert old in src
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new, 1))
+    lib = native.bind(native.build(src=str(mpath), out=str(tmp_path / "libmutant.so")))
+
+    def attn(q, k, v, causal=True, q_offset=0, k_offset=0):
+        t = [torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32) for x in (q, k, v)]
+        return native.attention_rows(*t, causal=causal, q_offset=q_offset,
+                                     k_offset=k_offset, n_threads=1, lib=lib)
+
+    def bf16_check():
+        from oracle.attention import attention
+        from seeded_inputs import make_qkv
+        q, k, v = make_qkv(S=9, H=2, D=4, dtype=torch.bfloat16)
+        o, l = native.attention_rows(q, k, v, n_threads=1, lib=lib)
+        ro, rl = attention(q, k, v)
+        np.testing.assert_allclose(o, ro, atol=1e-12)
+
+    pins.ROUND_INPUTS = np.float32
+    failed = 0
+    try:
+        for c in (lambda: pins.pin_brute_force(attn), lambda: pins.pin_zero_query(attn),
+                  lambda: pins.pin_single_key(attn), lambda: pins.pin_sdpa(attn), bf16_check):
+            try:
+                with np.errstate(all="ignore"):
+                    c()
+            except (AssertionError, ValueError):
+                failed += 1
+    finally:
+        pins.ROUND_INPUTS = None
+    assert failed >= 1, f"no pin catches: {name}"
