@@ -1,0 +1,217 @@
+"""Benchmark: one rank's share of a 128K-token causal attention layer through
+both context-parallel schedules, on one MI355X.
+
+A step is one pass of the whole hot path over resident synthetic inputs:
+
+* ring share -- ``cp_ring_fwd`` for one rank of an 8-rank zigzag ring over
+  q, k, v bf16 [131072, 32, 128] (16 chunks of 8192; the rank's two query
+  chunks against all 8 KV blocks over 8 steps, masked blocks skipped,
+  log-sum-exp merged);
+* Ulysses share -- ``cp_seq_to_head`` of q [131072, 32, 128] and of k, v
+  [131072, 8, 128] for one rank of 8, full-sequence causal attention of its
+  4 query heads over its 1 KV head (``cp_attn_block_fwd``), and
+  ``cp_head_to_seq`` of the float32 output back into the sequence layout.
+
+Throughput is causal-adjusted FLOP: 4*D*Hq per visible (query, key) pair
+with a diagonal chunk counted as half (the handbook's work model, section
+"之字形切分"): 2^44 for each share.  The attention kernel's own rate is timed
+with HIP events recorded by the library around every launch on the launch
+stream; its fraction of the bf16 dense MFMA peak is the roofline figure.
+The CPU oracle is timed on a bounded sample of the ring share's rows.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+S, HQ, HKV_ULY, D, P = 131072, 32, 8, 128, 8
+RING_RANK, ULY_RANK = 0, 0
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
+PEAK_HBM_GBS = 8000.0
+METRIC = "causal block-attn fwd TFLOP/s + % bf16 MFMA peak, S=128K H=32 D=128"
+
+
+def ring_share_flop(S, H, D, P):
+    """Causal-adjusted FLOP of one zigzag rank: 2P chunk units of C x C."""
+    C = S // (2 * P)
+    return 4.0 * D * H * (2 * P) * C * C
+
+
+def ulysses_share_flop(S, H_local, D):
+    """Full-sequence causal attention of H_local heads, diagonal counted half."""
+    return 4.0 * D * H_local * S * S / 2.0
+
+
+def cpu_baseline(q, k, v, budget_s=12.0, max_rows=512):
+    """Time the float64 oracle on seeded rows of the ring rank's share."""
+    import numpy as np
+
+    from oracle import native
+    from oracle import schedules as OS
+    from seeded_inputs import sample_rows
+
+    positions = OS.layout_index(OS.ZIGZAG, S, P, RING_RANK)
+    order = sample_rows(len(positions), max_rows, seed=7).numpy()
+    rng = np.random.default_rng(7)
+    rng.shuffle(order)
+    threads = len(os.sched_getaffinity(0))
+    done_rows, flop, t_total = [], 0.0, 0.0
+    for b in range(0, len(order), 16):
+        rows = positions[order[b:b + 16]]
+        t0 = time.perf_counter()
+        native.attention_rows(q, k, v, rows=rows, n_threads=threads)
+        t_total += time.perf_counter() - t0
+        flop += sum(4.0 * D * HQ * (int(p) + 1) for p in rows)
+        done_rows.extend(int(p) for p in rows)
+        if t_total >= budget_s:
+            break
+    return {
+        "value": flop / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(done_rows)} seeded query rows of ring rank {RING_RANK}'s share "
+                   f"(S={S}, P={P} zigzag) x all {HQ} heads against every visible key, "
+                   f"float64 C oracle, {t_total:.1f} s, {flop / 1e12:.3f} TFLOP"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--part", choices=["both", "ring", "ulysses"], default="both")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the ring and Ulysses ranks are virtual and "
+              "played on a single MI355X; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import context_parallelism_cp_amd as cp
+    from seeded_inputs import make_qkv, sha256_of
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    q, k, v = make_qkv(S=S, H=HQ, D=D, seed=0, dtype=torch.bfloat16)
+    _, ku, vu = make_qkv(S=S, H=HQ, D=D, seed=0, dtype=torch.bfloat16, Hkv=HKV_ULY)
+    dq, dk, dv = q.to(dev), k.to(dev), v.to(dev)
+    dku, dvu = ku.to(dev), vu.to(dev)
+    print(f"# inputs generated and resident in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr)
+
+    rows = S // P
+    ring_out = torch.empty(rows, HQ, D, device=dev, dtype=torch.float32)
+    ring_lse = torch.empty(HQ, rows, device=dev, dtype=torch.float32)
+    hp, hkp = HQ // P, HKV_ULY // P
+    ql = torch.empty(S, hp, D, device=dev, dtype=torch.bfloat16)
+    kl = torch.empty(S, hkp, D, device=dev, dtype=torch.bfloat16)
+    vl = torch.empty(S, hkp, D, device=dev, dtype=torch.bfloat16)
+    uly_out_l = torch.empty(S, hp, D, device=dev, dtype=torch.float32)
+    uly_lse = torch.empty(hp, S, device=dev, dtype=torch.float32)
+    uly_out = torch.zeros(S, HQ, D, device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if args.part in ("both", "ring"):
+            cp.cp_ring_fwd(dq, dk, dv, P, "zigzag", RING_RANK, out=ring_out, lse=ring_lse,
+                           stream=stream)
+        if args.part in ("both", "ulysses"):
+            cp.cp_seq_to_head(dq, P, ULY_RANK, y=ql, stream=stream)
+            cp.cp_seq_to_head(dku, P, ULY_RANK, y=kl, stream=stream)
+            cp.cp_seq_to_head(dvu, P, ULY_RANK, y=vl, stream=stream)
+            cp.cp_attn_block_fwd(ql, kl, vl, uly_out_l, uly_lse, stream=stream)
+            cp.cp_head_to_seq(uly_out_l, uly_out, P, ULY_RANK, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    cp.cp_timing_enable(True)
+    cp.cp_timing_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    attn_ms, attn_n = cp.cp_timing_read(cp.CP_KERNEL_ATTN_BF16)
+    perm_ms, perm_n = cp.cp_timing_read(cp.CP_KERNEL_PERMUTE)
+    cp.cp_timing_enable(False)
+
+    flop_ring = ring_share_flop(S, HQ, D, P) if args.part in ("both", "ring") else 0.0
+    flop_uly = ulysses_share_flop(S, hp, D) if args.part in ("both", "ulysses") else 0.0
+    flop_step = flop_ring + flop_uly
+    ms_step = elapsed * 1e3 / args.steps
+    value = flop_step * args.steps / elapsed / 1e12
+    attn_tflops = flop_step * args.steps / (attn_ms * 1e-3) / 1e12 if attn_ms > 0 else None
+    perm_bytes_step = 0
+    if args.part in ("both", "ulysses"):
+        # each repack reads and writes its rank's share once
+        perm_bytes_step = 2 * (S * hp * D * 2 + 2 * S * hkp * D * 2 + S * hp * D * 4)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("one rank's share of a 128K-token causal attention layer: zigzag ring "
+                         "rank (S=131072, Hq=Hkv=32, D=128, P=8, 16 chunks of 8192) plus "
+                         "Ulysses GQA rank (Hq=32, Hkv=8, P=8 -> 4 q heads on 1 KV head over "
+                         "all 131072 tokens); bf16 inputs, fp32 out + lse"),
+            "parts": args.part,
+            "S": S, "Hq": HQ, "Hkv_ring": HQ, "Hkv_ulysses": HKV_ULY, "D": D, "P": P,
+            "flop_per_step": flop_step,
+            "flop_convention": "4*D*Hq per visible (q,k) pair, diagonal chunk counted half",
+            "inputs_sha256": sha256_of(q[:4096], k[:4096], v[:4096]),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_bf16_kernel",
+            "achieved": round(attn_tflops, 2) if attn_tflops else None,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
+            "traffic": None,
+            "launches": attn_n,
+            "avg_launch_ms": round(attn_ms / max(attn_n, 1), 4),
+            "flop_per_launch": flop_step * args.steps / max(attn_n, 1),
+        },
+        "breakdown": {
+            "attn_ms_per_step": round(attn_ms / args.steps, 3),
+            "repack_ms_per_step": round(perm_ms / args.steps, 3),
+            "repack_launches_per_step": perm_n // max(args.steps, 1),
+            "repack_GBps": round(perm_bytes_step * args.steps / (perm_ms * 1e-3) / 1e9, 1)
+            if perm_ms > 0 else None,
+            "repack_frac_hbm": round(perm_bytes_step * args.steps / (perm_ms * 1e-3) / 1e9
+                                     / PEAK_HBM_GBS, 4) if perm_ms > 0 else None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(q, k, v)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+"""Python binding of libcpattn.so: blockwise causal attention with per-row
+log-sum-exp, the log-sum-exp merge, the ring schedule and the Ulysses
+repacks on one MI355X (gfx950).
+
+Argument marshalling only: shapes and pointers are read from torch tensors
+and handed to the C-ABI declared in ``include/cp_attn.h``; every step runs
+in the library's HIP kernels on the caller's current HIP stream.  Torch
+provides device memory and streams.  There is no fallback: importing this
+package fails if ``libcpattn.so`` has not been built
+(``python -m context_parallelism_cp_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcpattn.so")
+
+CP_OK, CP_ERR_NULL, CP_ERR_SHAPE, CP_ERR_UNSUPPORTED, CP_ERR_CAPACITY, CP_ERR_HIP, CP_ERR_ALIGN = range(7)
+CP_F32, CP_BF16 = 0, 1
+CP_LAYOUT_CONTIGUOUS, CP_LAYOUT_ZIGZAG = 0, 1
+CP_PAIR_SKIP, CP_PAIR_FULL, CP_PAIR_DIAG = 0, 1, 2
+CP_KERNEL_ATTN_BF16, CP_KERNEL_ATTN_F32, CP_KERNEL_MERGE, CP_KERNEL_PERMUTE = range(4)
+
+LAYOUTS = {"contiguous": CP_LAYOUT_CONTIGUOUS, "zigzag": CP_LAYOUT_ZIGZAG}
+
+
+class CpError(RuntimeError):
+    """A non-zero cp_status; ``code`` holds it."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[cp_status {code}] {msg}")
+        self.code = code
+
+
+class cp_block_pair(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("step", ctypes.c_int32),
+                ("q_chunk", ctypes.c_int32), ("k_chunk", ctypes.c_int32),
+                ("q_offset", ctypes.c_int64), ("k_offset", ctypes.c_int64),
+                ("len_q", ctypes.c_int64), ("len_k", ctypes.c_int64),
+                ("kind", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "cp_attn_block_fwd": [_P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I64, _I64, _I, _I, _P],
+    "cp_lse_merge": [_P, _P, _P, _P, _P, _P, _I64, _I, _I, _P],
+    "cp_ring_fwd": [_P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I, _I, _P],
+    "cp_seq_to_head": [_P, _P, _I64, _I, _I, _I, _I, _SZ, _P],
+    "cp_head_to_seq": [_P, _P, _I64, _I, _I, _I, _I, _SZ, _P],
+    "cp_layout_index": [_I, _I64, _I, _I, _P],
+    "cp_ring_plan": [_I64, _I, _I, _I, _I, _P, ctypes.POINTER(ctypes.c_int)],
+    "cp_last_error": [],
+    "cp_timing_enable": [_I],
+    "cp_timing_reset": [],
+    "cp_timing_read": [_I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m context_parallelism_cp_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, args in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name == "cp_last_error" else ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def cp_last_error() -> str:
+    return lib.cp_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != CP_OK:
+        raise CpError(rc, cp_last_error())
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return CP_BF16
+    if t.dtype == torch.float32:
+        return CP_F32
+    raise CpError(CP_ERR_UNSUPPORTED, f"dtype {t.dtype} is not supported")
+
+
+def _dense(*ts):
+    for t in ts:
+        if not t.is_contiguous():
+            raise CpError(CP_ERR_ALIGN, "tensors must be contiguous")
+
+
+# ------------------------------------------------------------------ entry points
+def cp_attn_block_fwd(q, k, v, out=None, lse=None, q_offset: int = 0, k_offset: int = 0,
+                      causal: bool = True, stream=None):
+    """out [Sq,Hq,D] f32 and lse [Hq,Sq] f32 of q [Sq,Hq,D] against k, v [Sk,Hkv,D]."""
+    import torch
+    Sq, Hq, D = q.shape
+    Sk, Hkv, _ = k.shape
+    if out is None:
+        out = torch.empty(Sq, Hq, D, device=q.device, dtype=torch.float32)
+    if lse is None:
+        lse = torch.empty(Hq, Sq, device=q.device, dtype=torch.float32)
+    _dense(q, k, v, out, lse)
+    _check(lib.cp_attn_block_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr(), Sq, Sk, Hq, Hkv, D, q_offset, k_offset,
+                                 int(bool(causal)), _dtype_code(q), _stream(q, stream)))
+    return out, lse
+
+
+def cp_lse_merge(o1, lse1, o2, lse2, o=None, lse=None, stream=None):
+    """Log-sum-exp merge; o may be o1 and lse may be lse1 (in place)."""
+    import torch
+    Sq, H, D = o1.shape
+    if o is None:
+        o = torch.empty_like(o1)
+    if lse is None:
+        lse = torch.empty_like(lse1)
+    _dense(o1, lse1, o2, lse2, o, lse)
+    _check(lib.cp_lse_merge(o1.data_ptr(), lse1.data_ptr(), o2.data_ptr(), lse2.data_ptr(),
+                            o.data_ptr(), lse.data_ptr(), Sq, H, D, _stream(o1, stream)))
+    return o, lse
+
+
+def cp_ring_fwd(q, k, v, P: int, layout="zigzag", rank: int = -1, causal: bool = True,
+                out=None, lse=None, stream=None):
+    """Ring attention over P virtual ranks (rank=-1: all, natural order;
+    rank=r: that rank's share in its local order)."""
+    import torch
+    S, Hq, D = q.shape
+    _, Hkv, _ = k.shape
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    rows = S if rank < 0 else S // max(P, 1)
+    if out is None:
+        out = torch.empty(rows, Hq, D, device=q.device, dtype=torch.float32)
+    if lse is None:
+        lse = torch.empty(Hq, rows, device=q.device, dtype=torch.float32)
+    _dense(q, k, v, out, lse)
+    _check(lib.cp_ring_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), S, Hq, Hkv, D, P, lay, rank, int(bool(causal)),
+                           _dtype_code(q), _stream(q, stream)))
+    return out, lse
+
+
+def cp_seq_to_head(x, P: int, rank: int = -1, y=None, stream=None):
+    """x natural [S,H,D] -> [P,S,H/P,D] (rank=-1) or [S,H/P,D] (rank=p)."""
+    import torch
+    S, H, D = x.shape
+    Hp = H // max(P, 1)
+    if y is None:
+        shape = (P, S, Hp, D) if rank < 0 else (S, Hp, D)
+        y = torch.empty(shape, device=x.device, dtype=x.dtype)
+    _dense(x, y)
+    _check(lib.cp_seq_to_head(x.data_ptr(), y.data_ptr(), S, H, D, P, rank, x.element_size(),
+                              _stream(x, stream)))
+    return y
+
+
+def cp_head_to_seq(x, y, P: int, rank: int = -1, stream=None):
+    """Inverse of cp_seq_to_head into the natural [S,H,D] tensor y; rank=p
+    writes head slice p of y only."""
+    S, H, D = y.shape
+    _dense(x, y)
+    _check(lib.cp_head_to_seq(x.data_ptr(), y.data_ptr(), S, H, D, P, rank, x.element_size(),
+                              _stream(y, stream)))
+    return y
+
+
+def cp_layout_index(layout, S: int, P: int, rank: int) -> np.ndarray:
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    n = S // max(P, 1)
+    idx = np.empty(max(n, 1), dtype=np.int32)
+    _check(lib.cp_layout_index(lay, S, P, rank, idx.ctypes.data))
+    return idx[:n]
+
+
+def cp_ring_plan(S: int, P: int, layout, rank: int = -1, causal: bool = True):
+    """List of (rank, step, q_chunk, k_chunk, q_offset, k_offset, len_q, len_k, kind)."""
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    n = ctypes.c_int(0)
+    _check(lib.cp_ring_plan(S, P, lay, rank, int(bool(causal)), None, ctypes.byref(n)))
+    arr = (cp_block_pair * max(n.value, 1))()
+    _check(lib.cp_ring_plan(S, P, lay, rank, int(bool(causal)), arr, ctypes.byref(n)))
+    return [(p.rank, p.step, p.q_chunk, p.k_chunk, p.q_offset, p.k_offset, p.len_q, p.len_k,
+             p.kind) for p in arr[:n.value]]
+
+
+def cp_timing_enable(enable: bool = True):
+    _check(lib.cp_timing_enable(int(bool(enable))))
+
+
+def cp_timing_reset():
+    _check(lib.cp_timing_reset())
+
+
+def cp_timing_read(kind: int):
+    """(total milliseconds, launches) of one kernel kind since the last reset."""
+    ms, n = ctypes.c_double(0), ctypes.c_int64(0)
+    _check(lib.cp_timing_read(kind, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

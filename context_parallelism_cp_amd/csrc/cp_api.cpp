@@ -1,0 +1,562 @@
+// cp_api.cpp -- host side of libcpattn.so: argument validation, the ring
+// planner, the Ulysses repack offsets, kernel launches and kernel timing.
+// The public contract is include/cp_attn.h.
+//
+// Ring schedule (handbook page "上下文并行：Ring Attention 与 Ulysses",
+// section "Ring Attention：KV 沿环传一圈"): at step t rank r holds the KV block
+// of rank src = (r - t) mod P.  The zigzag split ("之字形切分") gives rank r
+// chunks r and 2P-1-r of a 2P-way split; a (query chunk, key chunk) pair is
+// skipped when the key chunk comes after the query chunk, masked when they
+// are the same chunk and computed in full otherwise.  One kernel launch per
+// ring step covers every query chunk of every rank that step touches (ranks
+// are independent), each query chunk attending to the key chunks of its step
+// in one pass; the log-sum-exp merge into the running result is fused into
+// the kernel epilogue.
+#include "../../include/cp_attn.h"
+#include "cp_kernels.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+using namespace cpattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok()
+{
+    g_last_error.clear();
+    return CP_OK;
+}
+
+bool aligned(const void *p, size_t n) { return ((uintptr_t)p) % n == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0)
+        return false;
+    const char *x = (const char *)a;
+    const char *y = (const char *)b;
+    return x < y + nb && y < x + na;
+}
+
+// ------------------------------------------------------------------ timing
+struct Timing {
+    std::mutex mu;
+    bool enabled = false;
+    struct Rec {
+        int kind;
+        hipEvent_t start, stop;
+    };
+    std::vector<Rec> pending;
+    std::vector<hipEvent_t> pool;
+    double total_ms[4] = {0, 0, 0, 0};
+    int64_t launches[4] = {0, 0, 0, 0};
+};
+
+Timing &timing()
+{
+    static Timing t;
+    return t;
+}
+
+hipEvent_t take_event(Timing &t)
+{
+    if (!t.pool.empty()) {
+        hipEvent_t e = t.pool.back();
+        t.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess)
+        return nullptr;
+    return e;
+}
+
+// Launch `fn` on `stream`, bracketed by events when timing is enabled.
+template <typename F>
+int timed_launch(int kind, hipStream_t stream, F &&fn)
+{
+    Timing &t = timing();
+    std::unique_lock<std::mutex> lock(t.mu, std::defer_lock);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (t.enabled) {
+        lock.lock();
+        e0 = take_event(t);
+        e1 = take_event(t);
+        if (!e0 || !e1)
+            return fail(CP_ERR_HIP, "hipEventCreate failed");
+        if (hipEventRecord(e0, stream) != hipSuccess)
+            return fail(CP_ERR_HIP, "hipEventRecord failed");
+    }
+    const hipError_t err = fn();
+    if (err != hipSuccess)
+        return fail(CP_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    if (e0) {
+        if (hipEventRecord(e1, stream) != hipSuccess)
+            return fail(CP_ERR_HIP, "hipEventRecord failed");
+        t.pending.push_back({kind, e0, e1});
+    }
+    return CP_OK;
+}
+
+// ------------------------------------------------------------- validation
+int check_attn_common(const void *q, const void *k, const void *v, const float *out,
+                      const float *lse, int64_t Sq, int64_t Sk, int Hq, int Hkv, int D,
+                      cp_dtype dtype)
+{
+    // a pointer may be NULL only when its tensor is empty
+    if ((Sq > 0 && (!q || !out || !lse)) || (Sk > 0 && (!k || !v)))
+        return fail(CP_ERR_NULL, "q, k, v, out and lse must be non-NULL");
+    if (Sq < 0 || Sk < 0)
+        return fail(CP_ERR_SHAPE, "negative sequence length (Sq=%lld, Sk=%lld)",
+                    (long long)Sq, (long long)Sk);
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return fail(CP_ERR_SHAPE, "need Hq >= 1, Hkv >= 1 and Hkv dividing Hq (Hq=%d, Hkv=%d)",
+                    Hq, Hkv);
+    if (dtype == CP_BF16) {
+        if (D != 128)
+            return fail(CP_ERR_UNSUPPORTED, "bf16 attention supports D = 128 only (D=%d)", D);
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+            return fail(CP_ERR_ALIGN, "bf16 attention needs 16-byte aligned q, k, v and out");
+    } else if (dtype == CP_F32) {
+        if (D < 1 || D > 128)
+            return fail(CP_ERR_UNSUPPORTED, "float32 attention supports 1 <= D <= 128 (D=%d)", D);
+        if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(out, 4))
+            return fail(CP_ERR_ALIGN, "float32 attention needs 4-byte aligned pointers");
+    } else {
+        return fail(CP_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    }
+    if (!aligned(lse, 4))
+        return fail(CP_ERR_ALIGN, "lse must be 4-byte aligned");
+    const size_t eb = dtype == CP_BF16 ? 2 : 4;
+    const size_t qb = (size_t)Sq * Hq * D * eb, kb = (size_t)Sk * Hkv * D * eb;
+    const size_t ob = (size_t)Sq * Hq * D * 4, lb = (size_t)Sq * Hq * 4;
+    if (overlaps(q, qb, out, ob) || overlaps(k, kb, out, ob) || overlaps(v, kb, out, ob) ||
+        overlaps(q, qb, lse, lb) || overlaps(k, kb, lse, lb) || overlaps(v, kb, lse, lb) ||
+        overlaps(out, ob, lse, lb))
+        return fail(CP_ERR_ALIGN, "q, k, v, out and lse must not overlap");
+    return CP_OK;
+}
+
+int launch_attn(const AttnLaunch &a, cp_dtype dtype, hipStream_t stream)
+{
+    if (dtype == CP_BF16)
+        return timed_launch(CP_KERNEL_ATTN_BF16, stream, [&] { return launch_attn_bf16(a, stream); });
+    return timed_launch(CP_KERNEL_ATTN_F32, stream, [&] { return launch_attn_f32(a, stream); });
+}
+
+// ------------------------------------------------------------ ring helpers
+struct Split {
+    std::vector<int> chunks;  // chunk ids of one rank, local order
+    int64_t chunk_len;
+};
+
+Split rank_chunks(cp_layout layout, int64_t S, int P, int r)
+{
+    if (layout == CP_LAYOUT_CONTIGUOUS)
+        return {{r}, S / P};
+    return {{r, 2 * P - 1 - r}, S / (2 * P)};
+}
+
+int check_ring_shape(int64_t S, int P, cp_layout layout, int rank)
+{
+    if (P < 1)
+        return fail(CP_ERR_SHAPE, "P must be >= 1 (P=%d)", P);
+    if (rank < -1 || rank >= P)
+        return fail(CP_ERR_SHAPE, "rank must be -1 or in [0, P) (rank=%d, P=%d)", rank, P);
+    if (S < 0)
+        return fail(CP_ERR_SHAPE, "negative sequence length");
+    if (layout == CP_LAYOUT_CONTIGUOUS) {
+        if (S % P != 0)
+            return fail(CP_ERR_SHAPE, "contiguous layout needs P | S (S=%lld, P=%d)",
+                        (long long)S, P);
+    } else if (layout == CP_LAYOUT_ZIGZAG) {
+        if (S % (2 * (int64_t)P) != 0)
+            return fail(CP_ERR_SHAPE, "zigzag layout needs 2P | S (S=%lld, P=%d)",
+                        (long long)S, P);
+    } else {
+        return fail(CP_ERR_SHAPE, "unknown layout %d", (int)layout);
+    }
+    return CP_OK;
+}
+
+int pair_kind(int causal, int qc, int kc)
+{
+    if (!causal || kc < qc)
+        return CP_PAIR_FULL;
+    return kc == qc ? CP_PAIR_DIAG : CP_PAIR_SKIP;
+}
+
+// First output row of the query chunk `chunk` held in local slot `slot`:
+// natural order when every rank is computed, the rank's local order otherwise.
+int64_t out_row_of(int rank_arg, int slot, int chunk, int64_t chunk_len)
+{
+    return rank_arg < 0 ? (int64_t)chunk * chunk_len : (int64_t)slot * chunk_len;
+}
+
+}  // namespace
+
+// =================================================================== C-ABI
+extern "C" {
+
+const char *cp_last_error(void) { return g_last_error.c_str(); }
+
+int cp_attn_block_fwd(const void *q, const void *k, const void *v, float *out, float *lse,
+                      int64_t Sq, int64_t Sk, int Hq, int Hkv, int D, int64_t q_offset,
+                      int64_t k_offset, int causal, cp_dtype dtype, void *stream)
+{
+    int rc = check_attn_common(q, k, v, out, lse, Sq, Sk, Hq, Hkv, D, dtype);
+    if (rc)
+        return rc;
+    if (Sq == 0)
+        return ok();
+    AttnLaunch a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.lse_ld = Sq;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.D = D;
+    a.causal = causal ? 1 : 0;
+    a.n_q = 1;
+    QSeg &s = a.qs[0];
+    s.row0 = 0;
+    s.pos0 = q_offset;
+    s.len = Sq;
+    s.out_row0 = 0;
+    s.merge = 0;
+    s.n_kv = Sk > 0 ? 1 : 0;
+    s.kv[0] = KvSeg{0, k_offset, Sk};
+    rc = launch_attn(a, dtype, (hipStream_t)stream);
+    return rc ? rc : ok();
+}
+
+int cp_lse_merge(const float *o1, const float *lse1, const float *o2, const float *lse2,
+                 float *o, float *lse, int64_t Sq, int H, int D, void *stream)
+{
+    if (Sq != 0 && (!o1 || !lse1 || !o2 || !lse2 || !o || !lse))
+        return fail(CP_ERR_NULL, "all merge pointers must be non-NULL");
+    if (Sq < 0 || H < 1 || D < 1)
+        return fail(CP_ERR_SHAPE, "need Sq >= 0, H >= 1, D >= 1");
+    if (D % 4 != 0 || D > 256)
+        return fail(CP_ERR_UNSUPPORTED, "merge needs D %% 4 == 0 and D <= 256 (D=%d)", D);
+    if (!aligned(o1, 16) || !aligned(o2, 16) || !aligned(o, 16) || !aligned(lse1, 4) ||
+        !aligned(lse2, 4) || !aligned(lse, 4))
+        return fail(CP_ERR_ALIGN, "merge needs 16-byte aligned o buffers");
+    const size_t ob = (size_t)Sq * H * D * 4, lb = (size_t)Sq * H * 4;
+    auto bad_alias = [&](const void *x, size_t nx, const void *y, size_t ny) {
+        return x != y && overlaps(x, nx, y, ny);
+    };
+    if (bad_alias(o, ob, o1, ob) || bad_alias(o, ob, o2, ob) || bad_alias(lse, lb, lse1, lb) ||
+        bad_alias(lse, lb, lse2, lb) || overlaps(o, ob, lse, lb) || overlaps(o, ob, lse1, lb) ||
+        overlaps(o, ob, lse2, lb) || overlaps(lse, lb, o1, ob) || overlaps(lse, lb, o2, ob))
+        return fail(CP_ERR_ALIGN, "merge outputs may only alias an input exactly");
+    if (Sq == 0)
+        return ok();
+    hipStream_t st = (hipStream_t)stream;
+    int rc = timed_launch(CP_KERNEL_MERGE, st, [&] {
+        return launch_lse_merge(o1, lse1, o2, lse2, o, lse, Sq, H, D, st);
+    });
+    return rc ? rc : ok();
+}
+
+int cp_layout_index(cp_layout layout, int64_t S, int P, int rank, int32_t *idx)
+{
+    if (!idx)
+        return fail(CP_ERR_NULL, "idx must be non-NULL");
+    int rc = check_ring_shape(S, P, layout, rank);
+    if (rc)
+        return rc;
+    if (rank < 0)
+        return fail(CP_ERR_SHAPE, "cp_layout_index needs a rank in [0, P)");
+    if (S >= (int64_t(1) << 31))
+        return fail(CP_ERR_SHAPE, "cp_layout_index needs S < 2^31");
+    const Split sp = rank_chunks(layout, S, P, rank);
+    int64_t j = 0;
+    for (int c : sp.chunks)
+        for (int64_t e = 0; e < sp.chunk_len; ++e)
+            idx[j++] = (int32_t)(c * sp.chunk_len + e);
+    return ok();
+}
+
+int cp_ring_plan(int64_t S, int P, cp_layout layout, int rank, int causal,
+                 cp_block_pair *pairs, int *n_pairs)
+{
+    if (!n_pairs)
+        return fail(CP_ERR_NULL, "n_pairs must be non-NULL");
+    int rc = check_ring_shape(S, P, layout, rank);
+    if (rc)
+        return rc;
+    const int per_step = layout == CP_LAYOUT_CONTIGUOUS ? 1 : 4;
+    const int64_t n_ranks = rank < 0 ? P : 1;
+    const int64_t need = n_ranks * P * per_step;
+    if (need > 0x7fffffff)
+        return fail(CP_ERR_SHAPE, "plan too large");
+    if (!pairs) {
+        *n_pairs = (int)need;
+        return ok();
+    }
+    if (*n_pairs < need) {
+        const int cap = *n_pairs;
+        *n_pairs = (int)need;
+        return fail(CP_ERR_CAPACITY, "pairs holds %d entries, the plan needs %lld", cap,
+                    (long long)need);
+    }
+    int n = 0;
+    for (int r = (rank < 0 ? 0 : rank); r < (rank < 0 ? P : rank + 1); ++r) {
+        const Split mine = rank_chunks(layout, S, P, r);
+        for (int t = 0; t < P; ++t) {
+            const int src = ((r - t) % P + P) % P;
+            const Split theirs = rank_chunks(layout, S, P, src);
+            for (int qc : mine.chunks)
+                for (int kc : theirs.chunks) {
+                    cp_block_pair &p = pairs[n++];
+                    p.rank = r;
+                    p.step = t;
+                    p.q_chunk = qc;
+                    p.k_chunk = kc;
+                    p.q_offset = qc * mine.chunk_len;
+                    p.k_offset = kc * mine.chunk_len;
+                    p.len_q = mine.chunk_len;
+                    p.len_k = mine.chunk_len;
+                    p.kind = pair_kind(causal, qc, kc);
+                    p.reserved = 0;
+                }
+        }
+    }
+    *n_pairs = n;
+    return ok();
+}
+
+int cp_ring_fwd(const void *q, const void *k, const void *v, float *out, float *lse, int64_t S,
+                int Hq, int Hkv, int D, int P, cp_layout layout, int rank, int causal,
+                cp_dtype dtype, void *stream)
+{
+    int rc = check_ring_shape(S, P, layout, rank);
+    if (rc)
+        return rc;
+    const int64_t rows_out = rank < 0 ? S : S / P;
+    // q, k, v span the whole sequence; out and lse span rows_out rows.
+    if (S > 0 && (!q || !k || !v || !out || !lse))
+        return fail(CP_ERR_NULL, "q, k, v, out and lse must be non-NULL");
+    rc = check_attn_common(q, k, v, out, lse, rows_out, S, Hq, Hkv, D, dtype);
+    if (rc)
+        return rc;
+    {
+        const size_t eb = dtype == CP_BF16 ? 2 : 4;
+        const size_t qb = (size_t)S * Hq * D * eb, ob = (size_t)rows_out * Hq * D * 4;
+        if (overlaps(q, qb, out, ob) || overlaps(q, qb, lse, (size_t)rows_out * Hq * 4))
+            return fail(CP_ERR_ALIGN, "q, k, v, out and lse must not overlap");
+    }
+    if (S == 0)
+        return ok();
+
+    hipStream_t st = (hipStream_t)stream;
+    const int r_begin = rank < 0 ? 0 : rank;
+    const int r_end = rank < 0 ? P : rank + 1;
+    // started[r][slot]: has this query chunk received its first result yet?
+    std::vector<std::vector<char>> started(P, std::vector<char>(2, 0));
+
+    for (int t = 0; t < P; ++t) {
+        AttnLaunch a{};
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.out = out;
+        a.lse = lse;
+        a.lse_ld = rows_out;
+        a.Hq = Hq;
+        a.Hkv = Hkv;
+        a.D = D;
+        a.causal = causal ? 1 : 0;
+        a.n_q = 0;
+        auto flush = [&]() -> int {
+            if (a.n_q == 0)
+                return CP_OK;
+            int r2 = launch_attn(a, dtype, st);
+            a.n_q = 0;
+            return r2;
+        };
+        for (int r = r_begin; r < r_end; ++r) {
+            const int src = ((r - t) % P + P) % P;
+            const Split mine = rank_chunks(layout, S, P, r);
+            const Split theirs = rank_chunks(layout, S, P, src);
+            for (int slot = 0; slot < (int)mine.chunks.size(); ++slot) {
+                const int qc = mine.chunks[slot];
+                QSeg seg{};
+                seg.row0 = (int64_t)qc * mine.chunk_len;
+                seg.pos0 = seg.row0;
+                seg.len = mine.chunk_len;
+                seg.out_row0 = out_row_of(rank, slot, qc, mine.chunk_len);
+                seg.n_kv = 0;
+                for (int kc : theirs.chunks) {
+                    if (pair_kind(causal, qc, kc) == CP_PAIR_SKIP)
+                        continue;
+                    const int64_t k0 = (int64_t)kc * theirs.chunk_len;
+                    seg.kv[seg.n_kv++] = KvSeg{k0, k0, theirs.chunk_len};
+                }
+                if (seg.n_kv == 0)
+                    continue;
+                seg.merge = started[r][slot] ? 1 : 0;
+                started[r][slot] = 1;
+                if (a.n_q == kMaxQSegs && (rc = flush()))
+                    return rc;
+                a.qs[a.n_q++] = seg;
+            }
+        }
+        if ((rc = flush()))
+            return rc;
+    }
+    // Every query chunk sees its own (diagonal) chunk at step 0, so every
+    // output row has been written.
+    for (int r = r_begin; r < r_end; ++r)
+        for (size_t slot = 0; slot < rank_chunks(layout, S, P, r).chunks.size(); ++slot)
+            if (!started[r][slot])
+                return fail(CP_ERR_HIP, "internal: ring left rank %d chunk %zu unwritten", r, slot);
+    return ok();
+}
+
+static int repack(bool to_head, const void *x, void *y, int64_t S, int H, int D, int P,
+                  int rank, size_t elem_bytes, void *stream)
+{
+    if (S != 0 && (!x || !y))
+        return fail(CP_ERR_NULL, "x and y must be non-NULL");
+    if (S < 0 || H < 1 || D < 1 || P < 1)
+        return fail(CP_ERR_SHAPE, "need S >= 0, H >= 1, D >= 1, P >= 1");
+    if (H % P != 0)
+        return fail(CP_ERR_SHAPE, "P must divide the head count (H=%d, P=%d)", H, P);
+    if (S % P != 0)
+        return fail(CP_ERR_SHAPE, "P must divide S (S=%lld, P=%d)", (long long)S, P);
+    if (rank < -1 || rank >= P)
+        return fail(CP_ERR_SHAPE, "rank must be -1 or in [0, P)");
+    if (elem_bytes != 2 && elem_bytes != 4)
+        return fail(CP_ERR_UNSUPPORTED, "elem_bytes must be 2 or 4");
+    if (!aligned(x, elem_bytes) || !aligned(y, elem_bytes))
+        return fail(CP_ERR_ALIGN, "x and y must be aligned to elem_bytes");
+    const int64_t Hp = H / P;
+    const int64_t unit = Hp * D * (int64_t)elem_bytes;  // bytes of one run
+    const int64_t row = (int64_t)H * D * (int64_t)elem_bytes;
+    // the natural tensor and the all-ranks tensor hold S*H*D elements, one
+    // rank's head share S*Hp*D
+    const size_t all_bytes = (size_t)S * H * D * elem_bytes;
+    const size_t share_bytes = rank < 0 ? all_bytes : (size_t)S * Hp * D * elem_bytes;
+    const size_t xb = to_head ? all_bytes : share_bytes;
+    const size_t yb = to_head ? share_bytes : all_bytes;
+    if (overlaps(x, xb, y, yb))
+        return fail(CP_ERR_ALIGN, "x and y must not overlap");
+    if (S == 0)
+        return ok();
+    UnitCopy c{};
+    c.src = x;
+    c.dst = y;
+    c.unit_bytes = unit;
+    if (rank < 0) {
+        c.n_units = (int64_t)P * S;  // u = p*S + t
+        c.per = S;
+        if (to_head) {  // y[p][t] <- x[t][p*Hp]
+            c.src_base = 0, c.src_a = unit, c.src_b = row;
+            c.dst_base = 0, c.dst_a = S * unit, c.dst_b = unit;
+        } else {        // y[t][p*Hp] <- x[p][t]
+            c.src_base = 0, c.src_a = S * unit, c.src_b = unit;
+            c.dst_base = 0, c.dst_a = unit, c.dst_b = row;
+        }
+    } else {
+        c.n_units = S;  // u = t
+        c.per = S;
+        if (to_head) {  // y[t] <- x[t][rank*Hp]
+            c.src_base = rank * unit, c.src_a = 0, c.src_b = row;
+            c.dst_base = 0, c.dst_a = 0, c.dst_b = unit;
+        } else {        // y[t][rank*Hp] <- x[t]
+            c.src_base = 0, c.src_a = 0, c.src_b = unit;
+            c.dst_base = rank * unit, c.dst_a = 0, c.dst_b = row;
+        }
+    }
+    hipStream_t st = (hipStream_t)stream;
+    int rc = timed_launch(CP_KERNEL_PERMUTE, st, [&] { return launch_unit_copy(c, st); });
+    return rc ? rc : ok();
+}
+
+int cp_seq_to_head(const void *x, void *y, int64_t S, int H, int D, int P, int rank,
+                   size_t elem_bytes, void *stream)
+{
+    return repack(true, x, y, S, H, D, P, rank, elem_bytes, stream);
+}
+
+int cp_head_to_seq(const void *x, void *y, int64_t S, int H, int D, int P, int rank,
+                   size_t elem_bytes, void *stream)
+{
+    return repack(false, x, y, S, H, D, P, rank, elem_bytes, stream);
+}
+
+int cp_timing_enable(int enable)
+{
+    Timing &t = timing();
+    std::lock_guard<std::mutex> lock(t.mu);
+    t.enabled = enable != 0;
+    return ok();
+}
+
+int cp_timing_reset(void)
+{
+    Timing &t = timing();
+    std::lock_guard<std::mutex> lock(t.mu);
+    for (auto &rec : t.pending) {
+        hipEventSynchronize(rec.stop);
+        t.pool.push_back(rec.start);
+        t.pool.push_back(rec.stop);
+    }
+    t.pending.clear();
+    for (int i = 0; i < 4; ++i) {
+        t.total_ms[i] = 0;
+        t.launches[i] = 0;
+    }
+    return ok();
+}
+
+int cp_timing_read(cp_kernel_kind kind, double *total_ms, int64_t *launches)
+{
+    if (!total_ms || !launches)
+        return fail(CP_ERR_NULL, "total_ms and launches must be non-NULL");
+    if ((int)kind < 0 || (int)kind > 3)
+        return fail(CP_ERR_SHAPE, "unknown kernel kind %d", (int)kind);
+    Timing &t = timing();
+    std::lock_guard<std::mutex> lock(t.mu);
+    for (auto &rec : t.pending) {
+        if (hipEventSynchronize(rec.stop) != hipSuccess)
+            return fail(CP_ERR_HIP, "hipEventSynchronize failed");
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, rec.start, rec.stop) != hipSuccess)
+            return fail(CP_ERR_HIP, "hipEventElapsedTime failed");
+        t.total_ms[rec.kind] += ms;
+        t.launches[rec.kind] += 1;
+        t.pool.push_back(rec.start);
+        t.pool.push_back(rec.stop);
+    }
+    t.pending.clear();
+    *total_ms = t.total_ms[kind];
+    *launches = t.launches[kind];
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,213 @@
+/*
+ * cp_attn.h -- C-ABI of libcpattn.so: blockwise causal attention with a
+ * per-row log-sum-exp, the log-sum-exp merge, the ring schedule and the
+ * Ulysses repacks, on one AMD Instinct MI355X (gfx950).
+ *
+ * Pages that define the operations (cited by title and section):
+ *   [HB] "上下文并行：Ring Attention 与 Ulysses" (Context parallelism: Ring
+ *        Attention and Ulysses), AI-infra handbook, train/model/context.
+ *   [SP] "Sequence Parallel vs Context Parallel" blog (xxqk.cn), section 3.2,
+ *        how the distributed softmax is merged.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major and contiguous.  q is [Sq][Hq][D], k and v
+ *     are [Sk][Hkv][D] (sequence-major, no batch dimension), out is
+ *     [Sq][Hq][D] float32 and lse is [Hq][Sq] float32 holding natural-log
+ *     log-sum-exp values.  A sub-chunk of the sequence is a pointer offset.
+ *   - Device pointers are owned by the caller; the library never allocates
+ *     or frees device memory.  Kernels are enqueued on `stream` (a
+ *     hipStream_t; NULL means the default stream) and nothing synchronises
+ *     the host: buffers must stay alive until the stream has drained.
+ *   - Every argument is checked before any HIP call.  On failure nothing is
+ *     enqueued, a non-zero cp_status is returned and cp_last_error() gives a
+ *     message.  A HIP launch error returns CP_ERR_HIP.  No C++ exception
+ *     crosses this interface.
+ *   - bf16 tensors need 16-byte aligned base pointers; float32 tensors need
+ *     4-byte alignment.  q, k, v must not overlap out or lse.  A pointer may
+ *     be NULL only when its tensor is empty (zero rows).
+ *   - The attention scale is fixed at 1/sqrt(D), D being the last dimension
+ *     of q ([HB], section "哪些运算可以直接切", function attention()).
+ *   - Query head h reads KV head h / (Hq / Hkv): contiguous head groups, as
+ *     the Ulysses section of [HB] hands rank p the p-th contiguous share of
+ *     heads.
+ *   - A query row that sees no key yields out = 0 and lse = -inf; the merge
+ *     treats lse = -inf as its identity.
+ */
+#ifndef CP_ATTN_H
+#define CP_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CP_OK = 0,
+    CP_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    CP_ERR_SHAPE = 2,       /* sizes inconsistent or not divisible              */
+    CP_ERR_UNSUPPORTED = 3, /* valid request this build does not implement      */
+    CP_ERR_CAPACITY = 4,    /* caller-provided host array too small             */
+    CP_ERR_HIP = 5,         /* a HIP runtime call or kernel launch failed       */
+    CP_ERR_ALIGN = 6        /* pointer alignment or aliasing rule broken        */
+} cp_status;
+
+typedef enum { CP_F32 = 0, CP_BF16 = 1 } cp_dtype;
+
+/* How the sequence is split over P ranks ([HB], sections "Ring Attention：KV
+ * 沿环传一圈" and "之字形切分"):
+ *   CONTIGUOUS: rank r owns positions [r*S/P, (r+1)*S/P).
+ *   ZIGZAG:     the sequence is cut into 2P chunks of C = S/(2P); rank r owns
+ *               chunk r then chunk 2P-1-r, in that local order. */
+typedef enum { CP_LAYOUT_CONTIGUOUS = 0, CP_LAYOUT_ZIGZAG = 1 } cp_layout;
+
+/* Classification of one (query chunk, key chunk) pair of the ring. */
+typedef enum { CP_PAIR_SKIP = 0, CP_PAIR_FULL = 1, CP_PAIR_DIAG = 2 } cp_pair_kind;
+
+typedef struct {
+    int32_t rank;      /* rank that owns the query chunk                        */
+    int32_t step;      /* ring step t; the KV block is rank (rank - t) mod P's  */
+    int32_t q_chunk;   /* chunk ids: P-way split (contiguous), 2P-way (zigzag)  */
+    int32_t k_chunk;
+    int64_t q_offset;  /* absolute first position of the query chunk            */
+    int64_t k_offset;  /* absolute first position of the key chunk              */
+    int64_t len_q;     /* chunk lengths                                         */
+    int64_t len_k;
+    int32_t kind;      /* cp_pair_kind                                          */
+    int32_t reserved;  /* zero                                                  */
+} cp_block_pair;
+
+/*
+ * cp_attn_block_fwd -- attention of one query chunk against one KV block at
+ * given absolute sequence offsets ([HB], section "哪些运算可以直接切",
+ * attention(q, k, v, causal, q_offset, k_offset)):
+ *   s[i][j] = q[i].k[j] / sqrt(D); with causal != 0 key j is visible to row i
+ *   iff k_offset + j <= q_offset + i (the diagonal is visible);
+ *   lse[h][i] = log sum_j exp(s[i][j]) over visible j;
+ *   out[i][h] = sum_j exp(s[i][j] - lse[h][i]) v[j].
+ * dtype CP_BF16 (q, k, v bf16; D must be 128) runs on bf16 MFMA with float32
+ * accumulation and the probabilities rounded to bf16 before the second
+ * product; CP_F32 (1 <= D <= 128) runs in float32.
+ * Sq == 0 is a no-op; Sk == 0 writes out = 0, lse = -inf.
+ * Errors: CP_ERR_NULL, CP_ERR_SHAPE (negative sizes, Hq % Hkv != 0,
+ * Hq or Hkv < 1), CP_ERR_UNSUPPORTED (D), CP_ERR_ALIGN, CP_ERR_HIP.
+ */
+int cp_attn_block_fwd(const void *q, const void *k, const void *v, float *out, float *lse,
+                      int64_t Sq, int64_t Sk, int Hq, int Hkv, int D,
+                      int64_t q_offset, int64_t k_offset, int causal,
+                      cp_dtype dtype, void *stream);
+
+/*
+ * cp_lse_merge -- fold two partial results over disjoint key sets into one
+ * ([HB], section "Ring Attention：KV 沿环传一圈"; [SP] section 3.2):
+ *   lse = log(exp(lse1) + exp(lse2)),
+ *   o   = o1 * exp(lse1 - lse) + o2 * exp(lse2 - lse).
+ * o* are [Sq][H][D] float32, lse* are [H][Sq] float32.  o/lse may alias
+ * o1/lse1 or o2/lse2 exactly (in-place accumulation); partial overlap is not
+ * allowed.  Two -inf inputs give (0, -inf).
+ * Errors: CP_ERR_NULL, CP_ERR_SHAPE, CP_ERR_UNSUPPORTED (D % 4 != 0 or
+ * D > 256), CP_ERR_ALIGN (16-byte alignment of o*), CP_ERR_HIP.
+ */
+int cp_lse_merge(const float *o1, const float *lse1, const float *o2, const float *lse2,
+                 float *o, float *lse, int64_t Sq, int H, int D, void *stream);
+
+/*
+ * cp_ring_fwd -- the P-step ring schedule of [HB], section "Ring Attention：
+ * KV 沿环传一圈", played by P virtual ranks on one GPU.  At step t rank r
+ * holds the KV block of rank src = (r - t) mod P, attends its local queries
+ * to it with the block's offsets and merges the result into its running
+ * (out, lse) with the log-sum-exp rule.  With causal != 0, (query chunk,
+ * key chunk) pairs whose keys all come after the queries are skipped
+ * (cp_ring_plan lists them).  For the zigzag layout the KV block of a rank is
+ * its two chunks; each of the rank's two query chunks attends to those of
+ * them it can see.
+ * q, k, v are the whole sequence in natural order: q [S][Hq][D], k/v
+ * [S][Hkv][D].
+ *   rank == -1: every rank; out [S][Hq][D] and lse [Hq][S] in natural order.
+ *   0 <= rank < P: that rank's share only; out [S/P][Hq][D] and lse
+ *   [Hq][S/P] in the rank's local row order (see cp_layout_index).
+ * The merge is fused into the attention epilogue; no workspace is needed.
+ * Errors: as cp_attn_block_fwd, plus CP_ERR_SHAPE when P < 1, rank outside
+ * [-1, P), S not divisible by P (contiguous) or by 2P (zigzag).
+ */
+int cp_ring_fwd(const void *q, const void *k, const void *v, float *out, float *lse,
+                int64_t S, int Hq, int Hkv, int D, int P, cp_layout layout, int rank,
+                int causal, cp_dtype dtype, void *stream);
+
+/*
+ * cp_seq_to_head / cp_head_to_seq -- the Ulysses layout changes of [HB],
+ * section "Ulysses：在序列和头之间转置", done as local repacks: the all-to-all
+ * between P ranks becomes a strided copy on one GPU.  Elements are opaque
+ * (elem_bytes 2 or 4) and copied bit for bit.  Hp = H / P.
+ *
+ * cp_seq_to_head: x is the natural [S][H][D] tensor (all ranks' [S/P][H][D]
+ * shards back to back).
+ *   rank == -1: y = [P][S][Hp][D], y[p][t][j] = x[t][p*Hp + j].
+ *   rank == p : y = [S][Hp][D], rank p's tensor after the all-to-all.
+ * cp_head_to_seq: the inverse.
+ *   rank == -1: x = [P][S][Hp][D] -> y natural [S][H][D].
+ *   rank == p : x = [S][Hp][D] (rank p's head share) is written into head
+ *               slice [p*Hp, (p+1)*Hp) of y [S][H][D]; the other heads of y
+ *               are left untouched, so the P calls together fill y.
+ * x and y must not overlap.  Errors: CP_ERR_NULL, CP_ERR_SHAPE (H % P != 0,
+ * S % P != 0, rank outside [-1, P)), CP_ERR_UNSUPPORTED (elem_bytes),
+ * CP_ERR_HIP.
+ */
+int cp_seq_to_head(const void *x, void *y, int64_t S, int H, int D, int P, int rank,
+                   size_t elem_bytes, void *stream);
+int cp_head_to_seq(const void *x, void *y, int64_t S, int H, int D, int P, int rank,
+                   size_t elem_bytes, void *stream);
+
+/*
+ * cp_layout_index -- host only, synchronous.  idx[j] (j < S/P) receives the
+ * natural sequence position of rank `rank`'s local row j:
+ *   contiguous: rank*S/P + j;
+ *   zigzag (C = S/(2P)): j < C ? rank*C + j : (2P-1-rank)*C + (j - C).
+ * idx is a host array of S/P int32 (so S must be below 2^31).
+ * Errors: CP_ERR_NULL, CP_ERR_SHAPE.
+ */
+int cp_layout_index(cp_layout layout, int64_t S, int P, int rank, int32_t *idx);
+
+/*
+ * cp_ring_plan -- host only, synchronous.  Lists every (rank, step, query
+ * chunk, key chunk) pair the ring visits, in order rank, step, query chunk
+ * in local order, key chunk in local order, each classified SKIP (causal and
+ * the key chunk comes after the query chunk), DIAG (causal and the same
+ * chunk) or FULL.  rank == -1 lists all ranks.  Contiguous: one pair per
+ * step (P-way chunks); zigzag: four pairs per step (2P-way chunks).
+ * *n_pairs is the capacity of `pairs` on entry and the number of pairs on
+ * return; pairs == NULL only queries the count.
+ * Errors: CP_ERR_NULL (n_pairs), CP_ERR_SHAPE, CP_ERR_CAPACITY (the needed
+ * count is still written to *n_pairs).
+ */
+int cp_ring_plan(int64_t S, int P, cp_layout layout, int rank, int causal,
+                 cp_block_pair *pairs, int *n_pairs);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char *cp_last_error(void);
+
+/*
+ * Kernel timing (measurement support).  While enabled, every kernel the
+ * library launches is bracketed by two HIP events recorded on the launch
+ * stream.  cp_timing_read waits for the recorded events, adds their elapsed
+ * times to the totals of the given kernel kind and returns the totals since
+ * the last reset.  Calls are serialised by a mutex; timing adds two event
+ * records per launch.
+ */
+typedef enum {
+    CP_KERNEL_ATTN_BF16 = 0,
+    CP_KERNEL_ATTN_F32 = 1,
+    CP_KERNEL_MERGE = 2,
+    CP_KERNEL_PERMUTE = 3
+} cp_kernel_kind;
+
+int cp_timing_enable(int enable);
+int cp_timing_reset(void);
+int cp_timing_read(cp_kernel_kind kind, double *total_ms, int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CP_ATTN_H */

@@ -1,0 +1,356 @@
+"""HIP path against the oracle, element by element, through the C-ABI.
+
+Tolerances (max abs error against the float64 oracle on the same input
+bytes): float32 path 1e-5 for out and lse; bf16 path (float32
+accumulation) 1e-2 for out and 1e-3 for lse; repacks and index maps bit
+exact.  Fully-masked rows must give exactly (0, -inf).
+
+Small cases compare every output.  The full-size workloads (32K, 64K and
+128K tokens, 32 heads, D = 128) run in the launch configuration the
+benchmark times and compare a seeded sample of rows -- the first and last
+row of every chunk plus uniform draws -- recomputed one by one by the C
+oracle.  Every output buffer sits between guard regions filled with a
+sentinel, checked after each call.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import context_parallelism_cp_amd as cp
+from oracle import attention as OA
+from oracle import native
+from oracle import schedules as OS
+from seeded_inputs import make_qkv, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+F32_TOL = 1e-5
+BF16_OUT_TOL = 1e-2
+BF16_LSE_TOL = 1e-3
+SENTINEL = 12345.0
+GUARD = 1024  # floats on each side
+
+
+def announce(msg):
+    print(f"[gpu case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+class Guarded:
+    """A float32 device tensor with sentinel-filled guard regions around it."""
+
+    def __init__(self, *shape):
+        n = int(np.prod(shape))
+        self.buf = torch.full((n + 2 * GUARD,), SENTINEL, device=DEV, dtype=torch.float32)
+        self.t = self.buf[GUARD:GUARD + n].view(*shape)
+
+    def check(self):
+        g = torch.cat([self.buf[:GUARD], self.buf[-GUARD:]])
+        assert bool((g == SENTINEL).all()), "a kernel wrote outside its output buffer"
+
+
+def compare(out, lse, ref_out, ref_lse, tol_out, tol_lse, what=""):
+    o = out.detach().double().cpu().numpy() if torch.is_tensor(out) else out
+    lv = lse.detach().double().cpu().numpy() if torch.is_tensor(lse) else lse
+    assert np.array_equal(np.isneginf(lv), np.isneginf(ref_lse)), f"{what}: -inf pattern of lse"
+    assert not np.isnan(o).any() and not np.isnan(lv).any(), f"{what}: NaN"
+    fin = np.isfinite(ref_lse)
+    err_l = float(np.abs(lv[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
+    err_o = float(np.abs(o - ref_out).max()) if o.size else 0.0
+    print(f"    {what}: max|dout| = {err_o:.3e}, max|dlse| = {err_l:.3e}", flush=True)
+    assert err_o <= tol_out, f"{what}: out error {err_o}"
+    assert err_l <= tol_lse, f"{what}: lse error {err_l}"
+    empty = np.isneginf(ref_lse).T  # [rows, H]
+    assert np.all(o[empty] == 0.0), f"{what}: fully-masked rows must be 0"
+
+
+def dev(*ts):
+    return [t.to(DEV).contiguous() for t in ts]
+
+
+# ----------------------------------------------------------------- float32
+def test_f32_block_single_pass_page_inputs():
+    announce("f32 block fwd, make_qkv() S=32 H=8 D=16")
+    q, k, v = make_qkv()
+    out, lse = Guarded(32, 8, 16), Guarded(8, 32)
+    cp.cp_attn_block_fwd(*dev(q, k, v), out.t, lse.t)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    ro, rl = OA.attention(q, k, v)
+    compare(out.t, lse.t, ro, rl, F32_TOL, F32_TOL, "page inputs")
+
+
+@pytest.mark.parametrize("Sq,Sk,Hq,Hkv,D,qo,ko,causal", [
+    (37, 53, 4, 2, 16, 20, 5, True),
+    (37, 53, 4, 2, 16, 0, 0, False),
+    (130, 70, 2, 1, 128, 100, 90, True),
+    (65, 129, 3, 3, 40, 64, 0, True),
+    (10, 10, 2, 2, 16, 0, 7, True),      # first rows see no key
+    (5, 8, 2, 2, 16, 0, 100, True),      # no row sees a key
+])
+def test_f32_block_offsets_and_ragged(Sq, Sk, Hq, Hkv, D, qo, ko, causal):
+    announce(f"f32 block fwd Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} D={D} qo={qo} ko={ko} causal={causal}")
+    q, _, _ = make_qkv(S=Sq, H=Hq, D=D, seed=Sq)
+    _, k, v = make_qkv(S=Sk, H=Hkv, D=D, seed=Sk + 1)
+    out, lse = Guarded(Sq, Hq, D), Guarded(Hq, Sq)
+    cp.cp_attn_block_fwd(*dev(q, k, v), out.t, lse.t, q_offset=qo, k_offset=ko, causal=causal)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    ro, rl = OA.attention(q, k, v, causal=causal, q_offset=qo, k_offset=ko)
+    compare(out.t, lse.t, ro, rl, F32_TOL, F32_TOL, "f32 block")
+
+
+def test_f32_empty_kv():
+    announce("f32 block fwd Sk=0")
+    q, k, v = make_qkv(S=8, H=2, D=16)
+    out, lse = Guarded(8, 2, 16), Guarded(2, 8)
+    cp.cp_attn_block_fwd(q.to(DEV), k[:0].to(DEV), v[:0].to(DEV), out.t, lse.t)
+    torch.cuda.synchronize()
+    assert bool((out.t == 0).all()) and bool(torch.isneginf(lse.t).all())
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+def test_f32_ring_page_inputs(layout):
+    announce(f"f32 ring P=4 {layout} on make_qkv()")
+    q, k, v = make_qkv()
+    ro, rl = OA.attention(q, k, v)
+    dq, dk, dv = dev(q, k, v)
+    out, lse = Guarded(32, 8, 16), Guarded(8, 32)
+    cp.cp_ring_fwd(dq, dk, dv, 4, layout, -1, out=out.t, lse=lse.t)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    compare(out.t, lse.t, ro, rl, F32_TOL, F32_TOL, f"{layout} all ranks")
+    lay = cp.LAYOUTS[layout]
+    for r in range(4):
+        o2, l2 = Guarded(8, 8, 16), Guarded(8, 8)
+        cp.cp_ring_fwd(dq, dk, dv, 4, layout, r, out=o2.t, lse=l2.t)
+        torch.cuda.synchronize()
+        o2.check(), l2.check()
+        idx = OS.layout_index(lay, 32, 4, r)
+        compare(o2.t, l2.t, ro[idx], rl[:, idx], F32_TOL, F32_TOL, f"{layout} rank {r}")
+
+
+def test_f32_ring_noncausal():
+    announce("f32 ring P=3 zigzag non-causal")
+    q, k, v = make_qkv(S=48, H=2, D=16, seed=4)
+    ro, rl = OA.attention(q, k, v, causal=False)
+    out, lse = cp.cp_ring_fwd(*dev(q, k, v), 3, "zigzag", -1, causal=False)
+    torch.cuda.synchronize()
+    compare(out, lse, ro, rl, F32_TOL, F32_TOL, "non-causal ring")
+
+
+def test_f32_ulysses_page_inputs():
+    announce("f32 Ulysses P=4 on make_qkv()")
+    q, k, v = make_qkv()
+    P = 4
+    dq, dk, dv = dev(q, k, v)
+    heads = [cp.cp_seq_to_head(x, P, -1) for x in (dq, dk, dv)]
+    torch.cuda.synchronize()
+    ref_heads = [OS.seq_to_head([x.numpy()[r * 8:(r + 1) * 8] for r in range(P)], P)
+                 for x in (q, k, v)]
+    for got, want in zip(heads, ref_heads):
+        for p in range(P):
+            assert np.array_equal(got[p].cpu().numpy(), want[p])   # bit exact
+    assert tuple(heads[0][0].shape) == (32, 2, 16)
+    outs = torch.empty(P, 32, 2, 16, device=DEV)
+    for p in range(P):
+        o, _ = cp.cp_attn_block_fwd(heads[0][p], heads[1][p], heads[2][p])
+        outs[p] = o
+    y = torch.full((32, 8, 16), SENTINEL, device=DEV)
+    cp.cp_head_to_seq(outs, y, P, -1)
+    torch.cuda.synchronize()
+    ro, _ = OA.attention(q, k, v)
+    compare(y, np.zeros((8, 32)), ro, np.zeros((8, 32)), F32_TOL, F32_TOL, "Ulysses out")
+    # one rank at a time gives the same bytes
+    y2 = torch.full((32, 8, 16), SENTINEL, device=DEV)
+    for p in range(P):
+        hp = cp.cp_seq_to_head(dq, P, p)
+        assert torch.equal(hp, heads[0][p])
+        cp.cp_head_to_seq(outs[p].contiguous(), y2, P, p)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    back = torch.empty_like(dq)
+    cp.cp_head_to_seq(heads[0], back, P, -1)
+    torch.cuda.synchronize()
+    assert torch.equal(back, dq)
+
+
+# ------------------------------------------------------------------ merge
+@pytest.mark.parametrize("Sq,H,D", [(33, 3, 128), (100, 8, 16), (7, 2, 256), (5, 1, 4)])
+def test_merge_against_oracle(Sq, H, D):
+    announce(f"lse merge Sq={Sq} H={H} D={D}")
+    g = torch.Generator().manual_seed(Sq * H + D)
+    o1, o2 = torch.randn(Sq, H, D, generator=g), torch.randn(Sq, H, D, generator=g)
+    l1, l2 = torch.randn(H, Sq, generator=g) * 4, torch.randn(H, Sq, generator=g) * 4
+    l1[0, 0] = -float("inf")                    # one side empty
+    l2[-1, -1] = -float("inf")
+    l1[0, -1] = l2[0, -1] = -float("inf")       # both empty
+    o1[-1, 0] = 0.0
+    o2[-1, 0] = 0.0
+    ro, rl = OA.lse_merge(o1, l1, o2, l2)
+    out, lse = Guarded(Sq, H, D), Guarded(H, Sq)
+    cp.cp_lse_merge(*dev(o1, l1, o2, l2), out.t, lse.t)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    compare(out.t, lse.t, ro, rl, F32_TOL, F32_TOL, "merge")
+    # in place: o, lse alias o1, lse1
+    d1, dl1, d2, dl2 = dev(o1, l1, o2, l2)
+    cp.cp_lse_merge(d1, dl1, d2, dl2, d1, dl1)
+    torch.cuda.synchronize()
+    compare(d1, dl1, ro, rl, F32_TOL, F32_TOL, "merge in place")
+
+
+# ------------------------------------------------------------------ bf16
+def oracle_rows(q, k, v, rows, **kw):
+    return native.attention_rows(q, k, v, rows=rows, **kw)
+
+
+@pytest.mark.parametrize("Sq,Sk,Hq,Hkv,qo,ko,causal", [
+    (300, 517, 4, 2, 400, 100, True),
+    (300, 517, 4, 2, 0, 0, False),
+    (128, 128, 2, 2, 0, 0, True),
+    (257, 300, 2, 1, 0, 200, True),    # rows 0..198 see no key
+    (64, 1000, 8, 2, 999, 0, True),
+    (1, 1, 1, 1, 5, 5, True),
+])
+def test_bf16_block_small(Sq, Sk, Hq, Hkv, qo, ko, causal):
+    announce(f"bf16 block fwd Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} qo={qo} ko={ko} causal={causal}")
+    q, _, _ = make_qkv(S=Sq, H=Hq, D=128, seed=Sq, dtype=torch.bfloat16)
+    _, k, v = make_qkv(S=Sk, H=Hkv, D=128, seed=Sk + 7, dtype=torch.bfloat16)
+    out, lse = Guarded(Sq, Hq, 128), Guarded(Hq, Sq)
+    cp.cp_attn_block_fwd(*dev(q, k, v), out.t, lse.t, q_offset=qo, k_offset=ko, causal=causal)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    ro, rl = oracle_rows(q, k, v, None, causal=causal, q_offset=qo, k_offset=ko)
+    compare(out.t, lse.t, ro, rl, BF16_OUT_TOL, BF16_LSE_TOL, "bf16 block")
+
+
+def test_bf16_block_empty_kv():
+    announce("bf16 block fwd Sk=0")
+    q, k, v = make_qkv(S=130, H=2, D=128, dtype=torch.bfloat16)
+    out, lse = cp.cp_attn_block_fwd(q.to(DEV), k[:0].to(DEV), v[:0].to(DEV))
+    torch.cuda.synchronize()
+    assert bool((out == 0).all()) and bool(torch.isneginf(lse).all())
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+def test_bf16_ring_small_every_rank(layout):
+    S, H, P = 2048, 4, 4
+    announce(f"bf16 ring S={S} H={H} P={P} {layout}")
+    q, k, v = make_qkv(S=S, H=H, D=128, seed=11, dtype=torch.bfloat16)
+    ro, rl = oracle_rows(q, k, v, None)
+    dq, dk, dv = dev(q, k, v)
+    out, lse = Guarded(S, H, 128), Guarded(H, S)
+    cp.cp_ring_fwd(dq, dk, dv, P, layout, -1, out=out.t, lse=lse.t)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    compare(out.t, lse.t, ro, rl, BF16_OUT_TOL, BF16_LSE_TOL, f"{layout} all ranks")
+    for r in range(P):
+        o2, l2 = cp.cp_ring_fwd(dq, dk, dv, P, layout, r)
+        torch.cuda.synchronize()
+        idx = OS.layout_index(cp.LAYOUTS[layout], S, P, r)
+        compare(o2, l2, ro[idx], rl[:, idx], BF16_OUT_TOL, BF16_LSE_TOL, f"{layout} rank {r}")
+
+
+# ------------------------------------------------------- full-size workloads
+@functools.lru_cache(maxsize=1)
+def inputs_cached(S, H, Hkv):
+    q, k, v = make_qkv(S=S, H=H, D=128, seed=0, dtype=torch.bfloat16, Hkv=Hkv)
+    return q, k, v
+
+
+def chunk_edge_rows(n_local, chunk, n_random, seed):
+    edges = set()
+    for c0 in range(0, n_local, chunk):
+        edges.update({c0, c0 + chunk - 1})
+    rnd = sample_rows(n_local, n_random + 2, seed=seed).tolist()
+    return np.array(sorted(edges.union(rnd)), dtype=np.int64)
+
+
+def check_share(out, lse, q, k, v, positions, local_rows, what):
+    ro, rl = oracle_rows(q, k, v, positions[local_rows])
+    o = out[torch.from_numpy(local_rows).to(DEV)].double().cpu().numpy()
+    lv = lse[:, torch.from_numpy(local_rows).to(DEV)].double().cpu().numpy()
+    compare(o, lv, ro, rl, BF16_OUT_TOL, BF16_LSE_TOL, what)
+
+
+def test_full_ring_32k_all_ranks():
+    S, H, P = 32768, 32, 8
+    announce(f"bf16 ring S={S} H={H} P={P} zigzag, all ranks (sampled rows)")
+    q, k, v = inputs_cached(S, H, H)
+    dq, dk, dv = dev(q, k, v)
+    out, lse = Guarded(S, H, 128), Guarded(H, S)
+    cp.cp_ring_fwd(dq, dk, dv, P, "zigzag", -1, out=out.t, lse=lse.t)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    rows = chunk_edge_rows(S, S // (2 * P), 16, seed=2)
+    check_share(out.t, lse.t, q, k, v, np.arange(S), rows, "32K all ranks")
+
+
+@pytest.mark.parametrize("layout,rank", [("contiguous", 3), ("contiguous", 0), ("zigzag", 0),
+                                         ("zigzag", 3)])
+def test_full_rank_share_64k(layout, rank):
+    S, H, P = 65536, 32, 4
+    announce(f"bf16 ring S={S} H={H} P={P} {layout} rank {rank} (sampled rows)")
+    q, k, v = inputs_cached(S, H, H)
+    dq, dk, dv = dev(q, k, v)
+    out, lse = Guarded(S // P, H, 128), Guarded(H, S // P)
+    cp.cp_ring_fwd(dq, dk, dv, P, layout, rank, out=out.t, lse=lse.t)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    lay = cp.LAYOUTS[layout]
+    chunk = S // P if layout == "contiguous" else S // (2 * P)
+    rows = chunk_edge_rows(S // P, chunk, 8, seed=3 + rank)
+    check_share(out.t, lse.t, q, k, v, OS.layout_index(lay, S, P, rank), rows,
+                f"64K {layout} rank {rank}")
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_full_rank_share_128k(rank):
+    S, H, P = 131072, 32, 8
+    announce(f"bf16 ring S={S} H={H} P={P} zigzag rank {rank} (sampled rows)")
+    q, k, v = inputs_cached(S, H, H)
+    dq, dk, dv = dev(q, k, v)
+    out, lse = Guarded(S // P, H, 128), Guarded(H, S // P)
+    cp.cp_ring_fwd(dq, dk, dv, P, "zigzag", rank, out=out.t, lse=lse.t)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    rows = chunk_edge_rows(S // P, S // (2 * P), 8, seed=5 + rank)
+    check_share(out.t, lse.t, q, k, v, OS.layout_index(cp.CP_LAYOUT_ZIGZAG, S, P, rank), rows,
+                f"128K zigzag rank {rank}")
+
+
+def test_full_ulysses_gqa_128k():
+    S, Hq, Hkv, P, p = 131072, 32, 8, 8, 5
+    announce(f"Ulysses GQA S={S} Hq={Hq} Hkv={Hkv} P={P} rank {p} (sampled rows)")
+    q, k, v = inputs_cached(S, Hq, Hkv)
+    dq, dk, dv = dev(q, k, v)
+    ql = cp.cp_seq_to_head(dq, P, p)
+    kl = cp.cp_seq_to_head(dk, P, p)
+    vl = cp.cp_seq_to_head(dv, P, p)
+    torch.cuda.synchronize()
+    # bit-exact head-slice identity
+    assert torch.equal(ql, dq[:, 4 * p:4 * p + 4]) and torch.equal(kl, dk[:, p:p + 1])
+    out_l, lse_l = Guarded(S, 4, 128), Guarded(4, S)
+    cp.cp_attn_block_fwd(ql, kl, vl, out_l.t, lse_l.t)
+    y = torch.full((S, Hq, 128), SENTINEL, device=DEV)
+    cp.cp_head_to_seq(out_l.t, y, P, p)
+    torch.cuda.synchronize()
+    out_l.check(), lse_l.check()
+    untouched = torch.cat([y[:, :4 * p], y[:, 4 * p + 4:]], dim=1)
+    assert bool((untouched == SENTINEL).all())
+    assert torch.equal(y[:, 4 * p:4 * p + 4], out_l.t)
+    rows = chunk_edge_rows(S, S // P, 16, seed=9)
+    ro, rl = oracle_rows(q[:, 4 * p:4 * p + 4].contiguous(), k[:, p:p + 1].contiguous(),
+                         v[:, p:p + 1].contiguous(), rows)
+    idx = torch.from_numpy(rows).to(DEV)
+    compare(y[idx][:, 4 * p:4 * p + 4].double().cpu().numpy(),
+            lse_l.t[:, idx].double().cpu().numpy(), ro, rl, BF16_OUT_TOL, BF16_LSE_TOL,
+            "Ulysses GQA 128K")
+    # the same rows from the GQA definition over all 32 query heads (head h reads KV h // 4)
+    ro_all, _ = oracle_rows(q, k, v, rows[:4])
+    np.testing.assert_allclose(ro_all[:, 4 * p:4 * p + 4], ro[:4], atol=1e-12)
