@@ -5,26 +5,40 @@
 // "哪些运算可以直接切", function attention()): s = q.k / sqrt(D), keys after
 // the query's absolute position masked, lse = logsumexp(s), out =
 // softmax(s) v.  The softmax runs in the streaming (m, l, o) form ("Sequence
-// Parallel vs Context Parallel" blog, section 3.2), in base 2 with
-// log2(e)/sqrt(D) folded into one multiply; lse is converted back to nats.
+// Parallel vs Context Parallel" blog, section 3.2) in base 2, with
+// log2(e)/sqrt(D) folded into one fused multiply-add; lse is returned in nats.
 //
 // Work decomposition
-//   * A workgroup of 4 wavefronts owns BM = 128 query rows of one head; each
-//     wavefront owns 32 rows.  Keys stream through LDS BN = 64 at a time.
+//   * A workgroup of 4 wavefronts owns BM = 256 query rows of one head; each
+//     wavefront owns 64 rows as two 32-row blocks, so every K or V fragment
+//     read from LDS feeds two MFMAs.  One wavefront per SIMD.
+//   * Keys stream through LDS BN = 64 at a time in a 3-stage ring filled by
+//     direct global->LDS 16-byte loads (no staging registers).  K and V tiles
+//     are both stored row-major with a 16-byte-chunk XOR swizzle that keeps
+//     the K reads (ds_read_b128) and the V transpose reads
+//     (ds_read_b64_tr_b16) free of bank conflicts.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from LDS, B = 16 dims x
-//     32 queries held in VGPRs for the whole kernel).  In the accumulator
-//     layout lane l then holds 16 scores of query l%32, so row max and row sum
-//     are in-lane reductions plus one exchange with lane l^32.
-//   * The output is accumulated transposed, O^T += V^T P^T.  The B operand
-//     P^T needs, per lane, 8 scores of its own query: exactly 8 consecutive
-//     accumulator registers, converted to bf16 in place (no data movement).
-//     The key order inside a 16-key MFMA step is permuted consistently for P
-//     and V; the A operand V^T is read from a d-major copy of the V tile in
-//     LDS.  O^T keeps each lane on one query, so the rescale by
-//     exp2(m_old - m_new) is a per-lane scalar.
-//   * Tiles strictly below the causal diagonal run without the mask; only
-//     tiles crossing the diagonal (or a ragged end) compare positions.
+//     32 queries kept in VGPRs for the whole kernel).  In the accumulator
+//     layout lane l holds 16 scores of query l%32, so row max and row sum are
+//     in-lane reductions plus one exchange with lane l^32.
+//   * The output is accumulated transposed, O^T += V^T P^T.  P^T's fragment
+//     for a 16-key step is 8 consecutive accumulator registers of the lane,
+//     converted to bf16 in place; the key order inside the step is permuted
+//     identically for P and V, and the V^T fragment is two transpose reads of
+//     the row-major V tile.  Each lane keeps one query per block, so the
+//     rescale by exp2(m_old - m_new) is a per-lane scalar.
+//   * Software pipeline: the S^T MFMAs of tile t+1 are issued before the
+//     softmax of tile t, so the VALU work of one tile overlaps the matrix
+//     work of the next.
+//   * The running max is only raised when a tile's max exceeds it by more
+//     than 2^8 (in base 2), so the 128-register rescale of O is rare; the
+//     exponentials stay <= 2^8 and the final O / l is unchanged.
+//   * Tiles strictly below the causal diagonal run without the mask; tiles
+//     crossing it (or a ragged end) compare absolute positions.
+//   * Workgroups are mapped XCD-aware: the heads of a launch are spread over
+//     the 8 XCDs, a head's tiles stay on its XCD(s), and every XCD walks its
+//     tiles heaviest-first (most visible keys first).
 //   * The epilogue either writes (out, lse) or folds the block result into
 //     the (out, lse) already stored (log-sum-exp merge, handbook section
 //     "Ring Attention：KV 沿环传一圈").
@@ -32,242 +46,455 @@
 
 #include <math.h>
 
+#include <algorithm>
+#include <type_traits>
+#include <utility>
+#include <vector>
+
 namespace cpattn {
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int HD = 128;            // head dimension
-constexpr int BM = 128;            // query rows per workgroup
-constexpr int BN = 64;             // keys per LDS tile
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int HD = 128;                 // head dimension
+constexpr int BN = 64;                  // keys per LDS tile
+constexpr int QB = 2;                   // 32-row query blocks per wavefront
 constexpr int kWaves = 4;
+constexpr int BM = kWaves * QB * 32;    // 256 query rows per workgroup
 constexpr int kThreads = kWaves * 64;
-constexpr int VT_LD = 66;          // bf16 per row of the d-major V tile (padded)
+constexpr int kStages = 3;
+constexpr int kTileBytes = BN * HD * 2;             // 16 KiB per K or V tile
+constexpr int kStageBytes = 2 * kTileBytes;         // K then V
+constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
+constexpr int kMaxOrder = 768;          // tiles of the heaviest-first table
+constexpr int kXcds = 8;
 
 struct TileMap {
-    int32_t start[kMaxQSegs + 1];  // prefix sum of row tiles over the segments
+    int32_t start[kMaxQSegs + 1];       // prefix sum of row tiles over the segments
+    int32_t total;                      // row tiles in the launch
+    int32_t use_order;                  // order[] valid (total <= kMaxOrder)
+    int32_t xcd_mode;                   // 0 linear, 1 Hq % 8 == 0, 2 8 % Hq == 0
+    int32_t slots;                      // tile positions walked per XCD lane
+    uint16_t order[kMaxOrder];          // tile positions, heaviest first
 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
-__device__ __forceinline__ float wave_xor32(float x)
+// Byte offset inside a tile of the 16-byte chunk c of row r.
+__device__ __forceinline__ int tile_off(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
+
+__device__ __forceinline__ bf16x8 lds_b128(const char LDS_AS *base, int off)
 {
-    return __shfl_xor(x, 32, 64);
+    return __builtin_bit_cast(bf16x8, *(const u32x4 LDS_AS *)(base + off));
 }
 
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnLaunch a, TileMap tm,
-                                                             float scale_log2)
+__device__ __forceinline__ i16x4 lds_tr(const char LDS_AS *base, int off)
 {
-    __shared__ u32x4 k_lds[BN * 16];                 // [key][16-byte chunk], XOR-swizzled
-    __shared__ unsigned short vt_lds[HD * VT_LD];    // [d][key], padded rows
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(base + off));
+}
 
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Issue the direct-to-LDS loads of one K tile and one V tile (keys
+// key0 .. key0+63 of a KV segment) into `stage`.  Rows past the segment end
+// are clamped to its last row; their scores are masked.
+__device__ __forceinline__ void load_tile(char LDS_AS *stage, const __bf16 *kbase,
+                                          const __bf16 *vbase, int64_t row_stride,
+                                          int64_t key0, int64_t len, int wave, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int blk = wave * 4 + i;              // 1 KiB block of the tile
+        const int r = blk * 4 + (lane >> 4);       // tile row this lane fills
+        const int c = (lane & 15) ^ swz(r);        // logical chunk for this LDS slot
+        int64_t key = key0 + r;
+        key = key < len ? key : len - 1;
+        const int64_t off = key * row_stride + c * 8;
+        __builtin_amdgcn_global_load_lds((const void *)(kbase + off),
+                                         (void LDS_AS *)(stage + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(vbase + off),
+                                         (void LDS_AS *)(stage + kTileBytes + blk * 1024), 16,
+                                         0, 0);
+    }
+}
+
+struct TileRef {
+    int seg;          // KV segment index
+    int64_t key0;     // first key of the tile within the segment
+};
+
+// The three pipeline stages are distinct LDS objects, and every access names
+// its stage at compile time: the compiler then sees that the loads landing
+// in one stage cannot alias reads of another and does not wait for them.
+__shared__ __attribute__((aligned(1024))) char g_stage0[kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_stage1[kStageBytes];
+__shared__ __attribute__((aligned(1024))) char g_stage2[kStageBytes];
+
+template <int ST>
+__device__ __forceinline__ char LDS_AS *stage_base()
+{
+    if constexpr (ST == 0)
+        return (char LDS_AS *)g_stage0;
+    else if constexpr (ST == 1)
+        return (char LDS_AS *)g_stage1;
+    else
+        return (char LDS_AS *)g_stage2;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnLaunch a, TileMap tm,
+                                                                float scale_log2)
+{
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
-    const int h = blockIdx.y;
 
+    // ---- which (head, row tile) this workgroup owns
+    int h, tp;
+    {
+        const int bid = blockIdx.x;
+        if (tm.xcd_mode == 1) {
+            const int x = bid % kXcds, s = bid / kXcds;
+            const int hpx = a.Hq / kXcds;
+            h = x + kXcds * (s % hpx);
+            tp = s / hpx;
+        } else if (tm.xcd_mode == 2) {
+            const int x = bid % kXcds, s = bid / kXcds;
+            const int xph = kXcds / a.Hq;
+            h = x % a.Hq;
+            tp = s * xph + x / a.Hq;
+        } else {
+            h = bid / tm.total;
+            tp = bid % tm.total;
+        }
+        if (h >= a.Hq || tp >= tm.total)
+            return;
+    }
+    int tile_lin;
+    if (tm.use_order) {
+        tile_lin = tm.order[tp];
+    } else {
+        tile_lin = tp;
+    }
     int s = 0;
-    while (s + 1 < a.n_q && (int)blockIdx.x >= tm.start[s + 1])
+    while (s + 1 < a.n_q && tile_lin >= tm.start[s + 1])
         ++s;
     const QSeg &qs = a.qs[s];
-    const int n_tiles_seg = tm.start[s + 1] - tm.start[s];
-    // heavy tiles (later rows see more keys under the causal mask) first
-    const int tile = n_tiles_seg - 1 - ((int)blockIdx.x - tm.start[s]);
+    int tile = tile_lin - tm.start[s];
+    if (!tm.use_order && a.causal)   // without the table: later rows (more keys) first
+        tile = (tm.start[s + 1] - tm.start[s]) - 1 - tile;
     const int64_t tile_row0 = (int64_t)tile * BM;
-    const int64_t my_row = tile_row0 + wave * 32 + l32;
-    const bool row_ok = my_row < qs.len;
-    const int64_t my_pos = qs.pos0 + my_row;
     const int g = h / (a.Hq / a.Hkv);
 
     const __bf16 *qg = (const __bf16 *)a.q;
-    const __bf16 *kg = (const __bf16 *)a.k;
-    const __bf16 *vg = (const __bf16 *)a.v;
+    const int64_t q_stride = (int64_t)a.Hq * HD;
+    const int64_t kv_stride = (int64_t)a.Hkv * HD;
+    const __bf16 *kg = (const __bf16 *)a.k + g * HD;
+    const __bf16 *vg = (const __bf16 *)a.v + g * HD;
 
-    // Q^T fragments: B operand of step sd holds dims 16*sd + 8*hi + [0, 8) of row l32.
-    bf16x8 qf[8];
-    {
-        const int64_t r = row_ok ? my_row : 0;
-        const u32x4 *src = (const u32x4 *)(qg + ((qs.row0 + r) * a.Hq + h) * HD + 8 * hi);
+    // ---- rows of this wavefront: block qb holds rows wave*64 + qb*32 + [0, 32)
+    int64_t my_row[QB];
+    bool row_ok[QB];
+    int64_t my_pos[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        my_row[qb] = tile_row0 + wave * 64 + qb * 32 + l32;
+        row_ok[qb] = my_row[qb] < qs.len;
+        my_pos[qb] = qs.pos0 + my_row[qb];
+    }
+
+    // Q^T fragments: B operand of step sd holds dims 16*sd + 8*hi + [0, 8).
+    bf16x8 qf[QB][8];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int64_t r = row_ok[qb] ? my_row[qb] : 0;
+        const u32x4 *src = (const u32x4 *)(qg + (qs.row0 + r) * q_stride + h * HD + 8 * hi);
 #pragma unroll
         for (int sd = 0; sd < 8; ++sd) {
             u32x4 x = src[2 * sd];
-            if (!row_ok)
+            if (!row_ok[qb])
                 x = u32x4{0, 0, 0, 0};
-            qf[sd] = as_bf16x8(x);
+            qf[qb][sd] = __builtin_bit_cast(bf16x8, x);
         }
     }
 
-    f32x16 o_acc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        o_acc[i] = f32x16{};
-    float m_run = -INFINITY;   // running max, log2 units
-    float l_run = 0.f;         // running sum of exp2(s - m_run)
-
+    // ---- the tile stream: every KV segment's tiles up to the causal bound
     const int64_t first_pos = qs.pos0 + tile_row0;
     const int64_t last_pos = qs.pos0 + min(tile_row0 + BM, qs.len) - 1;
-
+    int seg_tiles[2] = {0, 0};
     for (int kv_i = 0; kv_i < qs.n_kv; ++kv_i) {
-        const KvSeg kv = qs.kv[kv_i];
+        const KvSeg &kv = qs.kv[kv_i];
         int64_t n_keys = kv.len;
         if (a.causal)
             n_keys = min(max(last_pos - kv.pos0 + 1, (int64_t)0), kv.len);
-        for (int64_t key0 = 0; key0 < n_keys; key0 += BN) {
-            // ---- stage K (swizzled, row-major) and V (transposed) in LDS
-            __syncthreads();
-#pragma unroll
-            for (int it = 0; it < (BN * 16) / kThreads; ++it) {
-                const int cid = it * kThreads + threadIdx.x;
-                const int row = cid >> 4;
-                const int c = cid & 15;
-                const int64_t key = key0 + row;
-                u32x4 kx = u32x4{0, 0, 0, 0};
-                u32x4 vx = u32x4{0, 0, 0, 0};
-                if (key < kv.len) {
-                    const int64_t off = ((kv.row0 + key) * a.Hkv + g) * HD + c * 8;
-                    kx = *(const u32x4 *)(kg + off);
-                    vx = *(const u32x4 *)(vg + off);
-                }
-                k_lds[row * 16 + (c ^ (row & 15))] = kx;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vt_lds[(c * 8 + 2 * e) * VT_LD + row] = (unsigned short)(vx[e] & 0xffffu);
-                    vt_lds[(c * 8 + 2 * e + 1) * VT_LD + row] = (unsigned short)(vx[e] >> 16);
-                }
-            }
-            __syncthreads();
+        seg_tiles[kv_i] = (int)((n_keys + BN - 1) / BN);
+    }
+    const int n_tiles = seg_tiles[0] + seg_tiles[1];
 
-            // ---- S^T = K Q^T for two 32-key blocks
-            f32x16 sc[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                sc[kb] = f32x16{};
-                const int row = kb * 32 + l32;
-#pragma unroll
-                for (int sd = 0; sd < 8; ++sd) {
-                    const int c = 2 * sd + hi;
-                    const bf16x8 kf = as_bf16x8(k_lds[row * 16 + (c ^ (row & 15))]);
-                    sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[sd], sc[kb], 0, 0, 0);
-                }
-            }
+    auto tile_ref = [&](int t) {
+        TileRef r;
+        r.seg = t < seg_tiles[0] ? 0 : 1;
+        r.key0 = (int64_t)(r.seg == 0 ? t : t - seg_tiles[0]) * BN;
+        return r;
+    };
+    // loads of tile t into stage ST (ST == t % 3)
+    auto issue = [&](int t, auto st) {
+        if (t < n_tiles) {
+            const TileRef r = tile_ref(t);
+            const KvSeg &kv = qs.kv[r.seg];
+            load_tile(stage_base<decltype(st)::value>(), kg + kv.row0 * kv_stride,
+                      vg + kv.row0 * kv_stride, kv_stride, r.key0, kv.len, wave, lane);
+        }
+    };
 
-            // ---- scale, mask, running max
-            const bool need_mask =
-                (key0 + BN > kv.len) || (a.causal && kv.pos0 + key0 + BN - 1 > first_pos);
+    f32x16 o_acc[QB][4];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            o_acc[qb][i] = f32x16{};
+    float m_run[QB], l_run[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m_run[qb] = -INFINITY;
+        l_run[qb] = 0.f;
+    }
+
+    // S^T = K Q^T for sub-tile u (32 keys: half u%2 of LDS tile u/2): sc[qb].
+    // per-lane byte offsets of the K fragments inside a 32-row half tile
+    int k_off[8];
+#pragma unroll
+    for (int sd = 0; sd < 8; ++sd)
+        k_off[sd] = tile_off(l32, 2 * sd + hi);
+    // scores of sub-tile u, whose tile sits in stage ST
+    auto scores = [&](int u, f32x16 (&sc)[QB], auto st) {
+        const char LDS_AS *kt = stage_base<decltype(st)::value>() + (u & 1) * 32 * 256;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            sc[qb] = f32x16{};
+#pragma unroll
+        for (int sd = 0; sd < 8; ++sd) {
+            const bf16x8 kf = lds_b128(kt, k_off[sd]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][sd], sc[qb], 0, 0, 0);
+        }
+    };
+
+    // V^T fragment for 16-key step ks of a tile and 32-dim block db (two
+    // transpose reads; see the key order in the header comment).
+    const int grp = lane >> 4;          // 16-lane group
+    const int gi = lane & 15;
+    // rows 16*ks + r0 and +8 share swz(r0) because swz depends on row % 8
+    int v_off[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const int dcol = db * 32 + 16 * (grp & 1) + 4 * (gi & 3);   // first of 4 columns
+        const int r0 = 4 * (grp >> 1) + (gi >> 2);
+        v_off[db] = tile_off(r0, dcol >> 3) + (dcol & 7) * 2;
+    }
+    auto v_frag = [&](const char LDS_AS *vt, int ks, int db) {
+        const i16x4 lo = lds_tr(vt, ks * 16 * 256 + v_off[db]);
+        const i16x4 up = lds_tr(vt, ks * 16 * 256 + 8 * 256 + v_off[db]);
+        const bf16x4 blo = __builtin_bit_cast(bf16x4, lo);
+        const bf16x4 bup = __builtin_bit_cast(bf16x4, up);
+        return __builtin_shufflevector(blo, bup, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+
+    const int n_sub = 2 * n_tiles;
+
+    // One pipeline step: scores of sub-tile u+1 (into nxt), softmax of
+    // sub-tile u (in cur), then O^T += V^T P^T for sub-tile u.  J = u mod 6
+    // fixes the stages: tile t lives in stage t % 3.
+    auto step = [&](int u, f32x16 (&cur)[QB], f32x16 (&nxt)[QB], auto j) {
+        constexpr int J = decltype(j)::value;
+        constexpr int ST_V = (J / 2) % 3;                 // tile u/2
+        constexpr int ST_K = ((J + 1) / 2) % 3;           // tile (u+1)/2
+        constexpr int ST_NEW = ((J + 1) / 2 + 1) % 3;     // tile (u+1)/2 + 1
+        if ((J & 1) && u + 1 < n_sub) {
+            // next LDS tile complete in every wavefront; the stage the new
+            // loads overwrite is no longer read
+            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            issue((u + 1) / 2 + 1, std::integral_constant<int, ST_NEW>{});
+        }
+        if (u + 1 < n_sub)
+            scores(u + 1, nxt, std::integral_constant<int, ST_K>{});
+
+        const int t = u >> 1;
+        const TileRef r = tile_ref(t);
+        const KvSeg &kv = qs.kv[r.seg];
+        const int64_t key0 = r.key0 + (u & 1) * 32;      // first key of the sub-tile
+        const bool need_mask = (key0 + 32 > kv.len) ||
+                               (a.causal && kv.pos0 + key0 + 31 > first_pos);
+        float alpha[QB];
+        bool any_rescale = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
             float mx = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float x = sc[kb][i] * scale_log2;
-                    if (need_mask) {
-                        const int key = kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-                        const bool dead = (key0 + key >= kv.len) ||
-                                          (a.causal && kv.pos0 + key0 + key > my_pos);
-                        x = dead ? -INFINITY : x;
-                    }
-                    sc[kb][i] = x;
-                    mx = fmaxf(mx, x);
-                }
-            }
-            mx = fmaxf(mx, wave_xor32(mx));
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            float rs = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            if (need_mask) {
+                // key k of the sub-tile (0..31) is visible iff k <= lim
+                int64_t lim = kv.len - 1 - key0;
+                if (a.causal)
+                    lim = min(lim, my_pos[qb] - kv.pos0 - key0);
+                const int lim_l = (int)max(min(lim, (int64_t)64), (int64_t)-1) - 4 * hi;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(sc[kb][i] - m_use);
-                    sc[kb][i] = p;
-                    rs += p;
+                    // this register holds key 8*(i/4) + 4*hi + i%4
+                    const int kc = 8 * (i >> 2) + (i & 3);
+                    cur[qb][i] = kc > lim_l ? -INFINITY : cur[qb][i];
                 }
             }
-            rs += wave_xor32(rs);
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
-                o_acc[db] *= alpha;
-
-            // ---- O^T += V^T P^T, four 16-key steps
+            for (int i = 0; i < 16; ++i)
+                mx = fmaxf(mx, cur[qb][i]);
+            mx = fmaxf(mx, xor32(mx)) * scale_log2;
+            const bool up = mx > m_run[qb] + kTau;
+            any_rescale |= up;
+            const float m_new = up ? mx : m_run[qb];
+            alpha[qb] = up ? __builtin_amdgcn_exp2f(m_run[qb] - m_new) : 1.f;
+            m_run[qb] = m_new;
+        }
+        if (__any(any_rescale)) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                bf16x8 pf;
+            for (int qb = 0; qb < QB; ++qb) {
+                l_run[qb] *= alpha[qb];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    pf[j] = (__bf16)sc[ks >> 1][8 * (ks & 1) + j];
-                // keys of this lane for MFMA k-index 8*hi + j:
-                //   16*ks + 8*(j/4) + 4*hi + (j%4)
-                const int ka = 16 * ks + 4 * hi;
-#pragma unroll
-                for (int db = 0; db < 4; ++db) {
-                    const int d = db * 32 + l32;
-                    const unsigned int *vrow = (const unsigned int *)(vt_lds + d * VT_LD);
-                    u32x4 vx;
-                    vx[0] = vrow[ka / 2];
-                    vx[1] = vrow[ka / 2 + 1];
-                    vx[2] = vrow[(ka + 8) / 2];
-                    vx[3] = vrow[(ka + 8) / 2 + 1];
-                    o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vx), pf,
-                                                                        o_acc[db], 0, 0, 0);
-                }
+                for (int db = 0; db < 4; ++db)
+                    o_acc[qb][db] *= alpha[qb];
             }
         }
+        bf16x8 pf[QB][2];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+            float rs = 0.f;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float p = __builtin_amdgcn_exp2f(
+                        __builtin_fmaf(cur[qb][8 * kh + j], scale_log2, -m_use));
+                    rs += p;
+                    pf[qb][kh][j] = (__bf16)p;
+                }
+            l_run[qb] += rs + xor32(rs);
+        }
+
+        const char LDS_AS *vt = stage_base<ST_V>() + kTileBytes;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const bf16x8 vf = v_frag(vt, 2 * (u & 1) + kh, db);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    o_acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kh],
+                                                                            o_acc[qb][db], 0, 0, 0);
+            }
+    };
+
+    // ---- prologue: tiles 0 and 1 in flight, scores of sub-tile 0
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    f32x16 sc_a[QB], sc_b[QB];
+    issue(0, I0{});
+    issue(1, I1{});
+    if (n_tiles > 0) {
+        // loads retire in order: with at most 8 (one tile) outstanding, tile 0 has landed
+        __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        __syncthreads();
+        scores(0, sc_a, I0{});
+    }
+    // n_sub is even; six steps cover the three stages once
+    for (int u = 0; u < n_sub; u += 6) {
+        step(u, sc_a, sc_b, I0{});
+        step(u + 1, sc_b, sc_a, I1{});
+        if (u + 2 >= n_sub)
+            break;
+        step(u + 2, sc_a, sc_b, I2{});
+        step(u + 3, sc_b, sc_a, I3{});
+        if (u + 4 >= n_sub)
+            break;
+        step(u + 4, sc_a, sc_b, I4{});
+        step(u + 5, sc_b, sc_a, I5{});
     }
 
     // ---- epilogue: lane l holds O^T[d = 32*db + 8*(i/4) + 4*hi + i%4][row l32]
-    if (!row_ok)
-        return;
-    const int64_t orow = qs.out_row0 + my_row;
-    float *out = a.out + (orow * a.Hq + h) * HD;
-    float *lse_p = a.lse + (int64_t)h * a.lse_ld + orow;
     const float kLn2 = 0.6931471805599453f;
-    const float lse_blk = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-    const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
-    if (!qs.merge) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        if (!row_ok[qb])
+            continue;
+        const int64_t orow = qs.out_row0 + my_row[qb];
+        float *out = a.out + (orow * a.Hq + h) * HD;
+        float *lse_p = a.lse + (int64_t)h * a.lse_ld + orow;
+        const float l = l_run[qb];
+        const float lse_blk = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+        const float inv_l = l > 0.f ? 1.f / l : 0.f;
+        if (!qs.merge) {
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    f32x4 v4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v4[e] = o_acc[qb][db][4 * i4 + e] * inv_l;
+                    *(f32x4 *)(out + db * 32 + 8 * i4 + 4 * hi) = v4;
+                }
+            if (hi == 0)
+                *lse_p = lse_blk;
+            continue;
+        }
+        const float lse_old = *lse_p;
+        const float mxl = fmaxf(lse_old, lse_blk);
+        if (mxl == -INFINITY)
+            continue;
+        const float lse_new = mxl + log1pf(expf(-fabsf(lse_old - lse_blk)));
+        const float w_old = expf(lse_old - lse_new);
+        const float w_blk = expf(lse_blk - lse_new) * inv_l;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
+                f32x4 *dst = (f32x4 *)(out + db * 32 + 8 * i4 + 4 * hi);
+                const f32x4 old = *dst;
                 f32x4 v4;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    v4[e] = o_acc[db][4 * i4 + e] * inv_l;
-                *(f32x4 *)(out + db * 32 + 8 * i4 + 4 * hi) = v4;
+                    v4[e] = old[e] * w_old + o_acc[qb][db][4 * i4 + e] * w_blk;
+                *dst = v4;
             }
+        // both halves of the wavefront read lse_old above before this store
         if (hi == 0)
-            *lse_p = lse_blk;
-        return;
+            *lse_p = lse_new;
     }
-    const float lse_old = *lse_p;
-    const float mxl = fmaxf(lse_old, lse_blk);
-    if (mxl == -INFINITY)
-        return;
-    const float lse_new = mxl + log1pf(expf(-fabsf(lse_old - lse_blk)));
-    const float w_old = expf(lse_old - lse_new);
-    const float w_blk = expf(lse_blk - lse_new) * inv_l;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            f32x4 *dst = (f32x4 *)(out + db * 32 + 8 * i4 + 4 * hi);
-            f32x4 old = *dst;
-            f32x4 v4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                v4[e] = old[e] * w_old + o_acc[db][4 * i4 + e] * w_blk;
-            *dst = v4;
-        }
-    // both halves of the wavefront read lse_old above before this store
-    if (hi == 0)
-        *lse_p = lse_new;
+}
+
+// Visible keys of the last row of row tile `tile` of segment `s`.
+int64_t tile_work(const AttnLaunch &a, int s, int tile)
+{
+    const QSeg &q = a.qs[s];
+    const int64_t last = q.pos0 + std::min<int64_t>((int64_t)(tile + 1) * BM, q.len) - 1;
+    int64_t w = 0;
+    for (int k = 0; k < q.n_kv; ++k) {
+        const KvSeg &kv = q.kv[k];
+        w += a.causal ? std::min(std::max<int64_t>(last - kv.pos0 + 1, 0), kv.len) : kv.len;
+    }
+    return w;
 }
 
 }  // namespace
@@ -283,9 +510,35 @@ hipError_t launch_attn_bf16(const AttnLaunch &a, hipStream_t stream)
     tm.start[a.n_q] = (int32_t)total;
     if (total == 0 || a.Hq == 0)
         return hipSuccess;
+    tm.total = (int32_t)total;
+    tm.use_order = total <= kMaxOrder ? 1 : 0;
+    if (tm.use_order) {
+        // heaviest first; ties keep later rows first
+        std::vector<std::pair<int64_t, int>> w;
+        w.reserve(total);
+        for (int s = 0; s < a.n_q; ++s)
+            for (int t = tm.start[s]; t < tm.start[s + 1]; ++t)
+                w.push_back({-tile_work(a, s, t - tm.start[s]), -t});
+        std::sort(w.begin(), w.end());
+        for (int64_t i = 0; i < total; ++i)
+            tm.order[i] = (uint16_t)(-w[i].second);
+    }
+    int64_t grid;
+    if (a.Hq % kXcds == 0) {
+        tm.xcd_mode = 1;
+        grid = total * a.Hq;
+    } else if (kXcds % a.Hq == 0) {
+        tm.xcd_mode = 2;
+        const int xph = kXcds / a.Hq;
+        const int64_t slots = (total + xph - 1) / xph;
+        grid = slots * kXcds;
+    } else {
+        tm.xcd_mode = 0;
+        grid = total * a.Hq;
+    }
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)total, a.Hq), dim3(kThreads), 0, stream,
-                       a, tm, scale_log2);
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a, tm,
+                       scale_log2);
     return hipGetLastError();
 }
 
