@@ -25,11 +25,18 @@ FLAGS = [
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-source device-compiler options.  The attention kernel keeps its MFMA
+# accumulators in VGPRs: with AGPR accumulators every VALU touch of the
+# output (the rescale) and of the scores costs v_accvgpr copies.
+SOURCE_FLAGS = {
+    "attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str, resource_usage: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, "-x", "hip", *FLAGS, "-I", os.path.join(HERE, "..", "include"),
+    cmd = [HIPCC, "-x", "hip", *FLAGS, *SOURCE_FLAGS.get(src, []),
+           "-I", os.path.join(HERE, "..", "include"),
            "-c", os.path.join(CSRC, src), "-o", obj]
     if resource_usage and src.endswith(".hip"):
         cmd.append("-Rpass-analysis=kernel-resource-usage")

@@ -66,8 +66,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int HD = 128;                 // head dimension
 constexpr int BN = 64;                  // keys per LDS tile
-constexpr int QB = 2;                   // 32-row query blocks per wavefront
-constexpr int kWaves = 4;
+constexpr int QB = 1;                   // 32-row query blocks per wavefront
+constexpr int kWaves = 8;
 constexpr int BM = kWaves * QB * 32;    // 256 query rows per workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr int kStages = 3;
@@ -86,7 +86,12 @@ struct TileMap {
     uint16_t order[kMaxOrder];          // tile positions, heaviest first
 };
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// 16-byte-chunk XOR swizzle of a 256-byte tile row.  The LDS has 64 banks of
+// 4 bytes, so a 256-byte row covers every bank once; 16 lanes of a
+// ds_read_b128 (16 consecutive rows, one chunk) and 32 lanes of a transpose
+// read (4 consecutive rows x 4 consecutive chunks) then land in 16 distinct
+// chunk slots.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 // Byte offset inside a tile of the 16-byte chunk c of row r.
 __device__ __forceinline__ int tile_off(int r, int c) { return r * 256 + ((c ^ swz(r)) << 4); }
@@ -101,7 +106,19 @@ __device__ __forceinline__ i16x4 lds_tr(const char LDS_AS *base, int off)
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((i16x4 LDS_AS *)(base + off));
 }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// max / sum of x over lanes l and l^32 (v_permlane32_swap exchanges the halves)
+__device__ __forceinline__ float max_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Issue the direct-to-LDS loads of one K tile and one V tile (keys
 // key0 .. key0+63 of a KV segment) into `stage`.  Rows past the segment end
@@ -110,9 +127,14 @@ __device__ __forceinline__ void load_tile(char LDS_AS *stage, const __bf16 *kbas
                                           const __bf16 *vbase, int64_t row_stride,
                                           int64_t key0, int64_t len, int wave, int lane)
 {
+    // The per-lane address terms are recomputed at every call (a few VALU
+    // operations per tile): the opaque copy of the lane index keeps the
+    // compiler from hoisting them out of the tile loop, where they would
+    // stay live in registers.
+    __asm__ volatile("" : "+v"(lane));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int blk = wave * 4 + i;              // 1 KiB block of the tile
+    for (int i = 0; i < 16 / kWaves; ++i) {
+        const int blk = wave * (16 / kWaves) + i;  // 1 KiB block of the tile
         const int r = blk * 4 + (lane >> 4);       // tile row this lane fills
         const int c = (lane & 15) ^ swz(r);        // logical chunk for this LDS slot
         int64_t key = key0 + r;
@@ -200,27 +222,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnLaunch a, Ti
     const __bf16 *kg = (const __bf16 *)a.k + g * HD;
     const __bf16 *vg = (const __bf16 *)a.v + g * HD;
 
-    // ---- rows of this wavefront: block qb holds rows wave*64 + qb*32 + [0, 32)
-    int64_t my_row[QB];
-    bool row_ok[QB];
-    int64_t my_pos[QB];
+    // ---- rows of this wavefront: block qb holds tile rows row_off[qb] =
+    // wave*32*QB + qb*32 + [0, 32)
+    int row_off[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        my_row[qb] = tile_row0 + wave * 64 + qb * 32 + l32;
-        row_ok[qb] = my_row[qb] < qs.len;
-        my_pos[qb] = qs.pos0 + my_row[qb];
-    }
+    for (int qb = 0; qb < QB; ++qb)
+        row_off[qb] = wave * 32 * QB + qb * 32 + l32;
 
     // Q^T fragments: B operand of step sd holds dims 16*sd + 8*hi + [0, 8).
     bf16x8 qf[QB][8];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        const int64_t r = row_ok[qb] ? my_row[qb] : 0;
+        const bool ok = tile_row0 + row_off[qb] < qs.len;
+        const int64_t r = ok ? tile_row0 + row_off[qb] : 0;
         const u32x4 *src = (const u32x4 *)(qg + (qs.row0 + r) * q_stride + h * HD + 8 * hi);
 #pragma unroll
         for (int sd = 0; sd < 8; ++sd) {
             u32x4 x = src[2 * sd];
-            if (!row_ok[qb])
+            if (!ok)
                 x = u32x4{0, 0, 0, 0};
             qf[qb][sd] = __builtin_bit_cast(bf16x8, x);
         }
@@ -270,6 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnLaunch a, Ti
 
     // S^T = K Q^T for sub-tile u (32 keys: half u%2 of LDS tile u/2): sc[qb].
     // per-lane byte offsets of the K fragments inside a 32-row half tile
+    // (rows l32 and 32 + l32 share a swizzle: it depends on row % 16)
     int k_off[8];
 #pragma unroll
     for (int sd = 0; sd < 8; ++sd)
@@ -293,152 +313,135 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnLaunch a, Ti
     // transpose reads; see the key order in the header comment).
     const int grp = lane >> 4;          // 16-lane group
     const int gi = lane & 15;
-    // rows 16*ks + r0 and +8 share swz(r0) because swz depends on row % 8
-    int v_off[4];
+    // rows 16*ks + r0 share swz(r0) because swz depends on row % 16; the
+    // second read (rows r0 + 8) has its own offsets
+    int v_off[2][4];
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
         const int dcol = db * 32 + 16 * (grp & 1) + 4 * (gi & 3);   // first of 4 columns
         const int r0 = 4 * (grp >> 1) + (gi >> 2);
-        v_off[db] = tile_off(r0, dcol >> 3) + (dcol & 7) * 2;
+        v_off[0][db] = tile_off(r0, dcol >> 3) + (dcol & 7) * 2;
+        v_off[1][db] = tile_off(r0 + 8, dcol >> 3) + (dcol & 7) * 2;
     }
     auto v_frag = [&](const char LDS_AS *vt, int ks, int db) {
-        const i16x4 lo = lds_tr(vt, ks * 16 * 256 + v_off[db]);
-        const i16x4 up = lds_tr(vt, ks * 16 * 256 + 8 * 256 + v_off[db]);
+        const i16x4 lo = lds_tr(vt, ks * 16 * 256 + v_off[0][db]);
+        const i16x4 up = lds_tr(vt, ks * 16 * 256 + v_off[1][db]);
         const bf16x4 blo = __builtin_bit_cast(bf16x4, lo);
         const bf16x4 bup = __builtin_bit_cast(bf16x4, up);
         return __builtin_shufflevector(blo, bup, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
-    const int n_sub = 2 * n_tiles;
-
-    // One pipeline step: scores of sub-tile u+1 (into nxt), softmax of
-    // sub-tile u (in cur), then O^T += V^T P^T for sub-tile u.  J = u mod 6
-    // fixes the stages: tile t lives in stage t % 3.
-    auto step = [&](int u, f32x16 (&cur)[QB], f32x16 (&nxt)[QB], auto j) {
-        constexpr int J = decltype(j)::value;
-        constexpr int ST_V = (J / 2) % 3;                 // tile u/2
-        constexpr int ST_K = ((J + 1) / 2) % 3;           // tile (u+1)/2
-        constexpr int ST_NEW = ((J + 1) / 2 + 1) % 3;     // tile (u+1)/2 + 1
-        if ((J & 1) && u + 1 < n_sub) {
-            // next LDS tile complete in every wavefront; the stage the new
-            // loads overwrite is no longer read
-            __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            issue((u + 1) / 2 + 1, std::integral_constant<int, ST_NEW>{});
-        }
-        if (u + 1 < n_sub)
-            scores(u + 1, nxt, std::integral_constant<int, ST_K>{});
-
-        const int t = u >> 1;
+    // One 64-key tile in stage ST: for each 32-key half, scores, masking and
+    // running max, exponentials, then O^T += V^T P^T.  The other wavefront
+    // on the SIMD overlaps its matrix work with this one's softmax.
+    auto tile_step = [&](int t, auto st) {
+        constexpr int ST = decltype(st)::value;
+        // tile t complete in every wavefront; the stage the new loads overwrite
+        // (tile t-1's) is no longer read
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        issue(t + 2, std::integral_constant<int, (ST + 2) % 3>{});
         const TileRef r = tile_ref(t);
         const KvSeg &kv = qs.kv[r.seg];
-        const int64_t key0 = r.key0 + (u & 1) * 32;      // first key of the sub-tile
-        const bool need_mask = (key0 + 32 > kv.len) ||
-                               (a.causal && kv.pos0 + key0 + 31 > first_pos);
-        float alpha[QB];
-        bool any_rescale = false;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            float mx = -INFINITY;
-            if (need_mask) {
-                // key k of the sub-tile (0..31) is visible iff k <= lim
-                int64_t lim = kv.len - 1 - key0;
-                if (a.causal)
-                    lim = min(lim, my_pos[qb] - kv.pos0 - key0);
-                const int lim_l = (int)max(min(lim, (int64_t)64), (int64_t)-1) - 4 * hi;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    // this register holds key 8*(i/4) + 4*hi + i%4
-                    const int kc = 8 * (i >> 2) + (i & 3);
-                    cur[qb][i] = kc > lim_l ? -INFINITY : cur[qb][i];
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                mx = fmaxf(mx, cur[qb][i]);
-            mx = fmaxf(mx, xor32(mx)) * scale_log2;
-            const bool up = mx > m_run[qb] + kTau;
-            any_rescale |= up;
-            const float m_new = up ? mx : m_run[qb];
-            alpha[qb] = up ? __builtin_amdgcn_exp2f(m_run[qb] - m_new) : 1.f;
-            m_run[qb] = m_new;
-        }
-        if (__any(any_rescale)) {
+        for (int half = 0; half < 2; ++half) {
+            f32x16 cur[QB];
+            scores(2 * t + half, cur, st);
+            const int64_t key0 = r.key0 + half * 32;      // first key of the half tile
+            const bool need_mask = (key0 + 32 > kv.len) ||
+                                   (a.causal && kv.pos0 + key0 + 31 > first_pos);
+            float alpha[QB];
+            bool any_rescale = false;
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                l_run[qb] *= alpha[qb];
+                if (need_mask) {
+                    // key k of the half tile (0..31) is visible iff k <= lim
+                    const int tail = (int)min(max(kv.len - 1 - key0, (int64_t)-1), (int64_t)64);
+                    const int base_c = (int)min(max(first_pos - kv.pos0 - key0, (int64_t)-512),
+                                                (int64_t)512);
+                    const int lim = a.causal ? min(tail, base_c + row_off[qb]) : tail;
+                    const int lim_l = max(lim, -1) - 4 * hi;
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    o_acc[qb][db] *= alpha[qb];
+                    for (int i = 0; i < 16; ++i) {
+                        // this register holds key 8*(i/4) + 4*hi + i%4
+                        const int kc = 8 * (i >> 2) + (i & 3);
+                        cur[qb][i] = kc > lim_l ? -INFINITY : cur[qb][i];
+                    }
+                }
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    mx = fmaxf(mx, cur[qb][i]);
+                mx = max_xor32(mx) * scale_log2;
+                const bool up = mx > m_run[qb] + kTau;
+                any_rescale |= up;
+                const float m_new = up ? mx : m_run[qb];
+                alpha[qb] = up ? __builtin_amdgcn_exp2f(m_run[qb] - m_new) : 1.f;
+                m_run[qb] = m_new;
             }
-        }
-        bf16x8 pf[QB][2];
+            if (__any(any_rescale)) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-            float rs = 0.f;
+                for (int qb = 0; qb < QB; ++qb) {
+                    l_run[qb] *= alpha[qb];
+#pragma unroll
+                    for (int db = 0; db < 4; ++db)
+                        o_acc[qb][db] *= alpha[qb];
+                }
+            }
+            bf16x8 pf[QB][2];
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+                float rs = 0.f;
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const float p = __builtin_amdgcn_exp2f(
+                            __builtin_fmaf(cur[qb][8 * kh + j], scale_log2, -m_use));
+                        rs += p;
+                        pf[qb][kh][j] = (__bf16)p;
+                    }
+                l_run[qb] += sum_xor32(rs);
+            }
+            const char LDS_AS *vt = stage_base<ST>() + kTileBytes;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float p = __builtin_amdgcn_exp2f(
-                        __builtin_fmaf(cur[qb][8 * kh + j], scale_log2, -m_use));
-                    rs += p;
-                    pf[qb][kh][j] = (__bf16)p;
+                for (int db = 0; db < 4; ++db) {
+                    const bf16x8 vf = v_frag(vt, 2 * half + kh, db);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        o_acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            vf, pf[qb][kh], o_acc[qb][db], 0, 0, 0);
                 }
-            l_run[qb] += rs + xor32(rs);
         }
-
-        const char LDS_AS *vt = stage_base<ST_V>() + kTileBytes;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const bf16x8 vf = v_frag(vt, 2 * (u & 1) + kh, db);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-                    o_acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kh],
-                                                                            o_acc[qb][db], 0, 0, 0);
-            }
     };
 
-    // ---- prologue: tiles 0 and 1 in flight, scores of sub-tile 0
+    // ---- tiles 0 and 1 in flight before the loop; tile t uses stage t % 3
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    using I4 = std::integral_constant<int, 4>;
-    using I5 = std::integral_constant<int, 5>;
-    f32x16 sc_a[QB], sc_b[QB];
     issue(0, I0{});
     issue(1, I1{});
-    if (n_tiles > 0) {
-        // loads retire in order: with at most 8 (one tile) outstanding, tile 0 has landed
-        __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        __syncthreads();
-        scores(0, sc_a, I0{});
-    }
-    // n_sub is even; six steps cover the three stages once
-    for (int u = 0; u < n_sub; u += 6) {
-        step(u, sc_a, sc_b, I0{});
-        step(u + 1, sc_b, sc_a, I1{});
-        if (u + 2 >= n_sub)
+    for (int t = 0; t < n_tiles; t += 3) {
+        tile_step(t, I0{});
+        if (t + 1 >= n_tiles)
             break;
-        step(u + 2, sc_a, sc_b, I2{});
-        step(u + 3, sc_b, sc_a, I3{});
-        if (u + 4 >= n_sub)
+        tile_step(t + 1, I1{});
+        if (t + 2 >= n_tiles)
             break;
-        step(u + 4, sc_a, sc_b, I4{});
-        step(u + 5, sc_b, sc_a, I5{});
+        tile_step(t + 2, I2{});
     }
 
     // ---- epilogue: lane l holds O^T[d = 32*db + 8*(i/4) + 4*hi + i%4][row l32]
     const float kLn2 = 0.6931471805599453f;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        if (!row_ok[qb])
+        const int64_t my_row = tile_row0 + row_off[qb];
+        if (my_row >= qs.len)
             continue;
-        const int64_t orow = qs.out_row0 + my_row[qb];
+        const int64_t orow = qs.out_row0 + my_row;
         float *out = a.out + (orow * a.Hq + h) * HD;
         float *lse_p = a.lse + (int64_t)h * a.lse_ld + orow;
         const float l = l_run[qb];
