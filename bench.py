@@ -51,6 +51,30 @@ def ulysses_share_flop(S, H_local, D):
     return 4.0 * D * H_local * S * S / 2.0
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_128k_rank_share_hbm_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "context_parallelism_cp_amd", "csrc", "attn_bf16.hip")
+
+
+def recorded_traffic():
+    """HBM bytes per attention launch from the committed FETCH_SIZE/WRITE_SIZE
+    summary, or None when the kernel source changed since it was taken."""
+    import hashlib
+    try:
+        fields = {}
+        with open(TRAFFIC_PROFILE, encoding="utf-8") as f:
+            for line in f:
+                if ":" in line and not line.startswith(("|", "#", "`")):
+                    key, _, val = line.partition(":")
+                    fields[key.strip()] = val.strip()
+        with open(KERNEL_SOURCE, "rb") as f:
+            current = hashlib.sha256(f.read()).hexdigest()
+        if fields.get("kernel_source_sha256") != current:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(q, k, v, budget_s=12.0, max_rows=512):
     """Time the float64 oracle on seeded rows of the ring rank's share."""
     import numpy as np
@@ -92,6 +116,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--part", choices=["both", "ring", "ulysses"], default="both")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="before warm-up, copy 1 GiB device to device once (a plain copy "
+                         "kernel of known size that scales HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the ring and Ulysses ranks are virtual and "
@@ -134,6 +161,14 @@ def main():
             cp.cp_seq_to_head(dvu, P, ULY_RANK, y=vl, stream=stream)
             cp.cp_attn_block_fwd(ql, kl, vl, uly_out_l, uly_lse, stream=stream)
             cp.cp_head_to_seq(uly_out_l, uly_out, P, ULY_RANK, stream=stream)
+
+    if args.calibration_copy:
+        src = torch.empty(1 << 28, device=dev, dtype=torch.float32).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)          # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -193,7 +228,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
-            "traffic": None,
+            "traffic": recorded_traffic(),
+            "traffic_unit": "bytes per launch (HBM read + write, calibrated)",
             "launches": attn_n,
             "avg_launch_ms": round(attn_ms / max(attn_n, 1), 4),
             "flop_per_launch": flop_step * args.steps / max(attn_n, 1),

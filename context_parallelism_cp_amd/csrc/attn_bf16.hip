@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnLaunch a, Ti
                                                                 float scale_log2)
 {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
