@@ -171,8 +171,12 @@ __device__ __forceinline__ char LDS_AS *stage_base()
         return (char LDS_AS *)g_stage2;
 }
 
-__global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnLaunch a, TileMap tm,
-                                                                float scale_log2)
+// One workgroup per CU (its LDS ring fills most of the CU's LDS), i.e. two
+// wavefronts per SIMD: telling the compiler lets its scheduler spend up to
+// 256 VGPRs on reading LDS fragments ahead of the MFMAs instead of
+// minimising registers for an occupancy the LDS cannot give.
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -300,12 +304,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnLaunch a, Ti
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
             sc[qb] = f32x16{};
+        // all eight K fragments are requested before the first MFMA, so the
+        // LDS latency is paid once per half tile rather than once per MFMA
+        bf16x8 kf[8];
+#pragma unroll
+        for (int sd = 0; sd < 8; ++sd)
+            kf[sd] = lds_b128(kt, k_off[sd]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int sd = 0; sd < 8; ++sd) {
-            const bf16x8 kf = lds_b128(kt, k_off[sd]);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
-                sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][sd], sc[qb], 0, 0, 0);
+                sc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sd], qf[qb][sd], sc[qb], 0,
+                                                                 0, 0);
         }
     };
 
@@ -347,6 +358,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnLaunch a, Ti
         for (int half = 0; half < 2; ++half) {
             f32x16 cur[QB];
             scores(2 * t + half, cur, st);
+            // V fragments of this half tile, requested now: they land while
+            // the softmax runs
+            const char LDS_AS *vt = stage_base<ST>() + kTileBytes;
+            bf16x8 vfr[2][4];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    vfr[kh][db] = v_frag(vt, 2 * half + kh, db);
+            __builtin_amdgcn_sched_barrier(0);
             const int64_t key0 = r.key0 + half * 32;      // first key of the half tile
             const bool need_mask = (key0 + 32 > kv.len) ||
                                    (a.causal && kv.pos0 + key0 + 31 > first_pos);
@@ -404,16 +425,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bf16_kernel(AttnLaunch a, Ti
                     }
                 l_run[qb] += sum_xor32(rs);
             }
-            const char LDS_AS *vt = stage_base<ST>() + kTileBytes;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                 for (int db = 0; db < 4; ++db) {
-                    const bf16x8 vf = v_frag(vt, 2 * half + kh, db);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb)
                         o_acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            vf, pf[qb][kh], o_acc[qb][db], 0, 0, 0);
+                            vfr[kh][db], pf[qb][kh], o_acc[qb][db], 0, 0, 0);
                 }
         }
     };
