@@ -120,31 +120,47 @@ __device__ __forceinline__ float sum_xor32(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Raw buffer resource over `bytes` bytes at `p` (no stride, the default
+// data format of a gfx9 descriptor).  Loads through it whose offset lies past
+// `bytes` are dropped by the address unit and return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes,
+                                             0x00020000);
+}
+
+constexpr int kLoadsPerLane = 16 / kWaves;  // 1 KiB blocks of a tile filled per wave
+
 // Issue the direct-to-LDS loads of one K tile and one V tile (keys
-// key0 .. key0+63 of a KV segment) into `stage`.  Rows past the segment end
-// are clamped to its last row; their scores are masked.
+// key0 .. key0+63 of a KV segment of `len` rows) into `stage`.  The buffer
+// resources end after the last row of the segment, so the chunks of rows
+// past it read as zeros (their scores are masked).  The tile's address
+// arithmetic is uniform (scalar unit); a lane adds only its fixed offset:
+// the chunk it copies sits in row blk*4 + lane/16 of the tile and lands in
+// the LDS slot the swizzle gives it.
 __device__ __forceinline__ void load_tile(char LDS_AS *stage, const __bf16 *kbase,
                                           const __bf16 *vbase, int64_t row_stride,
                                           int64_t key0, int64_t len, int wave, int lane)
 {
-    // The per-lane address terms are recomputed at every call (a few VALU
-    // operations per tile): the opaque copy of the lane index keeps the
-    // compiler from hoisting them out of the tile loop, where they would
-    // stay live in registers.
+    // The lane offsets are recomputed at every call (a few VALU operations
+    // per tile): the opaque copy of the lane index keeps the compiler from
+    // hoisting them out of the tile loop, which changes its register
+    // allocation of the loop for the worse.
     __asm__ volatile("" : "+v"(lane));
+    const int64_t rows = min(len - key0, (int64_t)BN);   // >= 1 for an issued tile
+    const int row_bytes = (int)(row_stride * 2);
+    const int bytes = (int)(rows - 1) * row_bytes + HD * 2;
+    const auto rk = buffer_rsrc(kbase + key0 * row_stride, bytes);
+    const auto rv = buffer_rsrc(vbase + key0 * row_stride, bytes);
 #pragma unroll
-    for (int i = 0; i < 16 / kWaves; ++i) {
-        const int blk = wave * (16 / kWaves) + i;  // 1 KiB block of the tile
-        const int r = blk * 4 + (lane >> 4);       // tile row this lane fills
-        const int c = (lane & 15) ^ swz(r);        // logical chunk for this LDS slot
-        int64_t key = key0 + r;
-        key = key < len ? key : len - 1;
-        const int64_t off = key * row_stride + c * 8;
-        __builtin_amdgcn_global_load_lds((const void *)(kbase + off),
-                                         (void LDS_AS *)(stage + blk * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)(vbase + off),
-                                         (void LDS_AS *)(stage + kTileBytes + blk * 1024), 16,
-                                         0, 0);
+    for (int i = 0; i < kLoadsPerLane; ++i) {
+        const int blk = wave * kLoadsPerLane + i;
+        const int r = blk * 4 + (lane >> 4);
+        const int off = r * row_bytes + (((lane & 15) ^ swz(r)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (void LDS_AS *)(stage + blk * 1024), 16,
+                                                 off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rv, (void LDS_AS *)(stage + kTileBytes + blk * 1024), 16, off, 0, 0, 0);
     }
 }
 

@@ -134,6 +134,9 @@ int check_attn_common(const void *q, const void *k, const void *v, const float *
     if (dtype == CP_BF16) {
         if (D != 128)
             return fail(CP_ERR_UNSUPPORTED, "bf16 attention supports D = 128 only (D=%d)", D);
+        // a 64-row K or V tile is addressed with 32-bit byte offsets
+        if ((int64_t)Hkv * D >= ((int64_t)1 << 24))
+            return fail(CP_ERR_UNSUPPORTED, "bf16 attention needs Hkv * D < 2^24 (Hkv=%d)", Hkv);
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
             return fail(CP_ERR_ALIGN, "bf16 attention needs 16-byte aligned q, k, v and out");
     } else if (dtype == CP_F32) {

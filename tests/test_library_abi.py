@@ -96,6 +96,9 @@ def test_block_fwd_argument_errors():
     assert rc_block(D=129, dtype=cp.CP_F32) == cp.CP_ERR_UNSUPPORTED
     assert rc_block(D=0, dtype=cp.CP_F32) == cp.CP_ERR_UNSUPPORTED
     assert rc_block(dtype=7) == cp.CP_ERR_UNSUPPORTED
+    # bf16 tiles are addressed with 32-bit byte offsets: Hkv * D < 2^24
+    assert rc_block(Hq=1 << 17, Hkv=1 << 17) == cp.CP_ERR_UNSUPPORTED
+    assert "2^24" in cp.cp_last_error()
     assert rc_block(q=FAKE + 2) == cp.CP_ERR_ALIGN
     assert rc_block(out=FAKE) == cp.CP_ERR_ALIGN          # out overlaps q
     assert "overlap" in cp.cp_last_error()
