@@ -9,14 +9,15 @@
 // log2(e)/sqrt(D) folded into one fused multiply-add; lse is returned in nats.
 //
 // Work decomposition
-//   * A workgroup of 4 wavefronts owns BM = 256 query rows of one head; each
-//     wavefront owns 64 rows as two 32-row blocks, so every K or V fragment
-//     read from LDS feeds two MFMAs.  One wavefront per SIMD.
+//   * A workgroup of 8 wavefronts (two per SIMD) owns BM = 256 query rows of
+//     one head; each wavefront owns 32 rows.  The two wavefronts of a SIMD
+//     overlap one's matrix work with the other's softmax.
 //   * Keys stream through LDS BN = 64 at a time in a 3-stage ring filled by
-//     direct global->LDS 16-byte loads (no staging registers).  K and V tiles
-//     are both stored row-major with a 16-byte-chunk XOR swizzle that keeps
-//     the K reads (ds_read_b128) and the V transpose reads
-//     (ds_read_b64_tr_b16) free of bank conflicts.
+//     direct buffer->LDS 16-byte loads (no staging registers); the buffer
+//     resource of a tile ends at the segment's last row, so rows past it read
+//     as zeros.  K and V tiles are both stored row-major with a 16-byte-chunk
+//     XOR swizzle that keeps the K reads (ds_read_b128) and the V transpose
+//     reads (ds_read_b64_tr_b16) free of bank conflicts.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from LDS, B = 16 dims x
 //     32 queries kept in VGPRs for the whole kernel).  In the accumulator
@@ -26,16 +27,16 @@
 //     for a 16-key step is 8 consecutive accumulator registers of the lane,
 //     converted to bf16 in place; the key order inside the step is permuted
 //     identically for P and V, and the V^T fragment is two transpose reads of
-//     the row-major V tile.  Each lane keeps one query per block, so the
-//     rescale by exp2(m_old - m_new) is a per-lane scalar.
-//   * Software pipeline: the S^T MFMAs of tile t+1 are issued before the
-//     softmax of tile t, so the VALU work of one tile overlaps the matrix
-//     work of the next.
-//   * The running max is only raised when a tile's max exceeds it by more
-//     than 2^8 (in base 2), so the 128-register rescale of O is rare; the
+//     the row-major V tile.  Each lane keeps one query, so the rescale by
+//     exp2(m_old - m_new) is a per-lane scalar.
+//   * Per 32-key half tile, all K fragments and then all V fragments are
+//     requested from LDS before their first use, so the LDS latency is paid
+//     once per phase rather than once per MFMA.
+//   * The running max is only raised when a half tile's max exceeds it by
+//     more than 2^8 (in base 2), so the 64-register rescale of O is rare; the
 //     exponentials stay <= 2^8 and the final O / l is unchanged.
-//   * Tiles strictly below the causal diagonal run without the mask; tiles
-//     crossing it (or a ragged end) compare absolute positions.
+//   * Half tiles strictly below the causal diagonal run without the mask;
+//     half tiles crossing it (or a ragged end) compare absolute positions.
 //   * Workgroups are mapped XCD-aware: the heads of a launch are spread over
 //     the 8 XCDs, a head's tiles stay on its XCD(s), and every XCD walks its
 //     tiles heaviest-first (most visible keys first).
@@ -359,8 +360,7 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
     };
 
     // One 64-key tile in stage ST: for each 32-key half, scores, masking and
-    // running max, exponentials, then O^T += V^T P^T.  The other wavefront
-    // on the SIMD overlaps its matrix work with this one's softmax.
+    // running max, exponentials, then O^T += V^T P^T.
     auto tile_step = [&](int t, auto st) {
         constexpr int ST = decltype(st)::value;
         // tile t complete in every wavefront; the stage the new loads overwrite
