@@ -124,3 +124,56 @@ def attention_global_max(q, k, v, key_parts, causal=True, q_offset=0, k_offset=0
         out[nz, h, :] = acc[nz] / l_global[nz, None]
         lse[h, nz] = m_safe[nz] + np.log(l_global[nz])
     return out, lse
+
+
+def attention_bwd(q, k, v, dout, out, lse, causal: bool = True, q_offset: int = 0,
+                  k_offset: int = 0):
+    """Gradients (dq, dk, dv) of one query chunk against one KV block.
+
+    The loss is ``sum(dout * out)`` where ``out`` / ``lse`` are the *final*
+    results of the query rows over every key they see (this block alone, or
+    all the blocks of a ring).  The block's share of each row's softmax is
+    then ``P_ij = exp(s_ij - lse_i)``, so the gradients of several blocks
+    add up to the gradient of the whole row.  With this block's own
+    ``(out, lse)`` from ``attention`` it is the ordinary gradient of that
+    function.
+
+    Chain rule through out_i = sum_j P_ij v_j, P_ij = exp(s_ij - lse_i),
+    lse_i = log sum_j exp(s_ij), s = q k^T / sqrt(D) (definitions of the
+    handbook's ``attention``):
+
+      dv_j  = sum_i P_ij dout_i
+      dP_ij = dout_i . v_j
+      Dv_i  = dout_i . out_i      (= sum over the row's keys of P_ij dP_ij)
+      ds_ij = P_ij (dP_ij - Dv_i)
+      dq_i  = sum_j ds_ij k_j / sqrt(D),   dk_j = sum_i ds_ij q_i / sqrt(D)
+
+    Grouped-query attention: KV head g receives the sum over its query
+    heads.  Rows with lse = -inf (no visible key) contribute nothing.
+    Shapes as in ``attention``; dout and out [Sq, Hq, D], lse [Hq, Sq].
+    Returns float64 dq [Sq, Hq, D], dk and dv [Sk, Hkv, D].
+    """
+    q, k, v, dout, out, lse = map(_as_f64, (q, k, v, dout, out, lse))
+    Sq, Hq, D = q.shape
+    Sk, Hkv, _ = k.shape
+    group = Hq // Hkv
+    qpos = np.arange(Sq)[:, None] + q_offset
+    kpos = np.arange(Sk)[None, :] + k_offset
+    visible = (kpos <= qpos) if causal else np.ones((Sq, Sk), dtype=bool)
+    dq = np.zeros((Sq, Hq, D))
+    dk = np.zeros((Sk, Hkv, D))
+    dv = np.zeros((Sk, Hkv, D))
+    scale = 1.0 / np.sqrt(D)
+    for h in range(Hq):
+        g = h // group
+        finite = np.isfinite(lse[h])
+        s = (q[:, h, :] @ k[:, g, :].T) * scale
+        p = np.where(visible & finite[:, None],
+                     np.exp(s - np.where(finite, lse[h], 0.0)[:, None]), 0.0)   # [Sq, Sk]
+        dv[:, g, :] += p.T @ dout[:, h, :]
+        dp = dout[:, h, :] @ v[:, g, :].T
+        dvec = np.sum(dout[:, h, :] * out[:, h, :], axis=1)                      # [Sq]
+        ds = p * (dp - dvec[:, None])
+        dq[:, h, :] = ds @ k[:, g, :] * scale
+        dk[:, g, :] += ds.T @ q[:, h, :] * scale
+    return dq, dk, dv

@@ -32,7 +32,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import attention, lse_merge
+from .attention import attention, attention_bwd, lse_merge
 
 CONTIGUOUS, ZIGZAG = 0, 1
 SKIP, FULL, DIAG = 0, 1, 2
@@ -166,6 +166,36 @@ def ring_zigzag(q, k, v, P: int, causal: bool = True):
         lses.append(np.concatenate([state[c][1] for c in split[rank]], axis=1))
         units.append(per_step)
     return outs, lses, units
+
+
+def ring_bwd(q, k, v, dout, P: int, layout: int, causal: bool = True):
+    """Backward pass through the ring (no algorithm on the pages; the
+    plainest reading of running the forward ring backwards).
+
+    Every pair that the forward plan computes (``ring_plan``, all ranks)
+    contributes ``attention_bwd`` of its query chunk against its key chunk,
+    taken with the query rows' final (out, lse) -- the forward result of
+    the whole ring, which equals the single-pass result.  dq accumulates on
+    the query rows' rank; dk and dv accumulate on the KV block's rows (on a
+    real ring these accumulators travel with the block and return to its
+    owner after P steps).  Returns dq, dk, dv in natural order, float64.
+    """
+    q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    S = q.shape[0]
+    out, lse = attention(q, k, v, causal=causal)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for (_r, _t, _qc, _kc, qo, ko, lq, lk, kind) in ring_plan(S, P, layout, -1, causal):
+        if kind == SKIP:
+            continue
+        gq, gk, gv = attention_bwd(q[qo:qo + lq], k[ko:ko + lk], v[ko:ko + lk],
+                                   dout[qo:qo + lq], out[qo:qo + lq], lse[:, qo:qo + lq],
+                                   causal=(kind == DIAG), q_offset=qo, k_offset=ko)
+        dq[qo:qo + lq] += gq
+        dk[ko:ko + lk] += gk
+        dv[ko:ko + lk] += gv
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------- Ulysses

@@ -203,3 +203,103 @@ def make_qkv_page():
     """The handbook's make_qkv(): manual_seed(0), then randn(32, 8, 16) x3."""
     torch.manual_seed(0)
     return torch.randn(32, 8, 16), torch.randn(32, 8, 16), torch.randn(32, 8, 16)
+
+
+# -------------------------------------------------------------- backward
+BWD_CASES = [
+    # (Sq, Sk, Hq, Hkv, D, causal, q_offset, k_offset)
+    (5, 6, 2, 1, 4, True, 3, 1),      # GQA, offsets, causal
+    (4, 4, 2, 2, 3, False, 0, 0),     # non-causal
+    (4, 5, 1, 1, 2, True, 0, 2),      # rows 0 and 1 see no key
+]
+
+
+def _loss_grad_fd(attn, q, k, v, dout, causal, qo, ko, eps=1e-6):
+    """Central finite differences of sum(dout * attn(q, k, v).out)."""
+    def loss(q_, k_, v_):
+        return float(np.sum(dout * attn(q_, k_, v_, causal=causal, q_offset=qo,
+                                         k_offset=ko)[0]))
+    grads = []
+    for which in range(3):
+        x = [q, k, v][which]
+        g = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            g[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        grads.append(g)
+    return grads
+
+
+def pin_bwd_finite_differences(attn, attn_bwd):
+    """The backward is the derivative of the (pinned) forward: central
+    differences of sum(dout * out) agree to the difference formula's
+    accuracy, on every case of BWD_CASES."""
+    for n, (Sq, Sk, Hq, Hkv, D, causal, qo, ko) in enumerate(BWD_CASES):
+        q, k, v = rand((Sq, Hq, D), 60 + n), rand((Sk, Hkv, D), 70 + n), rand((Sk, Hkv, D), 80 + n)
+        dout = rand((Sq, Hq, D), 90 + n)
+        out, lse = attn(q, k, v, causal=causal, q_offset=qo, k_offset=ko)
+        got = attn_bwd(q, k, v, dout, out, lse, causal=causal, q_offset=qo, k_offset=ko)
+        want = _loss_grad_fd(attn, q, k, v, dout, causal, qo, ko)
+        for g, w in zip(got, want):
+            np.testing.assert_allclose(g, w, atol=1e-7)
+
+
+def pin_bwd_autograd(attn, attn_bwd):
+    """Offsets 0: torch autograd through scaled_dot_product_attention in
+    float64 on the CPU (a library special case of the same gradient)."""
+    import torch.nn.functional as F
+    for causal in (True, False):
+        for (S, Hq, Hkv, D) in [(9, 4, 2, 8), (7, 2, 2, 4)]:
+            q, k, v = rand((S, Hq, D), 101), rand((S, Hkv, D), 102), rand((S, Hkv, D), 103)
+            dout = rand((S, Hq, D), 104)
+            out, lse = attn(q, k, v, causal=causal)
+            got = attn_bwd(q, k, v, dout, out, lse, causal=causal)
+            tq, tk, tv = (torch.from_numpy(x).permute(1, 0, 2).unsqueeze(0).requires_grad_()
+                          for x in (q, k, v))
+            o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                               enable_gqa=(Hq != Hkv))
+            o.backward(torch.from_numpy(dout).permute(1, 0, 2).unsqueeze(0))
+            for g, t in zip(got, (tq, tk, tv)):
+                np.testing.assert_allclose(g, t.grad[0].permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+def pin_bwd_closed_forms(attn, attn_bwd):
+    """Closed forms.  Equal value rows make out constant in q and k, so
+    dq = dk = 0.  Over a single block (full rows) the row sums of ds vanish,
+    so sum_j dk_j = 0 for every KV head, and sum_j dv_j = sum over rows that
+    see a key (and the heads of the group) of dout_i."""
+    Sq, Sk, Hq, Hkv, D, qo, ko = 6, 7, 4, 2, 5, 2, 0
+    q, k = rand((Sq, Hq, D), 111), rand((Sk, Hkv, D), 112)
+    dout = rand((Sq, Hq, D), 113)
+    v = np.broadcast_to(rand((1, Hkv, D), 114), (Sk, Hkv, D)).copy()
+    out, lse = attn(q, k, v, causal=True, q_offset=qo, k_offset=ko)
+    dq, dk, _ = attn_bwd(q, k, v, dout, out, lse, causal=True, q_offset=qo, k_offset=ko)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+    v = rand((Sk, Hkv, D), 115)
+    Sq, qo, ko = 6, 0, 2                          # rows 0 and 1 see no key
+    q, dout = rand((Sq, Hq, D), 116), rand((Sq, Hq, D), 117)
+    out, lse = attn(q, k, v, causal=True, q_offset=qo, k_offset=ko)
+    _, dk, dv = attn_bwd(q, k, v, dout, out, lse, causal=True, q_offset=qo, k_offset=ko)
+    group = Hq // Hkv
+    for g in range(Hkv):
+        np.testing.assert_allclose(dk[:, g, :].sum(axis=0), 0.0, atol=1e-12)
+        want = sum(dout[i, h, :] for h in range(g * group, (g + 1) * group)
+                   for i in range(Sq) if qo + i >= ko)
+        np.testing.assert_allclose(dv[:, g, :].sum(axis=0), want, atol=1e-12)
+
+
+def pin_bwd_ring(ring_bwd, attn, attn_bwd, contiguous, zigzag):
+    """The ring's block gradients, each taken with the rows' final (out,
+    lse), add up to the single-pass gradient (the pages ask that gradients
+    with context parallelism match a single card)."""
+    q, k, v = (x.double().numpy() for x in make_qkv_page())
+    dout = rand(q.shape, 121)
+    out, lse = attn(q, k, v, causal=True)
+    want = attn_bwd(q, k, v, dout, out, lse, causal=True)
+    for layout in (contiguous, zigzag):
+        got = ring_bwd(q, k, v, dout, 4, layout, True)
+        for g, w in zip(got, want):
+            np.testing.assert_allclose(g, w, atol=1e-12)

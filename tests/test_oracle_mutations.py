@@ -76,6 +76,60 @@ ATTENTION_MUTANTS = [
 ]
 
 
+def _bwd_pins_fail(att):
+    checks = [
+        lambda: pins.pin_bwd_finite_differences(att.attention, att.attention_bwd),
+        lambda: pins.pin_bwd_autograd(att.attention, att.attention_bwd),
+        lambda: pins.pin_bwd_closed_forms(att.attention, att.attention_bwd),
+    ]
+    failed = 0
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failed += 1
+    return failed
+
+
+BWD_MUTANTS = [
+    ("softmax-gradient row term dropped", "ds = p * (dp - dvec[:, None])", "ds = p * dp"),
+    ("row term sign", "ds = p * (dp - dvec[:, None])", "ds = p * (dp + dvec[:, None])"),
+    ("row term from out only", "np.sum(dout[:, h, :] * out[:, h, :], axis=1)",
+     "np.sum(out[:, h, :] * out[:, h, :], axis=1)"),
+    ("dq scale missing", "dq[:, h, :] = ds @ k[:, g, :] * scale", "dq[:, h, :] = ds @ k[:, g, :]"),
+    ("dk from dout", "dk[:, g, :] += ds.T @ q[:, h, :] * scale",
+     "dk[:, g, :] += ds.T @ dout[:, h, :] * scale"),
+    ("dv overwritten across the group", "dv[:, g, :] += p.T @ dout[:, h, :]",
+     "dv[:, g, :] = p.T @ dout[:, h, :]"),
+    ("P without the lse shift", "np.exp(s - np.where(finite, lse[h], 0.0)[:, None])",
+     "np.exp(s)"),
+    ("backward mask ignores offsets", "kpos = np.arange(Sk)[None, :] + k_offset\n    visible = (kpos <= qpos) if causal else np.ones((Sq, Sk), dtype=bool)\n    dq",
+     "kpos = np.arange(Sk)[None, :]\n    visible = (kpos <= qpos) if causal else np.ones((Sq, Sk), dtype=bool)\n    dq"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
+def test_bwd_mutant_is_caught(name, old, new):
+    att = _load_mutant("oracle/attention.py", old.replace("\\n", "\n"), new.replace("\\n", "\n"),
+                       "attention")
+    with np.errstate(all="ignore"):
+        assert _bwd_pins_fail(att) >= 1, f"no pin catches: {name}"
+
+
+def test_ring_bwd_mutants_are_caught():
+    """Ring backward slips: block-local (out, lse) instead of the rows'
+    final ones, and a KV block credited to the wrong rows."""
+    for old, new in [
+        ("dout[qo:qo + lq], out[qo:qo + lq], lse[:, qo:qo + lq],",
+         "dout[qo:qo + lq], *attention(q[qo:qo + lq], k[ko:ko + lk], v[ko:ko + lk], causal=(kind == DIAG), q_offset=qo, k_offset=ko),"),
+        ("dk[ko:ko + lk] += gk", "dk[qo:qo + lq] += gk"),
+    ]:
+        sch = _load_mutant("oracle/schedules.py", old, new, "schedules")
+        with pytest.raises(AssertionError):
+            pins.pin_bwd_ring(sch.ring_bwd, sch.attention, sch.attention_bwd, sch.CONTIGUOUS,
+                              sch.ZIGZAG)
+
+
 @pytest.mark.parametrize("name,old,new", ATTENTION_MUTANTS, ids=[m[0] for m in ATTENTION_MUTANTS])
 def test_attention_mutant_is_caught(name, old, new):
     att = _load_mutant("oracle/attention.py", old, new, "attention")

@@ -199,3 +199,20 @@ def test_ulysses_gqa_pins_head_mapping():
         np.testing.assert_allclose(outs[r], ref_o[r * 8:(r + 1) * 8], atol=1e-12)
     lim = pins.load_golden("ulysses_gqa_limit.txt")
     assert lim["max_degree"][0] == lim["Hkv"][0]
+
+
+# ------------------------------------------------------------- backward
+def test_bwd_finite_differences():
+    pins.pin_bwd_finite_differences(A.attention, A.attention_bwd)
+
+
+def test_bwd_autograd_special_case():
+    pins.pin_bwd_autograd(A.attention, A.attention_bwd)
+
+
+def test_bwd_closed_forms():
+    pins.pin_bwd_closed_forms(A.attention, A.attention_bwd)
+
+
+def test_ring_bwd_equals_single_pass():
+    pins.pin_bwd_ring(R.ring_bwd, A.attention, A.attention_bwd, R.CONTIGUOUS, R.ZIGZAG)
