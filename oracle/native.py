@@ -36,6 +36,13 @@ def bind(path: str):
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    lib.cp_oracle_attention_bwd.restype = ctypes.c_int
+    lib.cp_oracle_attention_bwd.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     lib.cp_oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -85,3 +92,38 @@ def attention_rows(q, k, v, rows=None, causal: bool = True, q_offset: int = 0,
     if rc != 0:
         raise ValueError(f"cp_oracle_attention failed with code {rc}")
     return out, lse
+
+
+def attention_bwd_rows(q, k, v, dout, q_rows=(), k_rows=(), causal: bool = True,
+                       q_offset: int = 0, k_offset: int = 0, n_threads: int | None = None,
+                       lib=None):
+    """Float64 gradients of sum(dout * out) for selected rows.
+
+    q, k, v, dout: CPU torch tensors (q and dout [Sq, Hq, D], k and v
+    [Sk, Hkv, D]) of one dtype, float32 or bfloat16.  Returns numpy
+    ``dq [len(q_rows), Hq, D]``, ``dk`` and ``dv [len(k_rows), Hkv, D]``.
+    """
+    import torch
+    ts = (q, k, v, dout)
+    assert all(t.dtype == q.dtype for t in ts) and q.dtype in (torch.float32, torch.bfloat16)
+    q, k, v, dout = (t.detach().cpu().contiguous() for t in ts)
+    Sq, Hq, D = q.shape
+    Sk, Hkv, _ = k.shape
+    dtype = 0 if q.dtype == torch.float32 else 1
+    qr = np.ascontiguousarray(np.asarray(q_rows, dtype=np.int64))
+    kr = np.ascontiguousarray(np.asarray(k_rows, dtype=np.int64))
+    dq = np.zeros((qr.size, Hq, D), dtype=np.float64)
+    dk = np.zeros((kr.size, Hkv, D), dtype=np.float64)
+    dv = np.zeros((kr.size, Hkv, D), dtype=np.float64)
+    if n_threads is None:
+        n_threads = len(os.sched_getaffinity(0))
+    rc = (lib or _load()).cp_oracle_attention_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dtype, Sq, Sk, Hq, Hkv, D,
+        q_offset, k_offset, int(bool(causal)),
+        qr.ctypes.data if qr.size else None, qr.size,
+        kr.ctypes.data if kr.size else None, kr.size,
+        dq.ctypes.data if qr.size else None, dk.ctypes.data if kr.size else None,
+        dv.ctypes.data if kr.size else None, int(n_threads))
+    if rc != 0:
+        raise ValueError(f"cp_oracle_attention_bwd failed with code {rc}")
+    return dq, dk, dv

@@ -267,3 +267,35 @@ def test_c_oracle_mutant_is_caught(name, old, new, tmp_path):
     finally:
         pins.ROUND_INPUTS = None
     assert failed >= 1, f"no pin catches: {name}"
+
+
+C_BWD_MUTANTS = [
+    ("row term dropped", "const double ds = p * (dp - dvi);", "const double ds = p * dp;"),
+    ("dk row term dropped", "const double ds = p * (dp - dvec[(int64_t)h * n_stat + i]);",
+     "const double ds = p * dp;"),
+    ("dv without P", "ov[d] += p * di;", "ov[d] += di;"),
+    ("dk scale missing", "ok[d] += ds * widen(q, dtype, (i * Hq + h) * (int64_t)D + d) * inv_sqrt_d;",
+     "ok[d] += ds * widen(q, dtype, (i * Hq + h) * (int64_t)D + d);"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", C_BWD_MUTANTS, ids=[m[0] for m in C_BWD_MUTANTS])
+def test_c_oracle_bwd_mutant_is_caught(name, old, new, tmp_path):
+    src = open(os.path.join(ROOT, "oracle/cp_oracle.c"), encoding="utf-8").read()
+    assert old in src
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new, 1))
+    lib = native.bind(native.build(src=str(mpath), out=str(tmp_path / "libmutant.so")))
+    from oracle.attention import attention, attention_bwd
+    g = torch.Generator().manual_seed(3)
+    Sq, Sk, Hq, Hkv, D, qo, ko = 7, 9, 4, 2, 8, 4, 2
+    q, k, v, do = (torch.randn(s, generator=g) for s in ((Sq, Hq, D), (Sk, Hkv, D),
+                                                        (Sk, Hkv, D), (Sq, Hq, D)))
+    out, lse = attention(q, k, v, q_offset=qo, k_offset=ko)
+    want = attention_bwd(q, k, v, do, out, lse, q_offset=qo, k_offset=ko)
+    rows = list(range(Sq)), list(range(Sk))
+    dq, dk, dv = native.attention_bwd_rows(q, k, v, do, *rows, q_offset=qo, k_offset=ko,
+                                           n_threads=1, lib=lib)
+    with pytest.raises(AssertionError):
+        for got, w in zip((dq, dk, dv), want):
+            np.testing.assert_allclose(got, w, atol=1e-10)
