@@ -23,7 +23,8 @@ CP_OK, CP_ERR_NULL, CP_ERR_SHAPE, CP_ERR_UNSUPPORTED, CP_ERR_CAPACITY, CP_ERR_HI
 CP_F32, CP_BF16 = 0, 1
 CP_LAYOUT_CONTIGUOUS, CP_LAYOUT_ZIGZAG = 0, 1
 CP_PAIR_SKIP, CP_PAIR_FULL, CP_PAIR_DIAG = 0, 1, 2
-CP_KERNEL_ATTN_BF16, CP_KERNEL_ATTN_F32, CP_KERNEL_MERGE, CP_KERNEL_PERMUTE = range(4)
+(CP_KERNEL_ATTN_BF16, CP_KERNEL_ATTN_F32, CP_KERNEL_MERGE, CP_KERNEL_PERMUTE, CP_KERNEL_BWD_BF16,
+ CP_KERNEL_BWD_F32, CP_KERNEL_BWD_DVEC) = range(7)
 
 LAYOUTS = {"contiguous": CP_LAYOUT_CONTIGUOUS, "zigzag": CP_LAYOUT_ZIGZAG}
 
@@ -49,6 +50,11 @@ SIGNATURES = {
     "cp_attn_block_fwd": [_P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I64, _I64, _I, _I, _P],
     "cp_lse_merge": [_P, _P, _P, _P, _P, _P, _I64, _I, _I, _P],
     "cp_ring_fwd": [_P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I, _I, _P],
+    "cp_attn_bwd_dvec": [_P, _P, _P, _I64, _I, _I, _I, _P],
+    "cp_attn_block_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I64,
+                          _I64, _I, _I, _I, _P],
+    "cp_ring_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I,
+                    _I, _P],
     "cp_seq_to_head": [_P, _P, _I64, _I, _I, _I, _I, _SZ, _P],
     "cp_head_to_seq": [_P, _P, _I64, _I, _I, _I, _I, _SZ, _P],
     "cp_layout_index": [_I, _I64, _I, _I, _P],
@@ -155,6 +161,67 @@ def cp_ring_fwd(q, k, v, P: int, layout="zigzag", rank: int = -1, causal: bool =
                            lse.data_ptr(), S, Hq, Hkv, D, P, lay, rank, int(bool(causal)),
                            _dtype_code(q), _stream(q, stream)))
     return out, lse
+
+
+def cp_attn_bwd_dvec(out, dout, dvec=None, stream=None):
+    """dvec[h][i] = sum_d dout[i][h][d] * out[i][h][d] (float32 [Hq][Sq])."""
+    import torch
+    Sq, Hq, D = out.shape
+    if dvec is None:
+        dvec = torch.empty(Hq, Sq, device=out.device, dtype=torch.float32)
+    _dense(out, dout, dvec)
+    _check(lib.cp_attn_bwd_dvec(out.data_ptr(), dout.data_ptr(), dvec.data_ptr(), Sq, Hq, D,
+                                _dtype_code(dout), _stream(out, stream)))
+    return dvec
+
+
+def cp_attn_block_bwd(q, k, v, dout, lse, dvec, dq=None, dk=None, dv=None, q_offset: int = 0,
+                      k_offset: int = 0, causal: bool = True, accumulate: bool = False,
+                      stream=None):
+    """Gradients of one query chunk against one KV block (float32 dq, dk,
+    dv), from the rows' final lse and dvec; accumulate adds into dq/dk/dv."""
+    import torch
+    Sq, Hq, D = q.shape
+    Sk, Hkv, _ = k.shape
+    if dq is None:
+        dq = torch.empty(Sq, Hq, D, device=q.device, dtype=torch.float32)
+    if dk is None:
+        dk = torch.empty(Sk, Hkv, D, device=q.device, dtype=torch.float32)
+    if dv is None:
+        dv = torch.empty(Sk, Hkv, D, device=q.device, dtype=torch.float32)
+    _dense(q, k, v, dout, lse, dvec, dq, dk, dv)
+    _check(lib.cp_attn_block_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                 lse.data_ptr(), dvec.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                 dv.data_ptr(), Sq, Sk, Hq, Hkv, D, q_offset, k_offset,
+                                 int(bool(causal)), int(bool(accumulate)), _dtype_code(q),
+                                 _stream(q, stream)))
+    return dq, dk, dv
+
+
+def cp_ring_bwd(q, k, v, out, lse, dout, P: int, layout="zigzag", rank: int = -1,
+                causal: bool = True, dq=None, dk=None, dv=None, dvec=None, stream=None):
+    """Backward of cp_ring_fwd: dq in the forward's output layout, dk and dv
+    [S][Hkv][D] float32 in natural order (contributions of the rank(s)
+    computed)."""
+    import torch
+    S, Hq, D = q.shape
+    _, Hkv, _ = k.shape
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    rows = S if rank < 0 else S // max(P, 1)
+    if dq is None:
+        dq = torch.empty(rows, Hq, D, device=q.device, dtype=torch.float32)
+    if dk is None:
+        dk = torch.empty(S, Hkv, D, device=q.device, dtype=torch.float32)
+    if dv is None:
+        dv = torch.empty(S, Hkv, D, device=q.device, dtype=torch.float32)
+    if dvec is None:
+        dvec = torch.empty(Hq, rows, device=q.device, dtype=torch.float32)
+    _dense(q, k, v, out, lse, dout, dq, dk, dv, dvec)
+    _check(lib.cp_ring_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                           lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                           dv.data_ptr(), dvec.data_ptr(), S, Hq, Hkv, D, P, lay, rank,
+                           int(bool(causal)), _dtype_code(q), _stream(q, stream)))
+    return dq, dk, dv
 
 
 def cp_seq_to_head(x, P: int, rank: int = -1, y=None, stream=None):

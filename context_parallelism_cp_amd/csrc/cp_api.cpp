@@ -58,6 +58,8 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 }
 
 // ------------------------------------------------------------------ timing
+constexpr int kKernelKinds = 7;   // cp_kernel_kind values
+
 struct Timing {
     std::mutex mu;
     bool enabled = false;
@@ -67,8 +69,8 @@ struct Timing {
     };
     std::vector<Rec> pending;
     std::vector<hipEvent_t> pool;
-    double total_ms[4] = {0, 0, 0, 0};
-    int64_t launches[4] = {0, 0, 0, 0};
+    double total_ms[kKernelKinds] = {};
+    int64_t launches[kKernelKinds] = {};
 };
 
 Timing &timing()
@@ -164,6 +166,70 @@ int launch_attn(const AttnLaunch &a, cp_dtype dtype, hipStream_t stream)
     if (dtype == CP_BF16)
         return timed_launch(CP_KERNEL_ATTN_BF16, stream, [&] { return launch_attn_bf16(a, stream); });
     return timed_launch(CP_KERNEL_ATTN_F32, stream, [&] { return launch_attn_f32(a, stream); });
+}
+
+// ---------------------------------------------------------------- backward
+int check_bwd(const void *q, const void *k, const void *v, const void *dout, const float *lse,
+              const float *dvec, const float *dq, const float *dk, const float *dv, int64_t Sq,
+              int64_t Sk, int Hq, int Hkv, int D, cp_dtype dtype)
+{
+    if ((Sq > 0 && (!q || !dout || !lse || !dvec || !dq)) || (Sk > 0 && (!k || !v || !dk || !dv)))
+        return fail(CP_ERR_NULL, "q, k, v, dout, lse, dvec, dq, dk and dv must be non-NULL");
+    if (Sq < 0 || Sk < 0)
+        return fail(CP_ERR_SHAPE, "negative sequence length (Sq=%lld, Sk=%lld)",
+                    (long long)Sq, (long long)Sk);
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return fail(CP_ERR_SHAPE, "need Hq >= 1, Hkv >= 1 and Hkv dividing Hq (Hq=%d, Hkv=%d)",
+                    Hq, Hkv);
+    if (dtype == CP_BF16) {
+        if (D != 128)
+            return fail(CP_ERR_UNSUPPORTED, "bf16 backward supports D = 128 only (D=%d)", D);
+        if ((int64_t)Hkv * D >= ((int64_t)1 << 24))
+            return fail(CP_ERR_UNSUPPORTED, "bf16 backward needs Hkv * D < 2^24 (Hkv=%d)", Hkv);
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
+            !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+            return fail(CP_ERR_ALIGN, "bf16 backward needs 16-byte aligned tensors");
+    } else if (dtype == CP_F32) {
+        if (D < 1 || D > 128)
+            return fail(CP_ERR_UNSUPPORTED, "float32 backward supports 1 <= D <= 128 (D=%d)", D);
+        if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(dout, 4) ||
+            !aligned(dq, 4) || !aligned(dk, 4) || !aligned(dv, 4))
+            return fail(CP_ERR_ALIGN, "float32 backward needs 4-byte aligned pointers");
+    } else {
+        return fail(CP_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    }
+    if (!aligned(lse, 4) || !aligned(dvec, 4))
+        return fail(CP_ERR_ALIGN, "lse and dvec must be 4-byte aligned");
+    const size_t eb = dtype == CP_BF16 ? 2 : 4;
+    const size_t qb = (size_t)Sq * Hq * D * eb, kb = (size_t)Sk * Hkv * D * eb;
+    const size_t gqb = (size_t)Sq * Hq * D * 4, gkb = (size_t)Sk * Hkv * D * 4;
+    const size_t sb = (size_t)Sq * Hq * 4;
+    const void *ins[6] = {q, k, v, dout, lse, dvec};
+    const size_t in_b[6] = {qb, kb, kb, qb, sb, sb};
+    const void *outs[3] = {dq, dk, dv};
+    const size_t out_b[3] = {gqb, gkb, gkb};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(outs[o], out_b[o], ins[i], in_b[i]))
+                return fail(CP_ERR_ALIGN, "gradient buffers must not overlap the inputs");
+        for (int o2 = o + 1; o2 < 3; ++o2)
+            if (overlaps(outs[o], out_b[o], outs[o2], out_b[o2]))
+                return fail(CP_ERR_ALIGN, "dq, dk and dv must not overlap");
+    }
+    return CP_OK;
+}
+
+int launch_bwd(const BwdLaunch &b, cp_dtype dtype, hipStream_t stream)
+{
+    if (dtype == CP_BF16)
+        return timed_launch(CP_KERNEL_BWD_BF16, stream, [&] { return launch_bwd_bf16(b, stream); });
+    return timed_launch(CP_KERNEL_BWD_F32, stream, [&] { return launch_bwd_f32(b, stream); });
+}
+
+int fill_zero(float *p, int64_t n, hipStream_t stream)
+{
+    const hipError_t e = launch_fill_zero(p, n, stream);
+    return e == hipSuccess ? CP_OK : fail(CP_ERR_HIP, "fill launch failed: %s", hipGetErrorString(e));
 }
 
 // ------------------------------------------------------------ ring helpers
@@ -440,6 +506,149 @@ int cp_ring_fwd(const void *q, const void *k, const void *v, float *out, float *
     return ok();
 }
 
+int cp_attn_bwd_dvec(const float *out, const void *dout, float *dvec, int64_t Sq, int Hq, int D,
+                     cp_dtype dtype, void *stream)
+{
+    if (Sq > 0 && (!out || !dout || !dvec))
+        return fail(CP_ERR_NULL, "out, dout and dvec must be non-NULL");
+    if (Sq < 0 || Hq < 1)
+        return fail(CP_ERR_SHAPE, "need Sq >= 0 and Hq >= 1");
+    if (dtype != CP_BF16 && dtype != CP_F32)
+        return fail(CP_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (D < 1 || D > 128)
+        return fail(CP_ERR_UNSUPPORTED, "dvec supports 1 <= D <= 128 (D=%d)", D);
+    if (!aligned(out, 4) || !aligned(dvec, 4) || !aligned(dout, dtype == CP_BF16 ? 2 : 4))
+        return fail(CP_ERR_ALIGN, "misaligned out, dout or dvec");
+    const size_t ob = (size_t)Sq * Hq * D * 4, db = (size_t)Sq * Hq * D * (dtype == CP_BF16 ? 2 : 4);
+    if (overlaps(dvec, (size_t)Sq * Hq * 4, out, ob) || overlaps(dvec, (size_t)Sq * Hq * 4, dout, db))
+        return fail(CP_ERR_ALIGN, "dvec must not overlap out or dout");
+    if (Sq == 0)
+        return ok();
+    hipStream_t st = (hipStream_t)stream;
+    int rc = timed_launch(CP_KERNEL_BWD_DVEC, st, [&] {
+        return launch_bwd_dvec(out, dout, dtype == CP_BF16 ? 1 : 0, dvec, Sq, Sq, Hq, D, st);
+    });
+    return rc ? rc : ok();
+}
+
+int cp_attn_block_bwd(const void *q, const void *k, const void *v, const void *dout,
+                      const float *lse, const float *dvec, float *dq, float *dk, float *dv,
+                      int64_t Sq, int64_t Sk, int Hq, int Hkv, int D, int64_t q_offset,
+                      int64_t k_offset, int causal, int accumulate, cp_dtype dtype, void *stream)
+{
+    int rc = check_bwd(q, k, v, dout, lse, dvec, dq, dk, dv, Sq, Sk, Hq, Hkv, D, dtype);
+    if (rc)
+        return rc;
+    if (Sq == 0 && Sk == 0)
+        return ok();
+    BwdLaunch b{};
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.dout = dout;
+    b.lse = lse;
+    b.dvec = dvec;
+    b.stat_ld = Sq;
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.Sq = Sq;
+    b.Sk = Sk;
+    b.Hq = Hq;
+    b.Hkv = Hkv;
+    b.D = D;
+    b.causal = causal ? 1 : 0;
+    b.accumulate = accumulate ? 1 : 0;
+    b.q_offset = q_offset;
+    b.k_offset = k_offset;
+    rc = launch_bwd(b, dtype, (hipStream_t)stream);
+    return rc ? rc : ok();
+}
+
+int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out, const float *lse,
+                const void *dout, float *dq, float *dk, float *dv, float *dvec, int64_t S, int Hq,
+                int Hkv, int D, int P, cp_layout layout, int rank, int causal, cp_dtype dtype,
+                void *stream)
+{
+    int rc = check_ring_shape(S, P, layout, rank);
+    if (rc)
+        return rc;
+    const int64_t rows_out = rank < 0 ? S : S / P;
+    if (S > 0 && (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !dvec))
+        return fail(CP_ERR_NULL, "every pointer of cp_ring_bwd must be non-NULL");
+    // dq, dout, lse and dvec span rows_out rows; q, k, v, dk and dv span S rows
+    rc = check_bwd(q, k, v, dout, lse, dvec, dq, dk, dv, rows_out, S, Hq, Hkv, D, dtype);
+    if (rc)
+        return rc;
+    {
+        const size_t eb = dtype == CP_BF16 ? 2 : 4;
+        const size_t qb = (size_t)S * Hq * D * eb, ob = (size_t)rows_out * Hq * D * 4;
+        const size_t gk = (size_t)S * Hkv * D * 4;
+        if (overlaps(q, qb, dq, ob) || overlaps(q, qb, dk, gk) || overlaps(q, qb, dv, gk) ||
+            overlaps(out, ob, dq, ob) || overlaps(out, ob, dk, gk) || overlaps(out, ob, dv, gk) ||
+            overlaps(dvec, (size_t)rows_out * Hq * 4, out, ob) ||
+            overlaps(dvec, (size_t)rows_out * Hq * 4, dq, ob))
+            return fail(CP_ERR_ALIGN, "gradient buffers must not overlap the inputs");
+        if (!aligned(out, 4))
+            return fail(CP_ERR_ALIGN, "out must be 4-byte aligned");
+    }
+    if (S == 0)
+        return ok();
+    hipStream_t st = (hipStream_t)stream;
+    rc = timed_launch(CP_KERNEL_BWD_DVEC, st, [&] {
+        return launch_bwd_dvec(out, dout, dtype == CP_BF16 ? 1 : 0, dvec, rows_out, rows_out, Hq,
+                               D, st);
+    });
+    if (rc)
+        return rc;
+    if ((rc = fill_zero(dq, rows_out * Hq * D, st)) || (rc = fill_zero(dk, S * Hkv * D, st)) ||
+        (rc = fill_zero(dv, S * Hkv * D, st)))
+        return rc;
+    const size_t eb = dtype == CP_BF16 ? 2 : 4;
+    const int r_begin = rank < 0 ? 0 : rank;
+    const int r_end = rank < 0 ? P : rank + 1;
+    for (int r = r_begin; r < r_end; ++r) {
+        const Split mine = rank_chunks(layout, S, P, r);
+        for (int t = 0; t < P; ++t) {
+            const int src = ((r - t) % P + P) % P;
+            const Split theirs = rank_chunks(layout, S, P, src);
+            for (int slot = 0; slot < (int)mine.chunks.size(); ++slot) {
+                const int qc = mine.chunks[slot];
+                const int64_t C = mine.chunk_len;
+                const int64_t orow = out_row_of(rank, slot, qc, C);
+                for (int kc : theirs.chunks) {
+                    const int kind = pair_kind(causal, qc, kc);
+                    if (kind == CP_PAIR_SKIP)
+                        continue;
+                    BwdLaunch b{};
+                    b.q = (const char *)q + (size_t)qc * C * Hq * D * eb;
+                    b.k = (const char *)k + (size_t)kc * C * Hkv * D * eb;
+                    b.v = (const char *)v + (size_t)kc * C * Hkv * D * eb;
+                    b.dout = (const char *)dout + (size_t)orow * Hq * D * eb;
+                    b.lse = lse + orow;
+                    b.dvec = dvec + orow;
+                    b.stat_ld = rows_out;
+                    b.dq = dq + (size_t)orow * Hq * D;
+                    b.dk = dk + (size_t)kc * C * Hkv * D;
+                    b.dv = dv + (size_t)kc * C * Hkv * D;
+                    b.Sq = C;
+                    b.Sk = C;
+                    b.Hq = Hq;
+                    b.Hkv = Hkv;
+                    b.D = D;
+                    b.causal = kind == CP_PAIR_DIAG ? 1 : 0;
+                    b.accumulate = 1;
+                    b.q_offset = (int64_t)qc * C;
+                    b.k_offset = (int64_t)kc * C;
+                    if ((rc = launch_bwd(b, dtype, st)))
+                        return rc;
+                }
+            }
+        }
+    }
+    return ok();
+}
+
 static int repack(bool to_head, const void *x, void *y, int64_t S, int H, int D, int P,
                   int rank, size_t elem_bytes, void *stream)
 {
@@ -530,7 +739,7 @@ int cp_timing_reset(void)
         t.pool.push_back(rec.stop);
     }
     t.pending.clear();
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kKernelKinds; ++i) {
         t.total_ms[i] = 0;
         t.launches[i] = 0;
     }
@@ -541,7 +750,7 @@ int cp_timing_read(cp_kernel_kind kind, double *total_ms, int64_t *launches)
 {
     if (!total_ms || !launches)
         return fail(CP_ERR_NULL, "total_ms and launches must be non-NULL");
-    if ((int)kind < 0 || (int)kind > 3)
+    if ((int)kind < 0 || (int)kind >= kKernelKinds)
         return fail(CP_ERR_SHAPE, "unknown kernel kind %d", (int)kind);
     Timing &t = timing();
     std::lock_guard<std::mutex> lock(t.mu);

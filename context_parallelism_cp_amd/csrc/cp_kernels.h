@@ -68,4 +68,38 @@ struct UnitCopy {
 };
 hipError_t launch_unit_copy(const UnitCopy &c, hipStream_t stream);
 
+// Backward of one (query chunk, KV block) pair.  q, dout: rows [0, Sq) of
+// [Sq][Hq][D]; k, v: rows [0, Sk) of [Sk][Hkv][D]; lse and dvec: columns
+// [0, Sq) of [Hq][ld] matrices (ld = stat_ld); dq [Sq][Hq][D], dk and dv
+// [Sk][Hkv][D] float32, added into when accumulate != 0.
+struct BwdLaunch {
+    const void *q;
+    const void *k;
+    const void *v;
+    const void *dout;
+    const float *lse;
+    const float *dvec;
+    int64_t stat_ld;
+    float *dq;
+    float *dk;
+    float *dv;
+    int64_t Sq;
+    int64_t Sk;
+    int Hq;
+    int Hkv;
+    int D;
+    int causal;
+    int accumulate;
+    int64_t q_offset;
+    int64_t k_offset;
+};
+// dvec[h * ld + i] = sum_d dout[i][h][d] * out[i][h][d]; dout bf16 when
+// dout_bf16 != 0, else float32.
+hipError_t launch_bwd_dvec(const float *out, const void *dout, int dout_bf16, float *dvec,
+                           int64_t ld, int64_t Sq, int Hq, int D, hipStream_t stream);
+hipError_t launch_bwd_f32(const BwdLaunch &b, hipStream_t stream);
+// p[0, n) = 0 (a kernel, so that the library records no memset)
+hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdLaunch &b, hipStream_t stream);
+
 }  // namespace cpattn

@@ -7,7 +7,11 @@
  *   [HB] "上下文并行：Ring Attention 与 Ulysses" (Context parallelism: Ring
  *        Attention and Ulysses), AI-infra handbook, train/model/context.
  *   [SP] "Sequence Parallel vs Context Parallel" blog (xxqk.cn), section 3.2,
- *        how the distributed softmax is merged.
+ *        how the distributed softmax is merged; section 5.3, gradients with
+ *        context parallelism checked against one card.
+ *   [CP] practitioner blog comparing All-Gather, Ring, Ulysses and TE
+ *        context parallelism (dpshk.com), section 4.2: the measured step is
+ *        a forward plus a backward pass.
  *
  * Conventions shared by every entry point
  *   - Tensors are dense, row-major and contiguous.  q is [Sq][Hq][D], k and v
@@ -137,6 +141,71 @@ int cp_ring_fwd(const void *q, const void *k, const void *v, float *out, float *
                 int causal, cp_dtype dtype, void *stream);
 
 /*
+ * Backward pass.  The pages give no algorithm for it: they measure forward
+ * plus backward steps ([CP] section 4.2) and ask that gradients with context
+ * parallelism match those of one card ([SP] section 5.3).  These entry
+ * points compute the gradients of L = sum(dout * out) for the attention
+ * defined above by the chain rule through its definition:
+ *   P_ij = exp(s_ij - lse_i),        Dv_i = dout_i . out_i,
+ *   dv_j = sum_i P_ij dout_i,        ds_ij = P_ij (dout_i . v_j - Dv_i),
+ *   dq_i = sum_j ds_ij k_j / sqrt(D),  dk_j = sum_i ds_ij q_i / sqrt(D),
+ * where lse and out are the query rows' final forward results (over every
+ * key the rows see), so the block gradients of a ring add up to the
+ * single-pass gradient.  KV head g receives the sum over its query heads.
+ * Rows with lse = -inf contribute nothing.
+ */
+
+/*
+ * cp_attn_bwd_dvec -- dvec[h][i] = sum_d dout[i][h][d] * out[i][h][d].
+ * out [Sq][Hq][D] float32; dout [Sq][Hq][D] of dtype (CP_BF16 or CP_F32);
+ * dvec [Hq][Sq] float32, the caller's buffer.  dvec must not overlap the
+ * inputs.  Errors: CP_ERR_NULL, CP_ERR_SHAPE, CP_ERR_UNSUPPORTED (dtype, D
+ * outside [1, 128]), CP_ERR_ALIGN, CP_ERR_HIP.
+ */
+int cp_attn_bwd_dvec(const float *out, const void *dout, float *dvec, int64_t Sq, int Hq, int D,
+                     cp_dtype dtype, void *stream);
+
+/*
+ * cp_attn_block_bwd -- gradients of one query chunk against one KV block
+ * with absolute offsets q_offset / k_offset (mask as cp_attn_block_fwd).
+ * q, dout [Sq][Hq][D] and k, v [Sk][Hkv][D] of dtype; lse and dvec
+ * [Hq][Sq] float32 (the rows' final log-sum-exp, and cp_attn_bwd_dvec of
+ * their final out); dq [Sq][Hq][D], dk and dv [Sk][Hkv][D] float32.
+ * accumulate == 0 overwrites dq, dk and dv; accumulate != 0 adds into them.
+ * dtype CP_BF16 (D = 128, Hkv * D < 2^24) runs on bf16 MFMA with float32
+ * accumulation, P and ds rounded to bf16 before the products that take
+ * them; CP_F32 (1 <= D <= 128) runs in float32.  dq, dk and dv must not
+ * overlap each other or any input.
+ * Errors: CP_ERR_NULL, CP_ERR_SHAPE, CP_ERR_UNSUPPORTED, CP_ERR_ALIGN,
+ * CP_ERR_HIP.
+ */
+int cp_attn_block_bwd(const void *q, const void *k, const void *v, const void *dout,
+                      const float *lse, const float *dvec, float *dq, float *dk, float *dv,
+                      int64_t Sq, int64_t Sk, int Hq, int Hkv, int D,
+                      int64_t q_offset, int64_t k_offset, int causal, int accumulate,
+                      cp_dtype dtype, void *stream);
+
+/*
+ * cp_ring_bwd -- the backward pass of cp_ring_fwd: every (query chunk, key
+ * chunk) pair that the forward ring computes (cp_ring_plan, pairs not
+ * SKIP) contributes its block gradients; dq accumulates on the query rows,
+ * dk and dv on the KV block's rows (on a real ring these accumulators
+ * travel with the KV block and return to its owner after P steps).
+ * q, k, v: natural order as in cp_ring_fwd.  out, lse, dout and dq use the
+ * forward's output layout: rank == -1 natural order ([S][Hq][D], [Hq][S]);
+ * 0 <= rank < P that rank's local order ([S/P][Hq][D], [Hq][S/P]).  dout
+ * has dtype; out and lse are float32 (cp_ring_fwd's results).  dq is
+ * overwritten.  dk and dv are [S][Hkv][D] float32 in natural order and are
+ * overwritten with the contributions of the rank(s) computed.  dvec is a
+ * caller-provided float32 scratch buffer of Hq * (rows of out) elements.
+ * Errors: as cp_ring_fwd and cp_attn_block_bwd.
+ */
+int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out,
+                const float *lse, const void *dout, float *dq, float *dk, float *dv,
+                float *dvec, int64_t S, int Hq, int Hkv, int D, int P, cp_layout layout,
+                int rank, int causal, cp_dtype dtype, void *stream);
+
+/*
  * cp_seq_to_head / cp_head_to_seq -- the Ulysses layout changes of [HB],
  * section "Ulysses：在序列和头之间转置", done as local repacks: the all-to-all
  * between P ranks becomes a strided copy on one GPU.  Elements are opaque
@@ -200,7 +269,10 @@ typedef enum {
     CP_KERNEL_ATTN_BF16 = 0,
     CP_KERNEL_ATTN_F32 = 1,
     CP_KERNEL_MERGE = 2,
-    CP_KERNEL_PERMUTE = 3
+    CP_KERNEL_PERMUTE = 3,
+    CP_KERNEL_BWD_BF16 = 4,   /* backward dq and dk/dv kernels, bf16 */
+    CP_KERNEL_BWD_F32 = 5,    /* backward dq and dk/dv kernels, float32 */
+    CP_KERNEL_BWD_DVEC = 6
 } cp_kernel_kind;
 
 int cp_timing_enable(int enable);

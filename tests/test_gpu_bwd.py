@@ -1,0 +1,170 @@
+"""Backward pass: HIP path against the oracle, element by element, through
+the C-ABI.
+
+Each case runs the library's own forward (cp_attn_block_fwd / cp_ring_fwd)
+to get out and lse, then cp_attn_bwd_dvec and the backward entry point;
+the oracle computes the float64 forward and the float64 gradients
+(oracle.attention.attention_bwd, and compositions of it over the ring's
+pairs) from the same input bytes.
+
+Tolerances (max abs error of dq, dk, dv): float32 path 2e-5; bf16 path
+2e-2 of the largest reference magnitude per tensor (P and ds are rounded to
+bf16 before the products that take them, relative error 2^-9 per term,
+summed over thousands of terms with random signs).  Gradient buffers sit
+between sentinel guard regions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import context_parallelism_cp_amd as cp
+from oracle import attention as OA
+from oracle import schedules as OS
+from seeded_inputs import make_qkv
+
+from test_gpu_parity import DEV, Guarded, announce, dev
+
+pytestmark = pytest.mark.gpu
+
+F32_GRAD_TOL = 2e-5
+
+
+def grads_compare(got, want, tol, what, rel=False):
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        g = g.detach().double().cpu().numpy() if torch.is_tensor(g) else g
+        assert not np.isnan(g).any(), f"{what} {name}: NaN"
+        err = float(np.abs(g - w).max()) if g.size else 0.0
+        scale = float(np.abs(w).max()) if (rel and w.size) else 1.0
+        print(f"    {what} {name}: max|err| = {err:.3e} (ref max {np.abs(w).max() if w.size else 0:.3e})",
+              flush=True)
+        assert err <= tol * max(scale, 1e-30), f"{what} {name}: error {err}"
+
+
+def inputs(Sq, Sk, Hq, Hkv, D, dtype, seed):
+    q, _, _ = make_qkv(S=Sq, H=Hq, D=D, seed=seed, dtype=dtype)
+    _, k, v = make_qkv(S=Sk, H=Hkv, D=D, seed=seed + 1, dtype=dtype)
+    dout, _, _ = make_qkv(S=Sq, H=Hq, D=D, seed=seed + 2, dtype=dtype)
+    return q, k, v, dout
+
+
+def run_block_bwd(q, k, v, dout, qo, ko, causal, accumulate_twice=False):
+    Sq, Hq, D = q.shape
+    Sk, Hkv, _ = k.shape
+    dq, dk, dv = Guarded(Sq, Hq, D), Guarded(Sk, Hkv, D), Guarded(Sk, Hkv, D)
+    dq_t, dk_t, dv_t = (g.t for g in (dq, dk, dv))
+    qd, kd, vd, dd = dev(q, k, v, dout)
+    out, lse = cp.cp_attn_block_fwd(qd, kd, vd, q_offset=qo, k_offset=ko, causal=causal)
+    dvec = cp.cp_attn_bwd_dvec(out, dd)
+    cp.cp_attn_block_bwd(qd, kd, vd, dd, lse, dvec, dq_t, dk_t, dv_t, q_offset=qo, k_offset=ko,
+                         causal=causal)
+    if accumulate_twice:
+        cp.cp_attn_block_bwd(qd, kd, vd, dd, lse, dvec, dq_t, dk_t, dv_t, q_offset=qo,
+                             k_offset=ko, causal=causal, accumulate=True)
+    torch.cuda.synchronize()
+    for g in (dq, dk, dv):
+        g.check()
+    return dq_t, dk_t, dv_t
+
+
+def oracle_grads(q, k, v, dout, qo, ko, causal):
+    out, lse = OA.attention(q, k, v, causal=causal, q_offset=qo, k_offset=ko)
+    return OA.attention_bwd(q, k, v, dout, out, lse, causal=causal, q_offset=qo, k_offset=ko)
+
+
+# ----------------------------------------------------------------- float32
+@pytest.mark.parametrize("Sq,Sk,Hq,Hkv,D,qo,ko,causal", [
+    (37, 53, 4, 2, 16, 20, 5, True),
+    (37, 53, 4, 2, 16, 0, 0, False),
+    (130, 70, 2, 1, 128, 100, 90, True),
+    (65, 129, 3, 3, 40, 64, 0, True),
+    (10, 10, 2, 2, 16, 0, 7, True),      # first rows see no key, last keys seen by nobody
+    (5, 8, 2, 2, 16, 0, 100, True),      # nothing visible: all gradients zero
+])
+def test_f32_block_bwd(Sq, Sk, Hq, Hkv, D, qo, ko, causal):
+    announce(f"f32 block bwd Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} D={D} qo={qo} ko={ko} causal={causal}")
+    q, k, v, dout = inputs(Sq, Sk, Hq, Hkv, D, torch.float32, Sq + 3 * Sk)
+    got = run_block_bwd(q, k, v, dout, qo, ko, causal)
+    grads_compare(got, oracle_grads(q, k, v, dout, qo, ko, causal), F32_GRAD_TOL, "f32 block")
+
+
+def test_f32_block_bwd_accumulate():
+    announce("f32 block bwd accumulate twice")
+    q, k, v, dout = inputs(33, 41, 4, 2, 16, torch.float32, 5)
+    got = run_block_bwd(q, k, v, dout, 10, 0, True, accumulate_twice=True)
+    want = [2 * w for w in oracle_grads(q, k, v, dout, 10, 0, True)]
+    grads_compare(got, want, 2 * F32_GRAD_TOL, "f32 accumulate")
+
+
+def test_f32_block_bwd_empty_sides():
+    announce("f32 block bwd Sq=0 and Sk=0")
+    q, k, v, dout = inputs(8, 8, 2, 2, 16, torch.float32, 9)
+    # no queries: dk = dv = 0 written
+    dk, dv = Guarded(8, 2, 16), Guarded(8, 2, 16)
+    dk.t.fill_(7.0), dv.t.fill_(7.0)
+    e = torch.empty(0, 2, 16, device=DEV)
+    cp.cp_attn_block_bwd(e, k.to(DEV), v.to(DEV), e, torch.empty(2, 0, device=DEV),
+                         torch.empty(2, 0, device=DEV), e, dk.t, dv.t)
+    # no keys: dq = 0 written
+    dq = Guarded(8, 2, 16)
+    dq.t.fill_(7.0)
+    ek = torch.empty(0, 2, 16, device=DEV)
+    lse = torch.full((2, 8), -float("inf"), device=DEV)
+    cp.cp_attn_block_bwd(q.to(DEV), ek, ek, dout.to(DEV), lse, torch.zeros(2, 8, device=DEV),
+                         dq.t, ek, ek)
+    torch.cuda.synchronize()
+    for g in (dk, dv, dq):
+        g.check()
+        assert bool((g.t == 0).all())
+
+
+def ring_rank_oracle(q, k, v, dout, P, layout, rank):
+    """dq of rank r's rows (its local order) and the rank's dk/dv
+    contributions, composed from oracle.attention_bwd over its pairs."""
+    qn, kn, vn, dn = (x.double().numpy() for x in (q, k, v, dout))
+    out, lse = OA.attention(qn, kn, vn)
+    S = qn.shape[0]
+    dq = np.zeros_like(qn)
+    dk = np.zeros_like(kn)
+    dv = np.zeros_like(vn)
+    for (r, _t, _qc, _kc, qo, ko, lq, lk, kind) in OS.ring_plan(S, P, layout, rank):
+        if kind == OS.SKIP:
+            continue
+        gq, gk, gv = OA.attention_bwd(qn[qo:qo + lq], kn[ko:ko + lk], vn[ko:ko + lk],
+                                      dn[qo:qo + lq], out[qo:qo + lq], lse[:, qo:qo + lq],
+                                      causal=(kind == OS.DIAG), q_offset=qo, k_offset=ko)
+        dq[qo:qo + lq] += gq
+        dk[ko:ko + lk] += gk
+        dv[ko:ko + lk] += gv
+    if rank >= 0:
+        dq = dq[OS.layout_index(layout, S, P, rank)]
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag"])
+def test_f32_ring_bwd_page_inputs(layout):
+    announce(f"f32 ring bwd P=4 {layout} on make_qkv()")
+    q, k, v = make_qkv()
+    dout, _, _ = make_qkv(S=32, H=8, D=16, seed=77)
+    lay = cp.LAYOUTS[layout]
+    qd, kd, vd = dev(q, k, v)
+    for rank in [-1, 0, 1, 2, 3]:
+        out, lse = cp.cp_ring_fwd(qd, kd, vd, 4, layout, rank)
+        if rank >= 0:
+            idx = torch.from_numpy(OS.layout_index(lay, 32, 4, rank).astype(np.int64))
+            dd = dout[idx].to(DEV).contiguous()
+        else:
+            dd = dout.to(DEV)
+        rows = 32 if rank < 0 else 8
+        dq, dk, dv = Guarded(rows, 8, 16), Guarded(32, 8, 16), Guarded(32, 8, 16)
+        cp.cp_ring_bwd(qd, kd, vd, out, lse, dd, 4, layout, rank, dq=dq.t, dk=dk.t, dv=dv.t)
+        torch.cuda.synchronize()
+        for g in (dq, dk, dv):
+            g.check()
+        want = ring_rank_oracle(q, k, v, dout, 4, lay, rank)
+        grads_compare((dq.t, dk.t, dv.t), want, F32_GRAD_TOL, f"ring {layout} rank {rank}")
+    # the full ring gradient equals the single-pass gradient
+    full = OS.ring_bwd(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                       dout.double().numpy(), 4, lay)
+    single = oracle_grads(q, k, v, dout, 0, 0, True)
+    for a, b in zip(full, single):
+        np.testing.assert_allclose(a, b, atol=1e-12)

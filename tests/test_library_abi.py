@@ -25,7 +25,8 @@ def header_functions():
 def test_header_declares_the_entry_points():
     fns = header_functions()
     for name in ("cp_attn_block_fwd", "cp_lse_merge", "cp_ring_fwd", "cp_seq_to_head",
-                 "cp_head_to_seq", "cp_layout_index", "cp_ring_plan", "cp_last_error"):
+                 "cp_head_to_seq", "cp_layout_index", "cp_ring_plan", "cp_last_error",
+                 "cp_attn_bwd_dvec", "cp_attn_block_bwd", "cp_ring_bwd"):
         assert name in fns
 
 
@@ -175,3 +176,60 @@ def test_timing_api_without_launches():
     cp.cp_timing_enable(False)
     with pytest.raises(cp.CpError):
         cp.cp_timing_read(9)
+
+
+def rc_block_bwd(**kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, dout=FAKE * 4, lse=FAKE * 5, dvec=FAKE * 6,
+             dq=FAKE * 7, dk=FAKE * 8, dv=FAKE * 9, Sq=8, Sk=8, Hq=4, Hkv=2, D=128, qo=0, ko=0,
+             causal=1, acc=0, dtype=cp.CP_BF16)
+    a.update(kw)
+    return cp.lib.cp_attn_block_bwd(a["q"], a["k"], a["v"], a["dout"], a["lse"], a["dvec"],
+                                    a["dq"], a["dk"], a["dv"], a["Sq"], a["Sk"], a["Hq"],
+                                    a["Hkv"], a["D"], a["qo"], a["ko"], a["causal"], a["acc"],
+                                    a["dtype"], None)
+
+
+def test_block_bwd_argument_errors():
+    assert rc_block_bwd(dout=None) == cp.CP_ERR_NULL
+    assert rc_block_bwd(dvec=None) == cp.CP_ERR_NULL
+    assert rc_block_bwd(dk=None) == cp.CP_ERR_NULL
+    assert rc_block_bwd(dq=None, q=None, dout=None, lse=None, dvec=None, dk=None, dv=None,
+                        k=None, v=None, Sq=0, Sk=0) == cp.CP_OK      # empty tensors may be NULL
+    assert rc_block_bwd(Sk=-1) == cp.CP_ERR_SHAPE
+    assert rc_block_bwd(Hq=3) == cp.CP_ERR_SHAPE
+    assert rc_block_bwd(D=64) == cp.CP_ERR_UNSUPPORTED
+    assert rc_block_bwd(D=129, dtype=cp.CP_F32) == cp.CP_ERR_UNSUPPORTED
+    assert rc_block_bwd(dtype=5) == cp.CP_ERR_UNSUPPORTED
+    assert rc_block_bwd(Hq=1 << 17, Hkv=1 << 17) == cp.CP_ERR_UNSUPPORTED
+    assert rc_block_bwd(dout=FAKE * 4 + 2) == cp.CP_ERR_ALIGN
+    assert rc_block_bwd(dq=FAKE * 7 + 4) == cp.CP_ERR_ALIGN          # 16 B for bf16
+    assert rc_block_bwd(dq=FAKE * 4) == cp.CP_ERR_ALIGN              # dq overlaps dout
+    assert "overlap" in cp.cp_last_error()
+    assert rc_block_bwd(dv=FAKE * 8) == cp.CP_ERR_ALIGN              # dv overlaps dk
+    assert rc_block_bwd(Sq=0, Sk=0) == cp.CP_OK and cp.cp_last_error() == ""
+
+
+def test_dvec_argument_errors():
+    f = cp.lib.cp_attn_bwd_dvec
+    assert f(None, FAKE, FAKE * 2, 8, 4, 128, cp.CP_BF16, None) == cp.CP_ERR_NULL
+    assert f(FAKE, FAKE * 2, FAKE * 3, 8, 0, 128, cp.CP_BF16, None) == cp.CP_ERR_SHAPE
+    assert f(FAKE, FAKE * 2, FAKE * 3, 8, 4, 0, cp.CP_F32, None) == cp.CP_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE * 2, FAKE * 3, 8, 4, 128, 9, None) == cp.CP_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE * 2, FAKE, 8, 4, 128, cp.CP_BF16, None) == cp.CP_ERR_ALIGN  # dvec on out
+    assert f(None, None, None, 0, 4, 128, cp.CP_BF16, None) == cp.CP_OK
+
+
+def test_ring_bwd_argument_errors():
+    f = cp.lib.cp_ring_bwd
+    a = [FAKE * i for i in range(1, 11)]   # q k v out lse dout dq dk dv dvec
+    assert f(*a, 30, 8, 8, 16, 4, cp.CP_LAYOUT_ZIGZAG, -1, 1, cp.CP_F32, None) == cp.CP_ERR_SHAPE
+    assert f(*a, 32, 8, 8, 16, 4, cp.CP_LAYOUT_ZIGZAG, 4, 1, cp.CP_F32, None) == cp.CP_ERR_SHAPE
+    assert f(None, *a[1:], 32, 8, 8, 16, 4, cp.CP_LAYOUT_ZIGZAG, -1, 1, cp.CP_F32,
+             None) == cp.CP_ERR_NULL
+    assert f(*a, 32, 8, 8, 100, 4, cp.CP_LAYOUT_ZIGZAG, -1, 1, cp.CP_BF16,
+             None) == cp.CP_ERR_UNSUPPORTED
+    b = list(a)
+    b[6] = a[0]                                 # dq on q
+    assert f(*b, 32, 8, 8, 16, 4, cp.CP_LAYOUT_ZIGZAG, -1, 1, cp.CP_F32, None) == cp.CP_ERR_ALIGN
+    assert f(None, None, None, None, None, None, None, None, None, None, 0, 8, 8, 16, 4,
+             cp.CP_LAYOUT_ZIGZAG, -1, 1, cp.CP_F32, None) == cp.CP_OK
