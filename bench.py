@@ -109,13 +109,122 @@ def cpu_baseline(q, k, v, budget_s=12.0, max_rows=512):
     }
 
 
+def backward(args, cp, torch, q_host, dq, dk, dv, dku, dvu, ql, kl, vl, uly_out_l, uly_lse,
+             ring_out, ring_lse, stream):
+    """The backward pass of the same two shares (one JSON line).
+
+    Ring share: cp_ring_bwd of zigzag rank 0 (its 17 computed pairs, dq in
+    the rank's local order, dk/dv over the whole sequence).  Ulysses share:
+    seq->head of dout, cp_attn_bwd_dvec, cp_attn_block_bwd of the 4 local
+    query heads against their KV head, head->seq of dq, dk and dv.  The
+    forward results (out, lse) are computed once before timing.
+    FLOP: 2.5x the forward's causal-adjusted count (S, dP, dV, dK and dQ:
+    10*D per visible pair and head, diagonal chunk counted half).
+    """
+    from seeded_inputs import make_qkv
+    dev = "cuda:0"
+    rows = S // P
+    hp, hkp = HQ // P, HKV_ULY // P
+    g = make_qkv(S=S, H=HQ, D=D, seed=1, dtype=torch.bfloat16)[0]
+    dout_seq = g.to(dev)                              # upstream gradient, natural order
+    idx = torch.from_numpy(cp.cp_layout_index("zigzag", S, P, RING_RANK).astype("int64"))
+    dout_ring = g[idx].to(dev).contiguous()           # the ring rank's rows, local order
+    del g
+    # forward results
+    cp.cp_ring_fwd(dq, dk, dv, P, "zigzag", RING_RANK, out=ring_out, lse=ring_lse, stream=stream)
+    cp.cp_seq_to_head(dq, P, ULY_RANK, y=ql, stream=stream)
+    cp.cp_seq_to_head(dku, P, ULY_RANK, y=kl, stream=stream)
+    cp.cp_seq_to_head(dvu, P, ULY_RANK, y=vl, stream=stream)
+    cp.cp_attn_block_fwd(ql, kl, vl, uly_out_l, uly_lse, stream=stream)
+    f32 = dict(device=dev, dtype=torch.float32)
+    g_q_ring, g_k_ring, g_v_ring = (torch.empty(rows, HQ, D, **f32), torch.empty(S, HQ, D, **f32),
+                                    torch.empty(S, HQ, D, **f32))
+    dvec_ring = torch.empty(HQ, rows, **f32)
+    dout_l = torch.empty(S, hp, D, device=dev, dtype=torch.bfloat16)
+    dvec_l = torch.empty(hp, S, **f32)
+    g_ql, g_kl, g_vl = (torch.empty(S, hp, D, **f32), torch.empty(S, hkp, D, **f32),
+                        torch.empty(S, hkp, D, **f32))
+    g_q_seq = torch.zeros(S, HQ, D, **f32)
+    g_k_seq = torch.zeros(S, HKV_ULY, D, **f32)
+    g_v_seq = torch.zeros(S, HKV_ULY, D, **f32)
+
+    def step():
+        cp.cp_ring_bwd(dq, dk, dv, ring_out, ring_lse, dout_ring, P, "zigzag", RING_RANK,
+                       dq=g_q_ring, dk=g_k_ring, dv=g_v_ring, dvec=dvec_ring, stream=stream)
+        cp.cp_seq_to_head(dout_seq, P, ULY_RANK, y=dout_l, stream=stream)
+        cp.cp_attn_bwd_dvec(uly_out_l, dout_l, dvec_l, stream=stream)
+        cp.cp_attn_block_bwd(ql, kl, vl, dout_l, uly_lse, dvec_l, g_ql, g_kl, g_vl, stream=stream)
+        cp.cp_head_to_seq(g_ql, g_q_seq, P, ULY_RANK, stream=stream)
+        cp.cp_head_to_seq(g_kl, g_k_seq, P, ULY_RANK, stream=stream)
+        cp.cp_head_to_seq(g_vl, g_v_seq, P, ULY_RANK, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    cp.cp_timing_enable(True)
+    cp.cp_timing_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    bwd_ms, bwd_n = cp.cp_timing_read(cp.CP_KERNEL_BWD_BF16)
+    dvec_ms, _ = cp.cp_timing_read(cp.CP_KERNEL_BWD_DVEC)
+    perm_ms, _ = cp.cp_timing_read(cp.CP_KERNEL_PERMUTE)
+    cp.cp_timing_enable(False)
+    flop_step = 2.5 * (ring_share_flop(S, HQ, D, P) + ulysses_share_flop(S, hp, D))
+    kern_tflops = flop_step * args.steps / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else None
+    result = {
+        "metric": "causal block-attn bwd TFLOP/s + % bf16 MFMA peak, S=128K H=32 D=128",
+        "value": round(flop_step * args.steps / elapsed / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("backward pass of one rank's share of a 128K-token causal attention "
+                         "layer: zigzag ring rank 0 (S=131072, Hq=Hkv=32, D=128, P=8) plus "
+                         "the Ulysses GQA rank (4 q heads on 1 KV head over 131072 tokens); "
+                         "bf16 q, k, v, dout; fp32 gradients"),
+            "parts": "bwd",
+            "flop_per_step": flop_step,
+            "flop_convention": "2.5 x (4*D*Hq per visible (q,k) pair, diagonal chunk half)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "bwd_dq_kernel + bwd_dkdv_kernel",
+            "achieved": round(kern_tflops, 2) if kern_tflops else None,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4) if kern_tflops else None,
+            "traffic": None,
+            "launches": bwd_n,
+            "avg_launch_ms": round(bwd_ms / max(bwd_n, 1), 4),
+        },
+        "breakdown": {
+            "bwd_kernels_ms_per_step": round(bwd_ms / args.steps, 3),
+            "dvec_ms_per_step": round(dvec_ms / args.steps, 3),
+            "repack_ms_per_step": round(perm_ms / args.steps, 3),
+        },
+    }
+    print(json.dumps(result))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--part", choices=["both", "ring", "ulysses"], default="both")
+    ap.add_argument("--part", choices=["both", "ring", "ulysses", "bwd"], default="both",
+                    help="bwd: time the backward pass of both shares instead")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="before warm-up, copy 1 GiB device to device once (a plain copy "
                          "kernel of known size that scales HBM byte counters)")
@@ -169,6 +278,11 @@ def main():
         dst.copy_(src)          # reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
         del src, dst
+
+    if args.part == "bwd":
+        backward(args, cp, torch, q, dq, dk, dv, dku, dvu, ql, kl, vl, uly_out_l, uly_lse,
+                 ring_out, ring_lse, stream)
+        return
 
     for _ in range(args.warmup):
         step()
