@@ -153,13 +153,27 @@ def attention_bwd(q, k, v, dout, out, lse, causal: bool = True, q_offset: int = 
     Shapes as in ``attention``; dout and out [Sq, Hq, D], lse [Hq, Sq].
     Returns float64 dq [Sq, Hq, D], dk and dv [Sk, Hkv, D].
     """
+    Sq, Sk = q.shape[0], k.shape[0]
+    qpos = np.arange(Sq)[:, None] + q_offset
+    kpos = np.arange(Sk)[None, :] + k_offset
+    visible = (kpos <= qpos) if causal else np.ones((Sq, Sk), dtype=bool)
+    return _bwd_masked(q, k, v, dout, out, lse, visible)
+
+
+def attention_bwd_at(q, k, v, dout, out, lse, qpos, kpos, causal: bool = True):
+    """``attention_bwd`` with explicit absolute positions (as ``attention_at``)."""
+    qp = np.asarray(qpos, dtype=np.int64)[:, None]
+    kp = np.asarray(kpos, dtype=np.int64)[None, :]
+    visible = (kp <= qp) if causal else np.ones((qp.shape[0], kp.shape[1]), dtype=bool)
+    return _bwd_masked(q, k, v, dout, out, lse, visible)
+
+
+def _bwd_masked(q, k, v, dout, out, lse, visible):
+    """The chain rule of ``attention_bwd`` for a given visibility matrix."""
     q, k, v, dout, out, lse = map(_as_f64, (q, k, v, dout, out, lse))
     Sq, Hq, D = q.shape
     Sk, Hkv, _ = k.shape
     group = Hq // Hkv
-    qpos = np.arange(Sq)[:, None] + q_offset
-    kpos = np.arange(Sk)[None, :] + k_offset
-    visible = (kpos <= qpos) if causal else np.ones((Sq, Sk), dtype=bool)
     dq = np.zeros((Sq, Hq, D))
     dk = np.zeros((Sk, Hkv, D))
     dv = np.zeros((Sk, Hkv, D))
@@ -177,3 +191,31 @@ def attention_bwd(q, k, v, dout, out, lse, causal: bool = True, q_offset: int = 
         dq[:, h, :] = ds @ k[:, g, :] * scale
         dk[:, g, :] += ds.T @ q[:, h, :] * scale
     return dq, dk, dv
+
+
+def attention_at(q, k, v, qpos, kpos, causal: bool = True):
+    """``attention`` with explicit absolute positions: key j is visible to
+    query i iff kpos[j] <= qpos[i] (the handbook's mask, whose positions are
+    q_offset + i and k_offset + j, for any position arrays -- needed when a
+    rank's rows are not one contiguous run, as in the striped split).
+    Returns (out [Sq, Hq, D], lse [Hq, Sq]) like ``attention``.
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    Sq, Hq, D = q.shape
+    Sk, Hkv, _ = k.shape
+    group = Hq // Hkv
+    qp = np.asarray(qpos, dtype=np.int64)[:, None]
+    kp = np.asarray(kpos, dtype=np.int64)[None, :]
+    visible = (kp <= qp) if causal else np.ones((Sq, Sk), dtype=bool)
+    out = np.zeros((Sq, Hq, D))
+    lse = np.full((Hq, Sq), NEG_INF)
+    for h in range(Hq):
+        g = h // group
+        s = np.where(visible, (q[:, h, :] @ k[:, g, :].T) / np.sqrt(D), NEG_INF)
+        has = visible.any(axis=1)
+        m = np.where(has, s.max(axis=1, initial=NEG_INF), 0.0)
+        e = np.where(visible, np.exp(s - m[:, None]), 0.0)
+        tot = e.sum(axis=1)
+        lse[h, has] = m[has] + np.log(tot[has])
+        out[has, h, :] = (e[has] / tot[has, None]) @ v[:, g, :]
+    return out, lse

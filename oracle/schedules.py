@@ -27,14 +27,19 @@ Readings where the page is silent (the page has no zigzag ring code):
   when the key chunk comes first.
 * plan order -- for each rank, each step, each query chunk in local
   order, each key chunk in local order.
+* striped split (from the "Sequence Parallel vs Context Parallel" blog,
+  section 3.3, prose only) -- stripes of one token dealt round-robin:
+  position t lives on rank t mod P.  Every (rank, source) pair of the ring
+  is computed (the positions interleave, so no block is wholly masked),
+  under the causal mask taken on the true positions.
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .attention import attention, attention_bwd, lse_merge
+from .attention import attention, attention_at, attention_bwd, attention_bwd_at, lse_merge
 
-CONTIGUOUS, ZIGZAG = 0, 1
+CONTIGUOUS, ZIGZAG, STRIPED = 0, 1, 2
 SKIP, FULL, DIAG = 0, 1, 2
 
 
@@ -60,10 +65,14 @@ def layout_index(layout: int, S: int, P: int, rank: int) -> np.ndarray:
 
     Contiguous: the ring section's ``slice(rank*C, (rank+1)*C)``.
     Zigzag: the 2P-chunk split, chunks concatenated in the order listed.
+    Striped: positions rank, rank + P, rank + 2P, ... (stripes of one token
+    dealt round-robin, the reading stated in ``ring_striped``).
     """
     if layout == CONTIGUOUS:
         C = S // P
         return np.arange(rank * C, (rank + 1) * C, dtype=np.int64)
+    if layout == STRIPED:
+        return np.arange(rank, S, P, dtype=np.int64)
     C = S // (2 * P)
     return np.concatenate([np.arange(c * C, (c + 1) * C, dtype=np.int64)
                            for c in split_zigzag(P)[rank]])
@@ -85,6 +94,16 @@ def ring_plan(S: int, P: int, layout: int, rank: int, causal: bool = True):
     """
     ranks = range(P) if rank < 0 else [rank]
     pairs = []
+    if layout == STRIPED:
+        # every rank's positions interleave with every other's: each pair is
+        # computed, under the causal mask when causal; chunk id = rank id,
+        # offsets are local row offsets (0)
+        C = S // P
+        for r in ranks:
+            for t in range(P):
+                src = (r - t) % P
+                pairs.append((r, t, r, src, 0, 0, C, C, DIAG if causal else FULL))
+        return pairs
     for r in ranks:
         q_chunks, C = _chunks(layout, S, P, r)
         for t in range(P):
@@ -168,6 +187,41 @@ def ring_zigzag(q, k, v, P: int, causal: bool = True):
     return outs, lses, units
 
 
+def ring_striped(q, k, v, P: int, causal: bool = True):
+    """Striped ring.  The "Sequence Parallel vs Context Parallel" blog,
+    section 3.3, gives Striped Attention in prose only: KV is dealt to the
+    devices in interleaved stripes so that each holds early and late
+    positions and every ring step carries about the same causal work (the
+    handbook's zigzag section mentions a similar striped split).
+
+    Reading: stripes of one token, position t on rank t mod P, so rank r's
+    local row j is position r + j*P; the ring is the handbook's loop
+    (src = (r - t) mod P, merge every block with the log-sum-exp rule), each
+    block attended with the true positions of its rows.
+
+    Returns (outs, lses, pairs): per rank its local out [S/P, Hq, D], lse
+    [Hq, S/P], and the number of visible (query, key) pairs it computed per
+    head.
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    S = q.shape[0]
+    outs, lses, work_pairs = [], [], []
+    for rank in range(P):
+        qpos = layout_index(STRIPED, S, P, rank)
+        state = None
+        n = 0
+        for step in range(P):
+            src = (rank - step) % P
+            kpos = layout_index(STRIPED, S, P, src)
+            o, l = attention_at(q[qpos], k[kpos], v[kpos], qpos, kpos, causal=causal)
+            state = (o, l) if state is None else lse_merge(*state, o, l)
+            n += int(np.sum(kpos[None, :] <= qpos[:, None])) if causal else qpos.size * kpos.size
+        outs.append(state[0])
+        lses.append(state[1])
+        work_pairs.append(n)
+    return outs, lses, work_pairs
+
+
 def ring_bwd(q, k, v, dout, P: int, layout: int, causal: bool = True):
     """Backward pass through the ring (no algorithm on the pages; the
     plainest reading of running the forward ring backwards).
@@ -186,8 +240,16 @@ def ring_bwd(q, k, v, dout, P: int, layout: int, causal: bool = True):
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for (_r, _t, _qc, _kc, qo, ko, lq, lk, kind) in ring_plan(S, P, layout, -1, causal):
+    for (r, _t, _qc, src, qo, ko, lq, lk, kind) in ring_plan(S, P, layout, -1, causal):
         if kind == SKIP:
+            continue
+        if layout == STRIPED:
+            qi, ki = layout_index(STRIPED, S, P, r), layout_index(STRIPED, S, P, src)
+            gq, gk, gv = attention_bwd_at(q[qi], k[ki], v[ki], dout[qi], out[qi], lse[:, qi],
+                                          qi, ki, causal=causal)
+            dq[qi] += gq
+            dk[ki] += gk
+            dv[ki] += gv
             continue
         gq, gk, gv = attention_bwd(q[qo:qo + lq], k[ko:ko + lk], v[ko:ko + lk],
                                    dout[qo:qo + lq], out[qo:qo + lq], lse[:, qo:qo + lq],

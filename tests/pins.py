@@ -51,8 +51,9 @@ def rand(shape, seed):
 
 
 # ----------------------------------------------------------- brute force
-def brute_force(q, k, v, causal, q_offset, k_offset):
-    """Pure-Python loops: p_j = exp(s_j) / sum_j exp(s_j) over visible j."""
+def brute_force(q, k, v, causal, q_offset, k_offset, qpos=None, kpos=None):
+    """Pure-Python loops: p_j = exp(s_j) / sum_j exp(s_j) over visible j.
+    Positions are q_offset + i and k_offset + j unless given explicitly."""
     Sq, Hq, D = q.shape
     Sk, Hkv, _ = k.shape
     group = Hq // Hkv
@@ -63,7 +64,9 @@ def brute_force(q, k, v, causal, q_offset, k_offset):
         for i in range(Sq):
             e = []
             for j in range(Sk):
-                if causal and k_offset + j > q_offset + i:
+                pq = q_offset + i if qpos is None else int(qpos[i])
+                pk = k_offset + j if kpos is None else int(kpos[j])
+                if causal and pk > pq:
                     continue
                 s = sum(float(q[i, h, d]) * float(k[j, g, d]) for d in range(D)) / math.sqrt(D)
                 e.append((j, math.exp(s)))
@@ -93,6 +96,56 @@ def pin_brute_force(attn, cases=None):
         assert np.array_equal(np.isinf(l), np.isinf(lb))
         np.testing.assert_allclose(np.where(np.isinf(lb), 0, l), np.where(np.isinf(lb), 0, lb),
                                    rtol=0, atol=1e-12)
+
+
+def pin_attention_at(attn_at, attn):
+    """Explicit positions: brute force on scattered positions (including
+    rows that see no key), and offsets written as positions reduce to the
+    offset form."""
+    rng = np.random.default_rng(31)
+    for n, (Sq, Sk, Hq, Hkv, D) in enumerate([(5, 7, 2, 1, 3), (6, 4, 4, 2, 2), (4, 6, 1, 1, 4)]):
+        q, k, v = rand((Sq, Hq, D), 200 + n), rand((Sk, Hkv, D), 210 + n), rand((Sk, Hkv, D), 220 + n)
+        qpos = rng.choice(np.arange(3, 40), Sq, replace=False)
+        kpos = rng.choice(np.arange(0, 40), Sk, replace=False)
+        kpos[0] = 0
+        qpos[0] = 1                       # sees key 0 only if kpos holds 0 or 1
+        qpos[-1] = -1                     # sees no key
+        for causal in (True, False):
+            o, l = attn_at(q, k, v, qpos, kpos, causal=causal)
+            ob, lb = brute_force(q, k, v, causal, 0, 0, qpos=qpos, kpos=kpos)
+            np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+            assert np.array_equal(np.isinf(l), np.isinf(lb))
+            np.testing.assert_allclose(np.where(np.isinf(lb), 0, l), np.where(np.isinf(lb), 0, lb),
+                                       rtol=0, atol=1e-12)
+        o, l = attn_at(q, k, v, np.arange(Sq) + 4, np.arange(Sk) + 2)
+        o2, l2 = attn(q, k, v, causal=True, q_offset=4, k_offset=2)
+        np.testing.assert_allclose(o, o2, atol=1e-14)
+        np.testing.assert_allclose(l, l2, atol=1e-14)
+
+
+def pin_striped(ring_striped, layout_index, striped, attn, cases=((4, 32), (8, 64), (3, 21), (2, 2))):
+    """Striped split: every position owned once, rank r holding r, r+P, ...;
+    the ring reproduces the single pass on every rank; the causal work of
+    rank r is sum over its rows of (position + 1) visible keys, i.e.
+    C*(r+1) + P*C*(C-1)/2, so ranks differ by C pairs at most."""
+    for P, S in cases:
+        C = S // P
+        allpos = np.concatenate([layout_index(striped, S, P, r) for r in range(P)])
+        assert sorted(allpos.tolist()) == list(range(S))
+        for r in range(P):
+            assert layout_index(striped, S, P, r).tolist() == [r + j * P for j in range(C)]
+        q, k, v = (rand((S, 4, 8), 40 + P + i) for i in range(3))
+        for causal in (True, False):
+            ref_o, ref_l = attn(q, k, v, causal=causal)
+            outs, lses, pairs = ring_striped(q, k, v, P, causal=causal)
+            for r in range(P):
+                idx = layout_index(striped, S, P, r)
+                np.testing.assert_allclose(outs[r], ref_o[idx], rtol=0, atol=1e-12)
+                np.testing.assert_allclose(lses[r], ref_l[:, idx], rtol=0, atol=1e-12)
+                want = C * (r + 1) + P * C * (C - 1) // 2 if causal else C * S
+                assert pairs[r] == want
+            if causal:
+                assert sum(pairs) == S * (S + 1) // 2
 
 
 # ----------------------------------------------------------- closed forms
@@ -247,6 +300,26 @@ def pin_bwd_finite_differences(attn, attn_bwd):
             np.testing.assert_allclose(g, w, atol=1e-7)
 
 
+def pin_bwd_at_finite_differences(attn_at, attn_bwd_at):
+    """Explicit-position backward against central differences of the
+    explicit-position forward, on scattered positions with a row that sees
+    no key."""
+    Sq, Sk, Hq, Hkv, D = 5, 6, 2, 1, 3
+    q, k, v = rand((Sq, Hq, D), 301), rand((Sk, Hkv, D), 302), rand((Sk, Hkv, D), 303)
+    dout = rand((Sq, Hq, D), 304)
+    qpos = np.array([7, 2, 11, -3, 5])
+    kpos = np.array([4, 0, 9, 12, 1, 6])
+    for causal in (True, False):
+        out, lse = attn_at(q, k, v, qpos, kpos, causal=causal)
+        got = attn_bwd_at(q, k, v, dout, out, lse, qpos, kpos, causal=causal)
+
+        def fwd(q_, k_, v_, causal, q_offset, k_offset):
+            return attn_at(q_, k_, v_, qpos, kpos, causal=causal)
+        want = _loss_grad_fd(fwd, q, k, v, dout, causal, 0, 0)
+        for g, w in zip(got, want):
+            np.testing.assert_allclose(g, w, atol=1e-7)
+
+
 def pin_bwd_autograd(attn, attn_bwd):
     """Offsets 0: torch autograd through scaled_dot_product_attention in
     float64 on the CPU (a library special case of the same gradient)."""
@@ -291,7 +364,7 @@ def pin_bwd_closed_forms(attn, attn_bwd):
         np.testing.assert_allclose(dv[:, g, :].sum(axis=0), want, atol=1e-12)
 
 
-def pin_bwd_ring(ring_bwd, attn, attn_bwd, contiguous, zigzag):
+def pin_bwd_ring(ring_bwd, attn, attn_bwd, contiguous, zigzag, striped=None):
     """The ring's block gradients, each taken with the rows' final (out,
     lse), add up to the single-pass gradient (the pages ask that gradients
     with context parallelism match a single card)."""
@@ -299,7 +372,7 @@ def pin_bwd_ring(ring_bwd, attn, attn_bwd, contiguous, zigzag):
     dout = rand(q.shape, 121)
     out, lse = attn(q, k, v, causal=True)
     want = attn_bwd(q, k, v, dout, out, lse, causal=True)
-    for layout in (contiguous, zigzag):
+    for layout in (contiguous, zigzag) + ((striped,) if striped is not None else ()):
         got = ring_bwd(q, k, v, dout, 4, layout, True)
         for g, w in zip(got, want):
             np.testing.assert_allclose(g, w, atol=1e-12)

@@ -103,8 +103,8 @@ BWD_MUTANTS = [
      "dv[:, g, :] = p.T @ dout[:, h, :]"),
     ("P without the lse shift", "np.exp(s - np.where(finite, lse[h], 0.0)[:, None])",
      "np.exp(s)"),
-    ("backward mask ignores offsets", "kpos = np.arange(Sk)[None, :] + k_offset\n    visible = (kpos <= qpos) if causal else np.ones((Sq, Sk), dtype=bool)\n    dq",
-     "kpos = np.arange(Sk)[None, :]\n    visible = (kpos <= qpos) if causal else np.ones((Sq, Sk), dtype=bool)\n    dq"),
+    ("backward mask ignores offsets", "kpos = np.arange(Sk)[None, :] + k_offset\n    visible = (kpos <= qpos) if causal else np.ones((Sq, Sk), dtype=bool)\n    return _bwd_masked",
+     "kpos = np.arange(Sk)[None, :]\n    visible = (kpos <= qpos) if causal else np.ones((Sq, Sk), dtype=bool)\n    return _bwd_masked"),
 ]
 
 
@@ -299,3 +299,71 @@ def test_c_oracle_bwd_mutant_is_caught(name, old, new, tmp_path):
     with pytest.raises(AssertionError):
         for got, w in zip((dq, dk, dv), want):
             np.testing.assert_allclose(got, w, atol=1e-10)
+
+
+def _schedules_over(att):
+    """The real schedules module bound to a (possibly mutated) attention module."""
+    sys.modules["oracle_mutant.attention"] = att
+    src = open(os.path.join(ROOT, "oracle/schedules.py"), encoding="utf-8").read()
+    mod = types.ModuleType("oracle_mutant.schedules")
+    mod.__package__ = "oracle_mutant"
+    exec(compile(src, "schedules_over_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _striped_pins_fail(att, sch):
+    checks = [
+        lambda: pins.pin_attention_at(att.attention_at, att.attention),
+        lambda: pins.pin_bwd_at_finite_differences(att.attention_at, att.attention_bwd_at),
+        lambda: pins.pin_striped(sch.ring_striped, sch.layout_index, sch.STRIPED, att.attention),
+        lambda: pins.pin_bwd_ring(sch.ring_bwd, att.attention, att.attention_bwd, sch.CONTIGUOUS,
+                                  sch.ZIGZAG, sch.STRIPED),
+    ]
+    failed = 0
+    for c in checks:
+        try:
+            c()
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    return failed
+
+
+STRIPED_MUTANTS = [
+    ("explicit-position mask strict", "oracle/attention.py",
+     "visible = (kp <= qp) if causal else np.ones((Sq, Sk), dtype=bool)",
+     "visible = (kp < qp) if causal else np.ones((Sq, Sk), dtype=bool)"),
+    ("explicit-position mask reversed", "oracle/attention.py",
+     "visible = (kp <= qp) if causal else np.ones((Sq, Sk), dtype=bool)",
+     "visible = (qp <= kp) if causal else np.ones((Sq, Sk), dtype=bool)"),
+    ("explicit-position backward mask strict", "oracle/attention.py",
+     "visible = (kp <= qp) if causal else np.ones((qp.shape[0]",
+     "visible = (kp < qp) if causal else np.ones((qp.shape[0]"),
+    ("striped split is contiguous", "oracle/schedules.py",
+     "return np.arange(rank, S, P, dtype=np.int64)",
+     "return np.arange(rank * (S // P), (rank + 1) * (S // P), dtype=np.int64)"),
+    ("striped ring masks keys with the query positions", "oracle/schedules.py",
+     "attention_at(q[qpos], k[kpos], v[kpos], qpos, kpos,",
+     "attention_at(q[qpos], k[kpos], v[kpos], qpos, qpos,"),
+    ("striped ring keys never leave their rank", "oracle/schedules.py",
+     "kpos = layout_index(STRIPED, S, P, src)",
+     "kpos = layout_index(STRIPED, S, P, rank)"),
+    ("striped work counts the diagonal out", "oracle/schedules.py",
+     "n += int(np.sum(kpos[None, :] <= qpos[:, None]))",
+     "n += int(np.sum(kpos[None, :] < qpos[:, None]))"),
+    ("striped ring backward dq to key rows", "oracle/schedules.py",
+     "dq[qi] += gq\n            dk[ki]", "dq[ki] += gq\n            dk[ki]"),
+    ("striped ring backward dk to query rows", "oracle/schedules.py",
+     "dk[ki] += gk", "dk[qi] += gk"),
+]
+
+
+@pytest.mark.parametrize("name,relpath,old,new", STRIPED_MUTANTS, ids=[m[0] for m in STRIPED_MUTANTS])
+def test_striped_mutant_is_caught(name, relpath, old, new):
+    if relpath == "oracle/attention.py":
+        att = _load_mutant(relpath, old, new, "attention")
+        sch = _schedules_over(att)
+    else:
+        sch = _load_mutant(relpath, old, new, "schedules")
+        att = sys.modules["oracle_mutant.attention"]
+    with np.errstate(all="ignore"):
+        assert _striped_pins_fail(att, sch) >= 1, f"no pin catches: {name}"

@@ -215,7 +215,39 @@ def test_bwd_closed_forms():
 
 
 def test_ring_bwd_equals_single_pass():
-    pins.pin_bwd_ring(R.ring_bwd, A.attention, A.attention_bwd, R.CONTIGUOUS, R.ZIGZAG)
+    pins.pin_bwd_ring(R.ring_bwd, A.attention, A.attention_bwd, R.CONTIGUOUS, R.ZIGZAG, R.STRIPED)
+
+
+def test_bwd_at_finite_differences():
+    pins.pin_bwd_at_finite_differences(A.attention_at, A.attention_bwd_at)
+
+
+# ------------------------------------------------------------- striped
+def test_attention_at_brute_force_and_offsets():
+    pins.pin_attention_at(A.attention_at, A.attention)
+
+
+def test_striped_ring_equals_single_pass_and_balances():
+    pins.pin_striped(R.ring_striped, R.layout_index, R.STRIPED, A.attention)
+
+
+@pytest.mark.parametrize("P", [2, 4, 8])
+def test_striped_plan_local_offsets(P):
+    """Every striped pair is computed, and in local coordinates it is the
+    plain causal mask with q_offset 0 and k_offset 1 when the source rank
+    comes after the query rank, 0 otherwise: rank r's row j is position
+    r + jP, so key j' of rank s is visible iff s + j'P <= r + jP."""
+    S = 8 * P
+    plan = R.ring_plan(S, P, R.STRIPED, -1)
+    assert len(plan) == P * P and all(p[8] == R.DIAG for p in plan)
+    assert all(p[8] == R.FULL for p in R.ring_plan(S, P, R.STRIPED, -1, causal=False))
+    q, k, v = (pins.rand((S, 2, 4), 500 + i) for i in range(3))
+    for (r, _t, _qc, src, *_rest) in plan:
+        qi, ki = R.layout_index(R.STRIPED, S, P, r), R.layout_index(R.STRIPED, S, P, src)
+        o, l = A.attention_at(q[qi], k[ki], v[ki], qi, ki)
+        o2, l2 = A.attention(q[qi], k[ki], v[ki], q_offset=0, k_offset=int(src > r))
+        np.testing.assert_allclose(o, o2, atol=1e-14)
+        np.testing.assert_allclose(l, l2, atol=1e-14)
 
 
 def test_c_oracle_bwd_matches_numpy():
