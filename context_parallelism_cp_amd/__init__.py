@@ -21,12 +21,13 @@ LIB_PATH = os.path.join(_HERE, "libcpattn.so")
 
 CP_OK, CP_ERR_NULL, CP_ERR_SHAPE, CP_ERR_UNSUPPORTED, CP_ERR_CAPACITY, CP_ERR_HIP, CP_ERR_ALIGN = range(7)
 CP_F32, CP_BF16 = 0, 1
-CP_LAYOUT_CONTIGUOUS, CP_LAYOUT_ZIGZAG = 0, 1
+CP_LAYOUT_CONTIGUOUS, CP_LAYOUT_ZIGZAG, CP_LAYOUT_STRIPED = 0, 1, 2
 CP_PAIR_SKIP, CP_PAIR_FULL, CP_PAIR_DIAG = 0, 1, 2
 (CP_KERNEL_ATTN_BF16, CP_KERNEL_ATTN_F32, CP_KERNEL_MERGE, CP_KERNEL_PERMUTE, CP_KERNEL_BWD_BF16,
  CP_KERNEL_BWD_F32, CP_KERNEL_BWD_DVEC) = range(7)
 
-LAYOUTS = {"contiguous": CP_LAYOUT_CONTIGUOUS, "zigzag": CP_LAYOUT_ZIGZAG}
+LAYOUTS = {"contiguous": CP_LAYOUT_CONTIGUOUS, "zigzag": CP_LAYOUT_ZIGZAG,
+           "striped": CP_LAYOUT_STRIPED}
 
 
 class CpError(RuntimeError):
@@ -145,8 +146,9 @@ def cp_lse_merge(o1, lse1, o2, lse2, o=None, lse=None, stream=None):
 
 def cp_ring_fwd(q, k, v, P: int, layout="zigzag", rank: int = -1, causal: bool = True,
                 out=None, lse=None, stream=None):
-    """Ring attention over P virtual ranks (rank=-1: all, natural order;
-    rank=r: that rank's share in its local order)."""
+    """Ring attention over P virtual ranks (rank=-1: all, in the inputs'
+    order -- natural, or striped for the striped layout; rank=r: that
+    rank's share in its local order)."""
     import torch
     S, Hq, D = q.shape
     _, Hkv, _ = k.shape
@@ -201,8 +203,8 @@ def cp_attn_block_bwd(q, k, v, dout, lse, dvec, dq=None, dk=None, dv=None, q_off
 def cp_ring_bwd(q, k, v, out, lse, dout, P: int, layout="zigzag", rank: int = -1,
                 causal: bool = True, dq=None, dk=None, dv=None, dvec=None, stream=None):
     """Backward of cp_ring_fwd: dq in the forward's output layout, dk and dv
-    [S][Hkv][D] float32 in natural order (contributions of the rank(s)
-    computed)."""
+    [S][Hkv][D] float32 in the inputs' order -- natural, or striped for the
+    striped layout (contributions of the rank(s) computed)."""
     import torch
     S, Hq, D = q.shape
     _, Hkv, _ = k.shape

@@ -233,18 +233,6 @@ int fill_zero(float *p, int64_t n, hipStream_t stream)
 }
 
 // ------------------------------------------------------------ ring helpers
-struct Split {
-    std::vector<int> chunks;  // chunk ids of one rank, local order
-    int64_t chunk_len;
-};
-
-Split rank_chunks(cp_layout layout, int64_t S, int P, int r)
-{
-    if (layout == CP_LAYOUT_CONTIGUOUS)
-        return {{r}, S / P};
-    return {{r, 2 * P - 1 - r}, S / (2 * P)};
-}
-
 int check_ring_shape(int64_t S, int P, cp_layout layout, int rank)
 {
     if (P < 1)
@@ -253,10 +241,10 @@ int check_ring_shape(int64_t S, int P, cp_layout layout, int rank)
         return fail(CP_ERR_SHAPE, "rank must be -1 or in [0, P) (rank=%d, P=%d)", rank, P);
     if (S < 0)
         return fail(CP_ERR_SHAPE, "negative sequence length");
-    if (layout == CP_LAYOUT_CONTIGUOUS) {
+    if (layout == CP_LAYOUT_CONTIGUOUS || layout == CP_LAYOUT_STRIPED) {
         if (S % P != 0)
-            return fail(CP_ERR_SHAPE, "contiguous layout needs P | S (S=%lld, P=%d)",
-                        (long long)S, P);
+            return fail(CP_ERR_SHAPE, "%s layout needs P | S (S=%lld, P=%d)",
+                        layout == CP_LAYOUT_STRIPED ? "striped" : "contiguous", (long long)S, P);
     } else if (layout == CP_LAYOUT_ZIGZAG) {
         if (S % (2 * (int64_t)P) != 0)
             return fail(CP_ERR_SHAPE, "zigzag layout needs 2P | S (S=%lld, P=%d)",
@@ -274,11 +262,61 @@ int pair_kind(int causal, int qc, int kc)
     return kc == qc ? CP_PAIR_DIAG : CP_PAIR_SKIP;
 }
 
-// First output row of the query chunk `chunk` held in local slot `slot`:
-// natural order when every rank is computed, the rank's local order otherwise.
-int64_t out_row_of(int rank_arg, int slot, int chunk, int64_t chunk_len)
+// Query chunks a rank holds (its local slots).
+int n_slots(cp_layout layout) { return layout == CP_LAYOUT_ZIGZAG ? 2 : 1; }
+
+// One (query chunk, key chunk) pair of a ring step: where its rows sit in the
+// q / k tensors and the positions the causal mask compares.
+struct RingPair {
+    int slot;            // local query slot of the rank
+    int qc, kc;          // chunk ids (striped: the rank ids)
+    int64_t q_row, k_row, len;
+    int64_t q_pos, k_pos;
+    int kind;
+};
+
+// The pairs of rank r at the step where it holds rank src's KV block, in
+// order query slot, then key chunk.
+//  contiguous / zigzag: chunks of C rows at their natural positions, the
+//    tensors in natural order;
+//  striped: rank r's local row j is position r + jP, the tensors are the
+//    ranks' shards back to back; key j of rank src is visible to query i
+//    iff src + jP <= r + iP, i.e. j <= i when src <= r and j <= i - 1 when
+//    src > r -- the plain causal mask with local positions q_pos = 0 and
+//    k_pos = (src > r).
+int ring_step_pairs(cp_layout layout, int64_t S, int P, int r, int src, int causal,
+                    RingPair out[4])
 {
-    return rank_arg < 0 ? (int64_t)chunk * chunk_len : (int64_t)slot * chunk_len;
+    if (layout == CP_LAYOUT_STRIPED) {
+        const int64_t C = S / P;
+        out[0] = RingPair{0, r, src, (int64_t)r * C, (int64_t)src * C, C, 0, src > r ? 1 : 0,
+                          causal ? CP_PAIR_DIAG : CP_PAIR_FULL};
+        return 1;
+    }
+    int n = 0;
+    if (layout == CP_LAYOUT_CONTIGUOUS) {
+        const int64_t C = S / P;
+        out[n++] = RingPair{0, r, src, r * C, src * C, C, r * C, src * C, pair_kind(causal, r, src)};
+        return n;
+    }
+    const int64_t C = S / (2 * P);
+    const int mine[2] = {r, 2 * P - 1 - r};
+    const int theirs[2] = {src, 2 * P - 1 - src};
+    for (int slot = 0; slot < 2; ++slot)
+        for (int kc : theirs) {
+            const int qc = mine[slot];
+            out[n++] = RingPair{slot, qc, kc, qc * C, kc * C, C, qc * C, kc * C,
+                                pair_kind(causal, qc, kc)};
+        }
+    return n;
+}
+
+// First output row of query slot `slot` of a pair: the pair's own rows when
+// every rank is computed (natural order, or the striped shards back to
+// back), the rank's local order otherwise.
+int64_t out_row_of(int rank_arg, const RingPair &p)
+{
+    return rank_arg < 0 ? p.q_row : (int64_t)p.slot * p.len;
 }
 
 }  // namespace
@@ -361,11 +399,19 @@ int cp_layout_index(cp_layout layout, int64_t S, int P, int rank, int32_t *idx)
         return fail(CP_ERR_SHAPE, "cp_layout_index needs a rank in [0, P)");
     if (S >= (int64_t(1) << 31))
         return fail(CP_ERR_SHAPE, "cp_layout_index needs S < 2^31");
-    const Split sp = rank_chunks(layout, S, P, rank);
-    int64_t j = 0;
-    for (int c : sp.chunks)
-        for (int64_t e = 0; e < sp.chunk_len; ++e)
-            idx[j++] = (int32_t)(c * sp.chunk_len + e);
+    const int64_t rows = S / P;
+    for (int64_t j = 0; j < rows; ++j) {
+        int64_t pos;
+        if (layout == CP_LAYOUT_CONTIGUOUS)
+            pos = rank * rows + j;
+        else if (layout == CP_LAYOUT_STRIPED)
+            pos = rank + j * P;
+        else {
+            const int64_t C = rows / 2;
+            pos = j < C ? rank * C + j : (2 * (int64_t)P - 1 - rank) * C + (j - C);
+        }
+        idx[j] = (int32_t)pos;
+    }
     return ok();
 }
 
@@ -377,7 +423,7 @@ int cp_ring_plan(int64_t S, int P, cp_layout layout, int rank, int causal,
     int rc = check_ring_shape(S, P, layout, rank);
     if (rc)
         return rc;
-    const int per_step = layout == CP_LAYOUT_CONTIGUOUS ? 1 : 4;
+    const int per_step = layout == CP_LAYOUT_ZIGZAG ? 4 : 1;
     const int64_t n_ranks = rank < 0 ? P : 1;
     const int64_t need = n_ranks * P * per_step;
     if (need > 0x7fffffff)
@@ -393,27 +439,25 @@ int cp_ring_plan(int64_t S, int P, cp_layout layout, int rank, int causal,
                     (long long)need);
     }
     int n = 0;
-    for (int r = (rank < 0 ? 0 : rank); r < (rank < 0 ? P : rank + 1); ++r) {
-        const Split mine = rank_chunks(layout, S, P, r);
+    for (int r = (rank < 0 ? 0 : rank); r < (rank < 0 ? P : rank + 1); ++r)
         for (int t = 0; t < P; ++t) {
             const int src = ((r - t) % P + P) % P;
-            const Split theirs = rank_chunks(layout, S, P, src);
-            for (int qc : mine.chunks)
-                for (int kc : theirs.chunks) {
-                    cp_block_pair &p = pairs[n++];
-                    p.rank = r;
-                    p.step = t;
-                    p.q_chunk = qc;
-                    p.k_chunk = kc;
-                    p.q_offset = qc * mine.chunk_len;
-                    p.k_offset = kc * mine.chunk_len;
-                    p.len_q = mine.chunk_len;
-                    p.len_k = mine.chunk_len;
-                    p.kind = pair_kind(causal, qc, kc);
-                    p.reserved = 0;
-                }
+            RingPair rp[4];
+            const int m = ring_step_pairs(layout, S, P, r, src, causal, rp);
+            for (int i = 0; i < m; ++i) {
+                cp_block_pair &p = pairs[n++];
+                p.rank = r;
+                p.step = t;
+                p.q_chunk = rp[i].qc;
+                p.k_chunk = rp[i].kc;
+                p.q_offset = rp[i].q_pos;
+                p.k_offset = rp[i].k_pos;
+                p.len_q = rp[i].len;
+                p.len_k = rp[i].len;
+                p.kind = rp[i].kind;
+                p.reserved = 0;
+            }
         }
-    }
     *n_pairs = n;
     return ok();
 }
@@ -469,21 +513,21 @@ int cp_ring_fwd(const void *q, const void *k, const void *v, float *out, float *
         };
         for (int r = r_begin; r < r_end; ++r) {
             const int src = ((r - t) % P + P) % P;
-            const Split mine = rank_chunks(layout, S, P, r);
-            const Split theirs = rank_chunks(layout, S, P, src);
-            for (int slot = 0; slot < (int)mine.chunks.size(); ++slot) {
-                const int qc = mine.chunks[slot];
+            RingPair rp[4];
+            const int m = ring_step_pairs(layout, S, P, r, src, causal, rp);
+            for (int slot = 0; slot < n_slots(layout); ++slot) {
                 QSeg seg{};
-                seg.row0 = (int64_t)qc * mine.chunk_len;
-                seg.pos0 = seg.row0;
-                seg.len = mine.chunk_len;
-                seg.out_row0 = out_row_of(rank, slot, qc, mine.chunk_len);
                 seg.n_kv = 0;
-                for (int kc : theirs.chunks) {
-                    if (pair_kind(causal, qc, kc) == CP_PAIR_SKIP)
+                for (int i = 0; i < m; ++i) {
+                    if (rp[i].slot != slot)
                         continue;
-                    const int64_t k0 = (int64_t)kc * theirs.chunk_len;
-                    seg.kv[seg.n_kv++] = KvSeg{k0, k0, theirs.chunk_len};
+                    seg.row0 = rp[i].q_row;
+                    seg.pos0 = rp[i].q_pos;
+                    seg.len = rp[i].len;
+                    seg.out_row0 = out_row_of(rank, rp[i]);
+                    if (rp[i].kind == CP_PAIR_SKIP)
+                        continue;
+                    seg.kv[seg.n_kv++] = KvSeg{rp[i].k_row, rp[i].k_pos, rp[i].len};
                 }
                 if (seg.n_kv == 0)
                     continue;
@@ -500,9 +544,9 @@ int cp_ring_fwd(const void *q, const void *k, const void *v, float *out, float *
     // Every query chunk sees its own (diagonal) chunk at step 0, so every
     // output row has been written.
     for (int r = r_begin; r < r_end; ++r)
-        for (size_t slot = 0; slot < rank_chunks(layout, S, P, r).chunks.size(); ++slot)
+        for (int slot = 0; slot < n_slots(layout); ++slot)
             if (!started[r][slot])
-                return fail(CP_ERR_HIP, "internal: ring left rank %d chunk %zu unwritten", r, slot);
+                return fail(CP_ERR_HIP, "internal: ring left rank %d slot %d unwritten", r, slot);
     return ok();
 }
 
@@ -607,45 +651,40 @@ int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out, c
     const size_t eb = dtype == CP_BF16 ? 2 : 4;
     const int r_begin = rank < 0 ? 0 : rank;
     const int r_end = rank < 0 ? P : rank + 1;
-    for (int r = r_begin; r < r_end; ++r) {
-        const Split mine = rank_chunks(layout, S, P, r);
+    for (int r = r_begin; r < r_end; ++r)
         for (int t = 0; t < P; ++t) {
             const int src = ((r - t) % P + P) % P;
-            const Split theirs = rank_chunks(layout, S, P, src);
-            for (int slot = 0; slot < (int)mine.chunks.size(); ++slot) {
-                const int qc = mine.chunks[slot];
-                const int64_t C = mine.chunk_len;
-                const int64_t orow = out_row_of(rank, slot, qc, C);
-                for (int kc : theirs.chunks) {
-                    const int kind = pair_kind(causal, qc, kc);
-                    if (kind == CP_PAIR_SKIP)
-                        continue;
-                    BwdLaunch b{};
-                    b.q = (const char *)q + (size_t)qc * C * Hq * D * eb;
-                    b.k = (const char *)k + (size_t)kc * C * Hkv * D * eb;
-                    b.v = (const char *)v + (size_t)kc * C * Hkv * D * eb;
-                    b.dout = (const char *)dout + (size_t)orow * Hq * D * eb;
-                    b.lse = lse + orow;
-                    b.dvec = dvec + orow;
-                    b.stat_ld = rows_out;
-                    b.dq = dq + (size_t)orow * Hq * D;
-                    b.dk = dk + (size_t)kc * C * Hkv * D;
-                    b.dv = dv + (size_t)kc * C * Hkv * D;
-                    b.Sq = C;
-                    b.Sk = C;
-                    b.Hq = Hq;
-                    b.Hkv = Hkv;
-                    b.D = D;
-                    b.causal = kind == CP_PAIR_DIAG ? 1 : 0;
-                    b.accumulate = 1;
-                    b.q_offset = (int64_t)qc * C;
-                    b.k_offset = (int64_t)kc * C;
-                    if ((rc = launch_bwd(b, dtype, st)))
-                        return rc;
-                }
+            RingPair rp[4];
+            const int m = ring_step_pairs(layout, S, P, r, src, causal, rp);
+            for (int i = 0; i < m; ++i) {
+                const RingPair &p = rp[i];
+                if (p.kind == CP_PAIR_SKIP)
+                    continue;
+                const int64_t orow = out_row_of(rank, p);
+                BwdLaunch b{};
+                b.q = (const char *)q + (size_t)p.q_row * Hq * D * eb;
+                b.k = (const char *)k + (size_t)p.k_row * Hkv * D * eb;
+                b.v = (const char *)v + (size_t)p.k_row * Hkv * D * eb;
+                b.dout = (const char *)dout + (size_t)orow * Hq * D * eb;
+                b.lse = lse + orow;
+                b.dvec = dvec + orow;
+                b.stat_ld = rows_out;
+                b.dq = dq + (size_t)orow * Hq * D;
+                b.dk = dk + (size_t)p.k_row * Hkv * D;
+                b.dv = dv + (size_t)p.k_row * Hkv * D;
+                b.Sq = p.len;
+                b.Sk = p.len;
+                b.Hq = Hq;
+                b.Hkv = Hkv;
+                b.D = D;
+                b.causal = p.kind == CP_PAIR_DIAG ? 1 : 0;
+                b.accumulate = 1;
+                b.q_offset = p.q_pos;
+                b.k_offset = p.k_pos;
+                if ((rc = launch_bwd(b, dtype, st)))
+                    return rc;
             }
         }
-    }
     return ok();
 }
 

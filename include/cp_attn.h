@@ -60,11 +60,19 @@ typedef enum {
 typedef enum { CP_F32 = 0, CP_BF16 = 1 } cp_dtype;
 
 /* How the sequence is split over P ranks ([HB], sections "Ring Attention：KV
- * 沿环传一圈" and "之字形切分"):
+ * 沿环传一圈" and "之字形切分"; [SP] section 3.3 for the striped split):
  *   CONTIGUOUS: rank r owns positions [r*S/P, (r+1)*S/P).
  *   ZIGZAG:     the sequence is cut into 2P chunks of C = S/(2P); rank r owns
- *               chunk r then chunk 2P-1-r, in that local order. */
-typedef enum { CP_LAYOUT_CONTIGUOUS = 0, CP_LAYOUT_ZIGZAG = 1 } cp_layout;
+ *               chunk r then chunk 2P-1-r, in that local order.
+ *   STRIPED:    stripes of one token dealt round-robin: rank r owns positions
+ *               r, r+P, r+2P, ... in that local order.  Sequence tensors for
+ *               this layout are given in striped order: the ranks' S/P-row
+ *               shards back to back (row r*S/P + j is position r + j*P). */
+typedef enum {
+    CP_LAYOUT_CONTIGUOUS = 0,
+    CP_LAYOUT_ZIGZAG = 1,
+    CP_LAYOUT_STRIPED = 2
+} cp_layout;
 
 /* Classification of one (query chunk, key chunk) pair of the ring. */
 typedef enum { CP_PAIR_SKIP = 0, CP_PAIR_FULL = 1, CP_PAIR_DIAG = 2 } cp_pair_kind;
@@ -72,7 +80,8 @@ typedef enum { CP_PAIR_SKIP = 0, CP_PAIR_FULL = 1, CP_PAIR_DIAG = 2 } cp_pair_ki
 typedef struct {
     int32_t rank;      /* rank that owns the query chunk                        */
     int32_t step;      /* ring step t; the KV block is rank (rank - t) mod P's  */
-    int32_t q_chunk;   /* chunk ids: P-way split (contiguous), 2P-way (zigzag)  */
+    int32_t q_chunk;   /* chunk ids: P-way split (contiguous), 2P-way (zigzag); */
+                       /* striped: the rank ids of the query and KV shards    */
     int32_t k_chunk;
     int64_t q_offset;  /* absolute first position of the query chunk            */
     int64_t k_offset;  /* absolute first position of the key chunk              */
@@ -126,15 +135,19 @@ int cp_lse_merge(const float *o1, const float *lse1, const float *o2, const floa
  * key chunk) pairs whose keys all come after the queries are skipped
  * (cp_ring_plan lists them).  For the zigzag layout the KV block of a rank is
  * its two chunks; each of the rank's two query chunks attends to those of
- * them it can see.
- * q, k, v are the whole sequence in natural order: q [S][Hq][D], k/v
- * [S][Hkv][D].
- *   rank == -1: every rank; out [S][Hq][D] and lse [Hq][S] in natural order.
+ * them it can see.  For the striped layout ([SP] section 3.3) every step is
+ * computed: rank r's local query i (position r + iP) sees local key j of
+ * rank src (position src + jP) iff j <= i when src <= r and j <= i - 1 when
+ * src > r, which is the causal mask at local offsets 0 and (src > r).
+ * q, k, v are the whole sequence: q [S][Hq][D], k/v [S][Hkv][D], in natural
+ * order (contiguous, zigzag) or striped order (striped).
+ *   rank == -1: every rank; out [S][Hq][D] and lse [Hq][S] in the order of
+ *   the inputs.
  *   0 <= rank < P: that rank's share only; out [S/P][Hq][D] and lse
  *   [Hq][S/P] in the rank's local row order (see cp_layout_index).
  * The merge is fused into the attention epilogue; no workspace is needed.
  * Errors: as cp_attn_block_fwd, plus CP_ERR_SHAPE when P < 1, rank outside
- * [-1, P), S not divisible by P (contiguous) or by 2P (zigzag).
+ * [-1, P), S not divisible by P (contiguous, striped) or by 2P (zigzag).
  */
 int cp_ring_fwd(const void *q, const void *k, const void *v, float *out, float *lse,
                 int64_t S, int Hq, int Hkv, int D, int P, cp_layout layout, int rank,
@@ -191,12 +204,13 @@ int cp_attn_block_bwd(const void *q, const void *k, const void *v, const void *d
  * SKIP) contributes its block gradients; dq accumulates on the query rows,
  * dk and dv on the KV block's rows (on a real ring these accumulators
  * travel with the KV block and return to its owner after P steps).
- * q, k, v: natural order as in cp_ring_fwd.  out, lse, dout and dq use the
- * forward's output layout: rank == -1 natural order ([S][Hq][D], [Hq][S]);
- * 0 <= rank < P that rank's local order ([S/P][Hq][D], [Hq][S/P]).  dout
- * has dtype; out and lse are float32 (cp_ring_fwd's results).  dq is
- * overwritten.  dk and dv are [S][Hkv][D] float32 in natural order and are
- * overwritten with the contributions of the rank(s) computed.  dvec is a
+ * q, k, v: as in cp_ring_fwd (natural order, striped order for the striped
+ * layout).  out, lse, dout and dq use the forward's output layout: rank ==
+ * -1 the inputs' order ([S][Hq][D], [Hq][S]); 0 <= rank < P that rank's
+ * local order ([S/P][Hq][D], [Hq][S/P]).  dout has dtype; out and lse are
+ * float32 (cp_ring_fwd's results).  dq is overwritten.  dk and dv are
+ * [S][Hkv][D] float32 in the inputs' order and are overwritten with the
+ * contributions of the rank(s) computed.  dvec is a
  * caller-provided float32 scratch buffer of Hq * (rows of out) elements.
  * Errors: as cp_ring_fwd and cp_attn_block_bwd.
  */
@@ -233,7 +247,8 @@ int cp_head_to_seq(const void *x, void *y, int64_t S, int H, int D, int P, int r
  * cp_layout_index -- host only, synchronous.  idx[j] (j < S/P) receives the
  * natural sequence position of rank `rank`'s local row j:
  *   contiguous: rank*S/P + j;
- *   zigzag (C = S/(2P)): j < C ? rank*C + j : (2P-1-rank)*C + (j - C).
+ *   zigzag (C = S/(2P)): j < C ? rank*C + j : (2P-1-rank)*C + (j - C);
+ *   striped: rank + j*P.
  * idx is a host array of S/P int32 (so S must be below 2^31).
  * Errors: CP_ERR_NULL, CP_ERR_SHAPE.
  */
@@ -245,7 +260,10 @@ int cp_layout_index(cp_layout layout, int64_t S, int P, int rank, int32_t *idx);
  * in local order, key chunk in local order, each classified SKIP (causal and
  * the key chunk comes after the query chunk), DIAG (causal and the same
  * chunk) or FULL.  rank == -1 lists all ranks.  Contiguous: one pair per
- * step (P-way chunks); zigzag: four pairs per step (2P-way chunks).
+ * step (P-way chunks); zigzag: four pairs per step (2P-way chunks);
+ * striped: one pair per step, DIAG when causal (every shard holds early and
+ * late positions), with the local offsets q_offset = 0 and k_offset =
+ * (k_chunk > q_chunk) that its mask uses.
  * *n_pairs is the capacity of `pairs` on entry and the number of pairs on
  * return; pairs == NULL only queries the count.
  * Errors: CP_ERR_NULL (n_pairs), CP_ERR_SHAPE, CP_ERR_CAPACITY (the needed

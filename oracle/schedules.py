@@ -96,13 +96,15 @@ def ring_plan(S: int, P: int, layout: int, rank: int, causal: bool = True):
     pairs = []
     if layout == STRIPED:
         # every rank's positions interleave with every other's: each pair is
-        # computed, under the causal mask when causal; chunk id = rank id,
-        # offsets are local row offsets (0)
+        # computed, under the causal mask when causal; chunk id = rank id.
+        # Local row i of rank r is position r + i*P and local key j of rank
+        # src is src + j*P, so j is visible to i iff j <= i - (src > r): the
+        # offsets given are these local ones, q 0 and k (src > r).
         C = S // P
         for r in ranks:
             for t in range(P):
                 src = (r - t) % P
-                pairs.append((r, t, r, src, 0, 0, C, C, DIAG if causal else FULL))
+                pairs.append((r, t, r, src, 0, int(src > r), C, C, DIAG if causal else FULL))
         return pairs
     for r in ranks:
         q_chunks, C = _chunks(layout, S, P, r)

@@ -148,6 +148,25 @@ def pin_striped(ring_striped, layout_index, striped, attn, cases=((4, 32), (8, 6
                 assert sum(pairs) == S * (S + 1) // 2
 
 
+def pin_striped_plan(ring_plan, layout_index, striped, diag, full, attn, attn_at):
+    """Every striped pair is computed, and in local coordinates it is the
+    plain causal mask at the plan's offsets, q 0 and k 1 when the source rank
+    comes after the query rank, 0 otherwise: rank r's row j is position
+    r + jP, so key j' of rank s is visible iff s + j'P <= r + jP."""
+    for P in (2, 4, 8):
+        S = 8 * P
+        plan = ring_plan(S, P, striped, -1)
+        assert len(plan) == P * P and all(p[8] == diag for p in plan)
+        assert all(p[8] == full for p in ring_plan(S, P, striped, -1, causal=False))
+        q, k, v = (rand((S, 2, 4), 500 + i) for i in range(3))
+        for (r, _t, _qc, src, qo, ko, *_rest) in plan:
+            qi, ki = layout_index(striped, S, P, r), layout_index(striped, S, P, src)
+            o, l = attn_at(q[qi], k[ki], v[ki], qi, ki)
+            o2, l2 = attn(q[qi], k[ki], v[ki], q_offset=qo, k_offset=ko)
+            np.testing.assert_allclose(o, o2, atol=1e-14)
+            np.testing.assert_allclose(l, l2, atol=1e-14)
+
+
 # ----------------------------------------------------------- closed forms
 def pin_zero_query(attn):
     """q = 0: lse_i = ln n_i, out_i = mean of visible v_j, n_i = number visible."""

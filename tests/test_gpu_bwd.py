@@ -24,7 +24,7 @@ from oracle import attention as OA
 from oracle import schedules as OS
 from seeded_inputs import make_qkv
 
-from test_gpu_parity import DEV, Guarded, announce, dev
+from test_gpu_parity import DEV, Guarded, announce, dev, striped_order
 
 pytestmark = pytest.mark.gpu
 
@@ -128,6 +128,18 @@ def ring_rank_oracle(q, k, v, dout, P, layout, rank):
     dq = np.zeros_like(qn)
     dk = np.zeros_like(kn)
     dv = np.zeros_like(vn)
+    if layout == OS.STRIPED:
+        # true positions (attention_bwd_at); tensors in striped order
+        for (r, _t, _qc, src, *_rest) in OS.ring_plan(S, P, layout, rank):
+            qi, ki = OS.layout_index(OS.STRIPED, S, P, r), OS.layout_index(OS.STRIPED, S, P, src)
+            gq, gk, gv = OA.attention_bwd_at(qn[qi], kn[ki], vn[ki], dn[qi], out[qi], lse[:, qi],
+                                             qi, ki)
+            dq[qi] += gq
+            dk[ki] += gk
+            dv[ki] += gv
+        perm = striped_order(S, P)
+        dq = dq[perm] if rank < 0 else dq[OS.layout_index(layout, S, P, rank)]
+        return dq, dk[perm], dv[perm]
     for (r, _t, _qc, _kc, qo, ko, lq, lk, kind) in OS.ring_plan(S, P, layout, rank):
         if kind == OS.SKIP:
             continue
@@ -172,6 +184,34 @@ def test_f32_ring_bwd_page_inputs(layout):
         np.testing.assert_allclose(a, b, atol=1e-12)
 
 
+def ring_inputs_for(layout, S, P, rank, q, k, v, dout):
+    """Device inputs in the layout's order and the dout rows of the call."""
+    lay = cp.LAYOUTS[layout]
+    order = striped_order(S, P) if lay == OS.STRIPED else np.arange(S)
+    ot = torch.from_numpy(order)
+    qd, kd, vd = dev(q[ot], k[ot], v[ot])
+    rows = order if rank < 0 else OS.layout_index(lay, S, P, rank)
+    dd = dout[torch.from_numpy(np.asarray(rows, dtype=np.int64))].to(DEV).contiguous()
+    return qd, kd, vd, dd
+
+
+def test_f32_striped_ring_bwd_page_inputs():
+    announce("f32 ring bwd P=4 striped on make_qkv()")
+    q, k, v = make_qkv()
+    dout, _, _ = make_qkv(S=32, H=8, D=16, seed=77)
+    for rank in [-1, 0, 1, 2, 3]:
+        qd, kd, vd, dd = ring_inputs_for("striped", 32, 4, rank, q, k, v, dout)
+        out, lse = cp.cp_ring_fwd(qd, kd, vd, 4, "striped", rank)
+        rows = 32 if rank < 0 else 8
+        dq, dk, dv = Guarded(rows, 8, 16), Guarded(32, 8, 16), Guarded(32, 8, 16)
+        cp.cp_ring_bwd(qd, kd, vd, out, lse, dd, 4, "striped", rank, dq=dq.t, dk=dk.t, dv=dv.t)
+        torch.cuda.synchronize()
+        for g in (dq, dk, dv):
+            g.check()
+        want = ring_rank_oracle(q, k, v, dout, 4, OS.STRIPED, rank)
+        grads_compare((dq.t, dk.t, dv.t), want, F32_GRAD_TOL, f"ring striped rank {rank}")
+
+
 # -------------------------------------------------------------------- bf16
 BF16_GRAD_REL = 5e-3     # of the largest reference magnitude of each tensor
 
@@ -201,6 +241,27 @@ def test_bf16_block_bwd_accumulate_and_empty():
     got = run_block_bwd(q, k, v, dout, 0, 1000, True)       # nothing visible
     for g in got:
         assert bool((g == 0).all())
+
+
+def test_bf16_striped_ring_bwd_4k():
+    """Striped ring backward at 4096 tokens over 4 ranks, 8 query heads on 2
+    KV heads: every rank's share and the whole ring."""
+    S, Hq, Hkv, P = 4096, 8, 2, 4
+    announce(f"bf16 ring bwd S={S} Hq={Hq} Hkv={Hkv} P={P} striped")
+    q, k, v = make_qkv(S=S, H=Hq, D=128, seed=23, dtype=torch.bfloat16, Hkv=Hkv)
+    dout, _, _ = make_qkv(S=S, H=Hq, D=128, seed=24, dtype=torch.bfloat16)
+    for rank in [-1, 0, 3]:
+        qd, kd, vd, dd = ring_inputs_for("striped", S, P, rank, q, k, v, dout)
+        out, lse = cp.cp_ring_fwd(qd, kd, vd, P, "striped", rank)
+        rows = S if rank < 0 else S // P
+        dq, dk, dv = Guarded(rows, Hq, 128), Guarded(S, Hkv, 128), Guarded(S, Hkv, 128)
+        cp.cp_ring_bwd(qd, kd, vd, out, lse, dd, P, "striped", rank, dq=dq.t, dk=dk.t, dv=dv.t)
+        torch.cuda.synchronize()
+        for g in (dq, dk, dv):
+            g.check()
+        want = ring_rank_oracle(q, k, v, dout, P, OS.STRIPED, rank)
+        grads_compare((dq.t, dk.t, dv.t), want, BF16_GRAD_REL, f"ring striped rank {rank}",
+                      rel=True)
 
 
 @pytest.mark.parametrize("layout", ["contiguous", "zigzag"])

@@ -134,6 +134,34 @@ def test_f32_ring_page_inputs(layout):
         compare(o2.t, l2.t, ro[idx], rl[:, idx], F32_TOL, F32_TOL, f"{layout} rank {r}")
 
 
+def striped_order(S, P):
+    """Natural positions of the rows of a striped-order tensor: the ranks'
+    shards back to back."""
+    return np.concatenate([OS.layout_index(OS.STRIPED, S, P, r) for r in range(P)])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_f32_striped_ring_page_inputs(causal):
+    announce(f"f32 ring P=4 striped causal={causal} on make_qkv()")
+    q, k, v = make_qkv()
+    ro, rl = OA.attention(q, k, v, causal=causal)
+    perm = striped_order(32, 4)
+    pt = torch.from_numpy(perm)
+    dq, dk, dv = dev(q[pt], k[pt], v[pt])
+    out, lse = Guarded(32, 8, 16), Guarded(8, 32)
+    cp.cp_ring_fwd(dq, dk, dv, 4, "striped", -1, causal=causal, out=out.t, lse=lse.t)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    compare(out.t, lse.t, ro[perm], rl[:, perm], F32_TOL, F32_TOL, "striped all ranks")
+    for r in range(4):
+        o2, l2 = Guarded(8, 8, 16), Guarded(8, 8)
+        cp.cp_ring_fwd(dq, dk, dv, 4, "striped", r, causal=causal, out=o2.t, lse=l2.t)
+        torch.cuda.synchronize()
+        o2.check(), l2.check()
+        idx = OS.layout_index(OS.STRIPED, 32, 4, r)
+        compare(o2.t, l2.t, ro[idx], rl[:, idx], F32_TOL, F32_TOL, f"striped rank {r}")
+
+
 def test_f32_ring_noncausal():
     announce("f32 ring P=3 zigzag non-causal")
     q, k, v = make_qkv(S=48, H=2, D=16, seed=4)
@@ -256,6 +284,28 @@ def test_bf16_ring_small_every_rank(layout):
         compare(o2, l2, ro[idx], rl[:, idx], BF16_OUT_TOL, BF16_LSE_TOL, f"{layout} rank {r}")
 
 
+@pytest.mark.parametrize("S,Hq,Hkv,P", [(2048, 4, 4, 4), (3000, 8, 2, 8), (256, 2, 1, 2)])
+def test_bf16_striped_ring_every_rank(S, Hq, Hkv, P):
+    """Striped order in, striped order out; each rank's share in its local
+    order.  S = 3000 over 8 ranks gives 375-row shards (ragged tiles)."""
+    announce(f"bf16 ring S={S} Hq={Hq} Hkv={Hkv} P={P} striped")
+    q, k, v = make_qkv(S=S, H=Hq, D=128, seed=13, dtype=torch.bfloat16, Hkv=Hkv)
+    ro, rl = oracle_rows(q, k, v, None)
+    perm = striped_order(S, P)
+    pt = torch.from_numpy(perm)
+    dq, dk, dv = dev(q[pt], k[pt], v[pt])
+    out, lse = Guarded(S, Hq, 128), Guarded(Hq, S)
+    cp.cp_ring_fwd(dq, dk, dv, P, "striped", -1, out=out.t, lse=lse.t)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    compare(out.t, lse.t, ro[perm], rl[:, perm], BF16_OUT_TOL, BF16_LSE_TOL, "striped all ranks")
+    for r in range(P):
+        o2, l2 = cp.cp_ring_fwd(dq, dk, dv, P, "striped", r)
+        torch.cuda.synchronize()
+        idx = OS.layout_index(OS.STRIPED, S, P, r)
+        compare(o2, l2, ro[idx], rl[:, idx], BF16_OUT_TOL, BF16_LSE_TOL, f"striped rank {r}")
+
+
 # ------------------------------------------------------- full-size workloads
 @functools.lru_cache(maxsize=1)
 def inputs_cached(S, H, Hkv):
@@ -322,6 +372,23 @@ def test_full_rank_share_128k(rank):
     rows = chunk_edge_rows(S // P, S // (2 * P), 8, seed=5 + rank)
     check_share(out.t, lse.t, q, k, v, OS.layout_index(cp.CP_LAYOUT_ZIGZAG, S, P, rank), rows,
                 f"128K zigzag rank {rank}")
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+def test_full_striped_rank_share_128k(rank):
+    S, H, P = 131072, 32, 8
+    announce(f"bf16 ring S={S} H={H} P={P} striped rank {rank} (sampled rows)")
+    q, k, v = inputs_cached(S, H, H)
+    pt = torch.from_numpy(striped_order(S, P)).to(DEV)
+    dq, dk, dv = (x[pt].contiguous() for x in dev(q, k, v))
+    out, lse = Guarded(S // P, H, 128), Guarded(H, S // P)
+    cp.cp_ring_fwd(dq, dk, dv, P, "striped", rank, out=out.t, lse=lse.t)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    del dq, dk, dv
+    rows = chunk_edge_rows(S // P, S // P, 12, seed=9 + rank)
+    check_share(out.t, lse.t, q, k, v, OS.layout_index(OS.STRIPED, S, P, rank), rows,
+                f"128K striped rank {rank}")
 
 
 def test_full_ulysses_gqa_128k():

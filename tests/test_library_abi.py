@@ -44,7 +44,7 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(cp.cp_block_pair) == 56
 
 
-@pytest.mark.parametrize("layout", [R.CONTIGUOUS, R.ZIGZAG])
+@pytest.mark.parametrize("layout", [R.CONTIGUOUS, R.ZIGZAG, R.STRIPED])
 @pytest.mark.parametrize("S,P", [(32, 4), (64, 8), (48, 3), (16, 1), (131072, 8)])
 def test_layout_index_matches_oracle(layout, S, P):
     for r in range(P):
@@ -53,7 +53,7 @@ def test_layout_index_matches_oracle(layout, S, P):
         assert got.dtype == np.int32 and np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("layout", [R.CONTIGUOUS, R.ZIGZAG])
+@pytest.mark.parametrize("layout", [R.CONTIGUOUS, R.ZIGZAG, R.STRIPED])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("S,P", [(32, 4), (64, 8), (24, 3), (8, 1), (32768, 8)])
 def test_ring_plan_matches_oracle(layout, causal, S, P):
@@ -122,6 +122,9 @@ def test_ring_argument_errors():
     assert rc_ring(rank=-2) == cp.CP_ERR_SHAPE
     assert rc_ring(S=60) == cp.CP_ERR_SHAPE              # 2P does not divide S
     assert rc_ring(S=62, layout=cp.CP_LAYOUT_CONTIGUOUS) == cp.CP_ERR_SHAPE
+    assert rc_ring(S=62, layout=cp.CP_LAYOUT_STRIPED) == cp.CP_ERR_SHAPE
+    assert "striped" in cp.cp_last_error()
+    assert rc_ring(S=0, layout=cp.CP_LAYOUT_STRIPED) == cp.CP_OK
     assert rc_ring(layout=5) == cp.CP_ERR_SHAPE
     assert rc_ring(Hq=6, Hkv=4) == cp.CP_ERR_SHAPE
     assert rc_ring(D=100) == cp.CP_ERR_UNSUPPORTED

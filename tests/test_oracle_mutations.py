@@ -318,6 +318,8 @@ def _striped_pins_fail(att, sch):
         lambda: pins.pin_striped(sch.ring_striped, sch.layout_index, sch.STRIPED, att.attention),
         lambda: pins.pin_bwd_ring(sch.ring_bwd, att.attention, att.attention_bwd, sch.CONTIGUOUS,
                                   sch.ZIGZAG, sch.STRIPED),
+        lambda: pins.pin_striped_plan(sch.ring_plan, sch.layout_index, sch.STRIPED, sch.DIAG,
+                                      sch.FULL, att.attention, att.attention_at),
     ]
     failed = 0
     for c in checks:
@@ -352,6 +354,12 @@ STRIPED_MUTANTS = [
      "n += int(np.sum(kpos[None, :] < qpos[:, None]))"),
     ("striped ring backward dq to key rows", "oracle/schedules.py",
      "dq[qi] += gq\n            dk[ki]", "dq[ki] += gq\n            dk[ki]"),
+    ("striped plan key offset dropped", "oracle/schedules.py",
+     "pairs.append((r, t, r, src, 0, int(src > r), C, C,",
+     "pairs.append((r, t, r, src, 0, 0, C, C,"),
+    ("striped plan key offset reversed", "oracle/schedules.py",
+     "pairs.append((r, t, r, src, 0, int(src > r), C, C,",
+     "pairs.append((r, t, r, src, 0, int(src < r), C, C,"),
     ("striped ring backward dk to query rows", "oracle/schedules.py",
      "dk[ki] += gk", "dk[qi] += gk"),
 ]

@@ -231,23 +231,9 @@ def test_striped_ring_equals_single_pass_and_balances():
     pins.pin_striped(R.ring_striped, R.layout_index, R.STRIPED, A.attention)
 
 
-@pytest.mark.parametrize("P", [2, 4, 8])
-def test_striped_plan_local_offsets(P):
-    """Every striped pair is computed, and in local coordinates it is the
-    plain causal mask with q_offset 0 and k_offset 1 when the source rank
-    comes after the query rank, 0 otherwise: rank r's row j is position
-    r + jP, so key j' of rank s is visible iff s + j'P <= r + jP."""
-    S = 8 * P
-    plan = R.ring_plan(S, P, R.STRIPED, -1)
-    assert len(plan) == P * P and all(p[8] == R.DIAG for p in plan)
-    assert all(p[8] == R.FULL for p in R.ring_plan(S, P, R.STRIPED, -1, causal=False))
-    q, k, v = (pins.rand((S, 2, 4), 500 + i) for i in range(3))
-    for (r, _t, _qc, src, *_rest) in plan:
-        qi, ki = R.layout_index(R.STRIPED, S, P, r), R.layout_index(R.STRIPED, S, P, src)
-        o, l = A.attention_at(q[qi], k[ki], v[ki], qi, ki)
-        o2, l2 = A.attention(q[qi], k[ki], v[ki], q_offset=0, k_offset=int(src > r))
-        np.testing.assert_allclose(o, o2, atol=1e-14)
-        np.testing.assert_allclose(l, l2, atol=1e-14)
+def test_striped_plan_local_offsets():
+    pins.pin_striped_plan(R.ring_plan, R.layout_index, R.STRIPED, R.DIAG, R.FULL, A.attention,
+                          A.attention_at)
 
 
 def test_c_oracle_bwd_matches_numpy():
