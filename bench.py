@@ -19,7 +19,12 @@ with HIP events recorded by the library around every launch on the launch
 stream; its fraction of the bf16 dense MFMA peak is the roofline figure.
 The CPU oracle is timed on a bounded sample of the ring share's rows.
 
+``--layout striped`` (or contiguous) times the ring share with that split
+instead (striped: q, k, v permuted to striped order once, before timing);
+``--part ring|ulysses|bwd`` times one share, or the backward pass.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--part both|ring|ulysses|bwd] [--layout zigzag|striped|contiguous]
 """
 from __future__ import annotations
 
@@ -40,10 +45,17 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "causal block-attn fwd TFLOP/s + % bf16 MFMA peak, S=128K H=32 D=128"
 
 
-def ring_share_flop(S, H, D, P):
-    """Causal-adjusted FLOP of one zigzag rank: 2P chunk units of C x C."""
-    C = S // (2 * P)
-    return 4.0 * D * H * (2 * P) * C * C
+def ring_share_flop(S, H, D, P, layout="zigzag", rank=0):
+    """Causal-adjusted FLOP of one ring rank, a diagonal block counted half:
+    zigzag 2P chunk units of (S/2P)^2; striped P causal blocks of (S/P)^2,
+    each half; contiguous rank r (r + 1/2) units of (S/P)^2."""
+    if layout == "zigzag":
+        C = S // (2 * P)
+        return 4.0 * D * H * (2 * P) * C * C
+    C = S // P
+    if layout == "striped":
+        return 4.0 * D * H * P * C * C / 2.0
+    return 4.0 * D * H * (rank + 0.5) * C * C
 
 
 def ulysses_share_flop(S, H_local, D):
@@ -110,11 +122,12 @@ def cpu_baseline(q, k, v, budget_s=12.0, max_rows=512):
 
 
 def backward(args, cp, torch, q_host, dq, dk, dv, dku, dvu, ql, kl, vl, uly_out_l, uly_lse,
-             ring_out, ring_lse, stream):
+             ring_out, ring_lse, stream, q_seq):
     """The backward pass of the same two shares (one JSON line).
 
-    Ring share: cp_ring_bwd of zigzag rank 0 (its 17 computed pairs, dq in
-    the rank's local order, dk/dv over the whole sequence).  Ulysses share:
+    Ring share: cp_ring_bwd of rank 0 (zigzag: its 17 computed pairs; dq in
+    the rank's local order, dk/dv over the whole sequence; dq, dk, dv here
+    are the ring's inputs, in striped order for the striped layout).  Ulysses share:
     seq->head of dout, cp_attn_bwd_dvec, cp_attn_block_bwd of the 4 local
     query heads against their KV head, head->seq of dq, dk and dv.  The
     forward results (out, lse) are computed once before timing.
@@ -127,12 +140,13 @@ def backward(args, cp, torch, q_host, dq, dk, dv, dku, dvu, ql, kl, vl, uly_out_
     hp, hkp = HQ // P, HKV_ULY // P
     g = make_qkv(S=S, H=HQ, D=D, seed=1, dtype=torch.bfloat16)[0]
     dout_seq = g.to(dev)                              # upstream gradient, natural order
-    idx = torch.from_numpy(cp.cp_layout_index("zigzag", S, P, RING_RANK).astype("int64"))
+    idx = torch.from_numpy(cp.cp_layout_index(args.layout, S, P, args.rank).astype("int64"))
     dout_ring = g[idx].to(dev).contiguous()           # the ring rank's rows, local order
     del g
     # forward results
-    cp.cp_ring_fwd(dq, dk, dv, P, "zigzag", RING_RANK, out=ring_out, lse=ring_lse, stream=stream)
-    cp.cp_seq_to_head(dq, P, ULY_RANK, y=ql, stream=stream)
+    cp.cp_ring_fwd(dq, dk, dv, P, args.layout, args.rank, out=ring_out, lse=ring_lse,
+                   stream=stream)
+    cp.cp_seq_to_head(q_seq, P, ULY_RANK, y=ql, stream=stream)
     cp.cp_seq_to_head(dku, P, ULY_RANK, y=kl, stream=stream)
     cp.cp_seq_to_head(dvu, P, ULY_RANK, y=vl, stream=stream)
     cp.cp_attn_block_fwd(ql, kl, vl, uly_out_l, uly_lse, stream=stream)
@@ -149,7 +163,7 @@ def backward(args, cp, torch, q_host, dq, dk, dv, dku, dvu, ql, kl, vl, uly_out_
     g_v_seq = torch.zeros(S, HKV_ULY, D, **f32)
 
     def step():
-        cp.cp_ring_bwd(dq, dk, dv, ring_out, ring_lse, dout_ring, P, "zigzag", RING_RANK,
+        cp.cp_ring_bwd(dq, dk, dv, ring_out, ring_lse, dout_ring, P, args.layout, args.rank,
                        dq=g_q_ring, dk=g_k_ring, dv=g_v_ring, dvec=dvec_ring, stream=stream)
         cp.cp_seq_to_head(dout_seq, P, ULY_RANK, y=dout_l, stream=stream)
         cp.cp_attn_bwd_dvec(uly_out_l, dout_l, dvec_l, stream=stream)
@@ -173,7 +187,8 @@ def backward(args, cp, torch, q_host, dq, dk, dv, dku, dvu, ql, kl, vl, uly_out_
     dvec_ms, _ = cp.cp_timing_read(cp.CP_KERNEL_BWD_DVEC)
     perm_ms, _ = cp.cp_timing_read(cp.CP_KERNEL_PERMUTE)
     cp.cp_timing_enable(False)
-    flop_step = 2.5 * (ring_share_flop(S, HQ, D, P) + ulysses_share_flop(S, hp, D))
+    flop_step = 2.5 * (ring_share_flop(S, HQ, D, P, args.layout, args.rank)
+                       + ulysses_share_flop(S, hp, D))
     kern_tflops = flop_step * args.steps / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else None
     result = {
         "metric": "causal block-attn bwd TFLOP/s + % bf16 MFMA peak, S=128K H=32 D=128",
@@ -190,10 +205,12 @@ def backward(args, cp, torch, q_host, dq, dk, dv, dku, dvu, ql, kl, vl, uly_out_
         "data": "synthetic",
         "config": {
             "workload": ("backward pass of one rank's share of a 128K-token causal attention "
-                         "layer: zigzag ring rank 0 (S=131072, Hq=Hkv=32, D=128, P=8) plus "
-                         "the Ulysses GQA rank (4 q heads on 1 KV head over 131072 tokens); "
-                         "bf16 q, k, v, dout; fp32 gradients"),
+                         f"layer: {args.layout} ring rank {args.rank} (S=131072, Hq=Hkv=32, "
+                         "D=128, P=8) plus the Ulysses GQA rank (4 q heads on 1 KV head over "
+                         "131072 tokens); bf16 q, k, v, dout; fp32 gradients"),
             "parts": "bwd",
+            "ring_layout": args.layout,
+            "ring_rank": args.rank,
             "flop_per_step": flop_step,
             "flop_convention": "2.5 x (4*D*Hq per visible (q,k) pair, diagonal chunk half)",
         },
@@ -225,6 +242,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--part", choices=["both", "ring", "ulysses", "bwd"], default="both",
                     help="bwd: time the backward pass of both shares instead")
+    ap.add_argument("--layout", choices=["zigzag", "striped", "contiguous"], default="zigzag",
+                    help="split of the ring share (striped: inputs permuted to striped order "
+                         "once, before timing)")
+    ap.add_argument("--rank", type=int, default=RING_RANK, choices=range(P),
+                    help="the virtual ring rank whose share is timed")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="before warm-up, copy 1 GiB device to device once (a plain copy "
                          "kernel of known size that scales HBM byte counters)")
@@ -248,6 +270,15 @@ def main():
     dku, dvu = ku.to(dev), vu.to(dev)
     print(f"# inputs generated and resident in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr)
 
+    if args.layout == "striped":
+        # a striped rank holds its shard in striped order: permute once
+        order = torch.cat([torch.from_numpy(cp.cp_layout_index("striped", S, P, r).astype("int64"))
+                           for r in range(P)]).to(dev)
+        rq, rk, rv = dq[order].contiguous(), dk[order].contiguous(), dv[order].contiguous()
+        del order
+    else:
+        rq, rk, rv = dq, dk, dv
+
     rows = S // P
     ring_out = torch.empty(rows, HQ, D, device=dev, dtype=torch.float32)
     ring_lse = torch.empty(HQ, rows, device=dev, dtype=torch.float32)
@@ -262,7 +293,7 @@ def main():
 
     def step():
         if args.part in ("both", "ring"):
-            cp.cp_ring_fwd(dq, dk, dv, P, "zigzag", RING_RANK, out=ring_out, lse=ring_lse,
+            cp.cp_ring_fwd(rq, rk, rv, P, args.layout, args.rank, out=ring_out, lse=ring_lse,
                            stream=stream)
         if args.part in ("both", "ulysses"):
             cp.cp_seq_to_head(dq, P, ULY_RANK, y=ql, stream=stream)
@@ -280,8 +311,8 @@ def main():
         del src, dst
 
     if args.part == "bwd":
-        backward(args, cp, torch, q, dq, dk, dv, dku, dvu, ql, kl, vl, uly_out_l, uly_lse,
-                 ring_out, ring_lse, stream)
+        backward(args, cp, torch, q, rq, rk, rv, dku, dvu, ql, kl, vl, uly_out_l, uly_lse,
+                 ring_out, ring_lse, stream, dq)
         return
 
     for _ in range(args.warmup):
@@ -300,7 +331,8 @@ def main():
     perm_ms, perm_n = cp.cp_timing_read(cp.CP_KERNEL_PERMUTE)
     cp.cp_timing_enable(False)
 
-    flop_ring = ring_share_flop(S, HQ, D, P) if args.part in ("both", "ring") else 0.0
+    flop_ring = (ring_share_flop(S, HQ, D, P, args.layout, args.rank)
+                 if args.part in ("both", "ring") else 0.0)
     flop_uly = ulysses_share_flop(S, hp, D) if args.part in ("both", "ulysses") else 0.0
     flop_step = flop_ring + flop_uly
     ms_step = elapsed * 1e3 / args.steps
@@ -328,8 +360,13 @@ def main():
             "workload": ("one rank's share of a 128K-token causal attention layer: zigzag ring "
                          "rank (S=131072, Hq=Hkv=32, D=128, P=8, 16 chunks of 8192) plus "
                          "Ulysses GQA rank (Hq=32, Hkv=8, P=8 -> 4 q heads on 1 KV head over "
-                         "all 131072 tokens); bf16 inputs, fp32 out + lse"),
+                         "all 131072 tokens); bf16 inputs, fp32 out + lse"
+                         if (args.layout, args.rank) == ("zigzag", RING_RANK) else
+                         f"as the default workload with ring rank {args.rank} of the "
+                         f"{args.layout} split"),
             "parts": args.part,
+            "ring_layout": args.layout,
+            "ring_rank": args.rank,
             "S": S, "Hq": HQ, "Hkv_ring": HQ, "Hkv_ulysses": HKV_ULY, "D": D, "P": P,
             "flop_per_step": flop_step,
             "flop_convention": "4*D*Hq per visible (q,k) pair, diagonal chunk counted half",
