@@ -298,3 +298,65 @@ def ulysses_attention(q, k, v, P: int, causal: bool = True):
     vl = seq_to_head([v[s] for s in rows], P)
     out_heads = [attention(ql[p], kl[p], vl[p], causal=causal)[0] for p in range(P)]
     return head_to_seq(out_heads, P), [x.shape for x in ql]
+
+
+# ------------------------------------------------------------ USP hybrid
+def usp_rank(rank: int, P_u: int) -> tuple[int, int]:
+    """(Ulysses index u, ring group r) of a rank: the P_u ranks of one ring
+    group are consecutive (Ulysses inside a node, Ring across nodes)."""
+    return rank % P_u, rank // P_u
+
+
+def usp_attention(q, k, v, P_u: int, P_r: int, layout: int = ZIGZAG, causal: bool = True):
+    """The hybrid the handbook names in its comparison table and its GQA
+    exercise (Ulysses inside a node, Ring Attention across nodes; 32 query
+    heads on 8 KV heads over 16 ranks = 8-way Ulysses x 2-way ring).
+
+    Reading: P = P_u * P_r ranks, rank = r * P_u + u.  The sequence is split
+    over the P_r ring groups with ``layout``; inside group r its rows (in the
+    group's local order) are cut into P_u consecutive shards, shard u on rank
+    (u, r).  Then, as the pages' steps:
+      1. seq_to_head inside every group (P_u-way all-to-all): rank (u, r)
+         holds all of group r's rows for query heads u*Hq/P_u ... and KV
+         heads u*Hkv/P_u ...;
+      2. for every head share u, the ring over the P_r groups (the ring loop
+         of ``layout``) on those heads;
+      3. head_to_seq inside every group.
+    Returns (outs, lses, positions): per rank its out [S/P, Hq, D], lse
+    [Hq, S/P] and the natural positions of its rows.
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) if not hasattr(x, "detach")
+               else x.detach().double().numpy() for x in (q, k, v))
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if Hkv % P_u or Hq % Hkv or S % (P_u * P_r * (2 if layout == ZIGZAG else 1)):
+        # the exercise: every Ulysses rank needs at least one whole KV head
+        raise ValueError("USP needs P_u | Hkv, Hkv | Hq and the split to divide S")
+    Sg = S // P_r
+    Sl = Sg // P_u
+    ring = {CONTIGUOUS: ring_contiguous, ZIGZAG: ring_zigzag, STRIPED: ring_striped}[layout]
+    group_rows = [layout_index(layout, S, P_r, r) for r in range(P_r)]
+    # 1. all-to-all inside each group, then the head shares reassembled over
+    #    the whole sequence (what the P_r ranks with index u hold together)
+    heads = {}
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        full = [np.zeros((S, x.shape[1] // P_u, D)) for _ in range(P_u)]
+        for r in range(P_r):
+            shards = [x[group_rows[r][u * Sl:(u + 1) * Sl]] for u in range(P_u)]
+            for u, y in enumerate(seq_to_head(shards, P_u)):
+                full[u][group_rows[r]] = y
+        heads[name] = full
+    # 2. ring over the groups on each head share
+    ring_out = [ring(heads["q"][u], heads["k"][u], heads["v"][u], P_r, causal=causal)[:2]
+                for u in range(P_u)]
+    # 3. all-to-all back inside each group; lse [Hp, Sg] follows the same
+    #    route as a [Sg, Hp, 1] tensor
+    outs, lses, positions = [None] * (P_u * P_r), [None] * (P_u * P_r), [None] * (P_u * P_r)
+    for r in range(P_r):
+        o = head_to_seq([ring_out[u][0][r] for u in range(P_u)], P_u)
+        l = head_to_seq([ring_out[u][1][r].T[:, :, None] for u in range(P_u)], P_u)
+        for u in range(P_u):
+            outs[r * P_u + u] = o[u]
+            lses[r * P_u + u] = l[u][:, :, 0].T
+            positions[r * P_u + u] = group_rows[r][u * Sl:(u + 1) * Sl]
+    return outs, lses, positions

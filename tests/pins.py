@@ -395,3 +395,46 @@ def pin_bwd_ring(ring_bwd, attn, attn_bwd, contiguous, zigzag, striped=None):
         got = ring_bwd(q, k, v, dout, 4, layout, True)
         for g, w in zip(got, want):
             np.testing.assert_allclose(g, w, atol=1e-12)
+
+
+# ------------------------------------------------------------ USP hybrid
+def pin_usp(usp, ring_fns, ulysses, layout_ids, attn):
+    """USP (Ulysses inside groups, ring across them): every rank's rows equal
+    the single pass for every layout, including the handbook's GQA exercise
+    (32 query heads on 8 KV heads, 16 ranks = 8-way Ulysses x 2-way ring,
+    one KV head per rank, where Ulysses alone stops at 8); every position is
+    owned once; P_u = 1 is the plain ring and P_r = 1 plain Ulysses."""
+    cases = [(64, 8, 4, 2, 2), (64, 8, 4, 4, 2), (64, 8, 2, 2, 4), (32, 32, 8, 8, 2)]
+    for n, (S, Hq, Hkv, P_u, P_r) in enumerate(cases):
+        D = 4 if Hq > 8 else 8
+        q, k, v = rand((S, Hq, D), 600 + n), rand((S, Hkv, D), 610 + n), rand((S, Hkv, D), 620 + n)
+        for causal in (True, False):
+            ro, rl = attn(q, k, v, causal=causal)
+            for layout in layout_ids:
+                outs, lses, pos = usp(q, k, v, P_u, P_r, layout, causal=causal)
+                assert len(outs) == P_u * P_r
+                assert sorted(np.concatenate(pos).tolist()) == list(range(S))
+                for o, l, p in zip(outs, lses, pos):
+                    assert o.shape == (S // (P_u * P_r), Hq, D)
+                    np.testing.assert_allclose(o, ro[p], rtol=0, atol=1e-12)
+                    np.testing.assert_allclose(l, rl[:, p], rtol=0, atol=1e-12)
+    # reductions
+    q, k, v = rand((32, 4, 8), 630), rand((32, 2, 8), 631), rand((32, 2, 8), 632)
+    for layout, ring in zip(layout_ids, ring_fns):
+        outs, lses, _ = usp(q, k, v, 1, 4, layout)
+        r_outs, r_lses = ring(q, k, v, 4)[:2]
+        for a, b in zip(outs, r_outs):
+            np.testing.assert_allclose(a, b, atol=1e-14)
+        for a, b in zip(lses, r_lses):
+            np.testing.assert_allclose(a, b, atol=1e-14)
+    outs, _, pos = usp(q, k, v, 2, 1, layout_ids[0])
+    u_outs, _ = ulysses(q, k, v, 2)
+    for a, b in zip(outs, u_outs):
+        np.testing.assert_allclose(a, b, atol=1e-14)
+    # the GQA limit: more Ulysses ranks than KV heads is refused
+    try:
+        usp(q, k, v, 4, 1, layout_ids[0])
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("P_u > Hkv accepted")

@@ -375,3 +375,36 @@ def test_striped_mutant_is_caught(name, relpath, old, new):
         att = sys.modules["oracle_mutant.attention"]
     with np.errstate(all="ignore"):
         assert _striped_pins_fail(att, sch) >= 1, f"no pin catches: {name}"
+
+
+USP_MUTANTS = [
+    ("USP shard of the wrong Ulysses rank", "shards = [x[group_rows[r][u * Sl:(u + 1) * Sl]] for u in range(P_u)]",
+     "shards = [x[group_rows[r][(P_u - 1 - u) * Sl:(P_u - u) * Sl]] for u in range(P_u)]"),
+    ("USP head shares scattered to natural rows", "full[u][group_rows[r]] = y",
+     "full[u][r * Sg:(r + 1) * Sg] = y"),
+    ("USP positions of the wrong shard", "positions[r * P_u + u] = group_rows[r][u * Sl:(u + 1) * Sl]",
+     "positions[r * P_u + u] = group_rows[r][:Sl]"),
+    ("USP lse not transposed back", "lses[r * P_u + u] = l[u][:, :, 0].T",
+     "lses[r * P_u + u] = l[u][:, :, 0].T[::-1]"),
+    ("USP rank numbering ring-major", "return rank % P_u, rank // P_u", "return rank // P_u, rank % P_u"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", USP_MUTANTS, ids=[m[0] for m in USP_MUTANTS])
+def test_usp_mutant_is_caught(name, old, new):
+    sch = _load_mutant("oracle/schedules.py", old, new, "schedules")
+    failed = 0
+    for check in (
+        lambda: pins.pin_usp(sch.usp_attention, (sch.ring_contiguous, sch.ring_zigzag,
+                                                 sch.ring_striped),
+                             sch.ulysses_attention, (sch.CONTIGUOUS, sch.ZIGZAG, sch.STRIPED),
+                             sch.attention),
+        lambda: [sch.usp_rank(x, 8) for x in (0, 7, 8, 15)] == [(0, 0), (7, 0), (0, 1), (7, 1)]
+        or (_ for _ in ()).throw(AssertionError("rank numbering")),
+    ):
+        try:
+            with np.errstate(all="ignore"):
+                check()
+        except (AssertionError, ValueError, IndexError, ZeroDivisionError):
+            failed += 1
+    assert failed >= 1, f"no pin catches: {name}"

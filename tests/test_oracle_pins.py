@@ -253,3 +253,14 @@ def test_c_oracle_bwd_matches_numpy():
             np.testing.assert_allclose(dq, want[0][qr], atol=1e-10)
             np.testing.assert_allclose(dk, want[1][kr], atol=1e-10)
             np.testing.assert_allclose(dv, want[2][kr], atol=1e-10)
+
+
+# ------------------------------------------------------------- USP hybrid
+def test_usp_equals_single_pass_and_reduces():
+    pins.pin_usp(R.usp_attention, (R.ring_contiguous, R.ring_zigzag, R.ring_striped),
+                 R.ulysses_attention, (R.CONTIGUOUS, R.ZIGZAG, R.STRIPED), A.attention)
+
+
+def test_usp_rank_numbering():
+    """Ranks of one ring group are consecutive: rank = r * P_u + u."""
+    assert [R.usp_rank(x, 8) for x in (0, 7, 8, 15)] == [(0, 0), (7, 0), (0, 1), (7, 1)]
