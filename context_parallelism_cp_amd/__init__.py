@@ -19,7 +19,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcpattn.so")
 
-CP_OK, CP_ERR_NULL, CP_ERR_SHAPE, CP_ERR_UNSUPPORTED, CP_ERR_CAPACITY, CP_ERR_HIP, CP_ERR_ALIGN = range(7)
+(CP_OK, CP_ERR_NULL, CP_ERR_SHAPE, CP_ERR_UNSUPPORTED, CP_ERR_CAPACITY, CP_ERR_HIP, CP_ERR_ALIGN,
+ CP_ERR_WORKSPACE) = range(8)
 CP_F32, CP_BF16 = 0, 1
 CP_LAYOUT_CONTIGUOUS, CP_LAYOUT_ZIGZAG, CP_LAYOUT_STRIPED = 0, 1, 2
 CP_PAIR_SKIP, CP_PAIR_FULL, CP_PAIR_DIAG = 0, 1, 2
@@ -58,6 +59,9 @@ SIGNATURES = {
                     _I, _P],
     "cp_seq_to_head": [_P, _P, _I64, _I, _I, _I, _I, _SZ, _P],
     "cp_head_to_seq": [_P, _P, _I64, _I, _I, _I, _I, _SZ, _P],
+    "cp_usp_fwd_workspace": [_I64, _I, _I, _I, _I, _I, _I, _I, _I,
+                             ctypes.POINTER(ctypes.c_size_t)],
+    "cp_usp_fwd": [_P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _SZ, _P],
     "cp_layout_index": [_I, _I64, _I, _I, _P],
     "cp_ring_plan": [_I64, _I, _I, _I, _I, _P, ctypes.POINTER(ctypes.c_int)],
     "cp_last_error": [],
@@ -224,6 +228,42 @@ def cp_ring_bwd(q, k, v, out, lse, dout, P: int, layout="zigzag", rank: int = -1
                            dv.data_ptr(), dvec.data_ptr(), S, Hq, Hkv, D, P, lay, rank,
                            int(bool(causal)), _dtype_code(q), _stream(q, stream)))
     return dq, dk, dv
+
+
+def cp_usp_fwd_workspace(S: int, Hq: int, Hkv: int, D: int, P_u: int, P_r: int, layout,
+                         rank: int, dtype) -> int:
+    """Workspace bytes of cp_usp_fwd (dtype: CP_F32 / CP_BF16 or a torch dtype)."""
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    code = dtype if isinstance(dtype, int) else (CP_BF16 if str(dtype) == "torch.bfloat16"
+                                                 else CP_F32)
+    n = ctypes.c_size_t(0)
+    _check(lib.cp_usp_fwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, code, ctypes.byref(n)))
+    return n.value
+
+
+def cp_usp_fwd(q, k, v, P_u: int, P_r: int, layout="zigzag", rank: int = -1,
+               causal: bool = True, out=None, lse=None, workspace=None, stream=None):
+    """USP hybrid on P_u * P_r virtual ranks (rank = r * P_u + u).  rank=-1:
+    out [S,Hq,D], lse [Hq,S] in the inputs' order; rank: ring group r's
+    rows in its local order, head share u written."""
+    import torch
+    S, Hq, D = q.shape
+    _, Hkv, _ = k.shape
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    rows = S if rank < 0 else S // max(P_r, 1)
+    if out is None:
+        out = torch.empty(rows, Hq, D, device=q.device, dtype=torch.float32)
+    if lse is None:
+        lse = torch.empty(Hq, rows, device=q.device, dtype=torch.float32)
+    need = cp_usp_fwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, _dtype_code(q))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _dense(q, k, v, out, lse, workspace)
+    _check(lib.cp_usp_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), S, Hq, Hkv, D, P_u, P_r, lay, rank, int(bool(causal)),
+                          _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                          _stream(q, stream)))
+    return out, lse
 
 
 def cp_seq_to_head(x, P: int, rank: int = -1, y=None, stream=None):

@@ -688,6 +688,31 @@ int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out, c
     return ok();
 }
 
+// One rank's head share, row by row: to_head copies y[t] <- x[t][p*Hp, (p+1)*Hp),
+// otherwise y[t][p*Hp, (p+1)*Hp) <- x[t], for rows t in [0, rows).
+static int head_share_copy(bool to_head, const void *x, void *y, int64_t rows, int H, int D,
+                           int P, int p, size_t elem_bytes, hipStream_t st)
+{
+    if (rows == 0)
+        return CP_OK;
+    const int64_t unit = (int64_t)(H / P) * D * (int64_t)elem_bytes;
+    const int64_t row = (int64_t)H * D * (int64_t)elem_bytes;
+    UnitCopy c{};
+    c.src = x;
+    c.dst = y;
+    c.unit_bytes = unit;
+    c.n_units = rows;  // u = t
+    c.per = rows;
+    if (to_head) {
+        c.src_base = p * unit, c.src_a = 0, c.src_b = row;
+        c.dst_base = 0, c.dst_a = 0, c.dst_b = unit;
+    } else {
+        c.src_base = 0, c.src_a = 0, c.src_b = unit;
+        c.dst_base = p * unit, c.dst_a = 0, c.dst_b = row;
+    }
+    return timed_launch(CP_KERNEL_PERMUTE, st, [&] { return launch_unit_copy(c, st); });
+}
+
 static int repack(bool to_head, const void *x, void *y, int64_t S, int H, int D, int P,
                   int rank, size_t elem_bytes, void *stream)
 {
@@ -718,32 +743,24 @@ static int repack(bool to_head, const void *x, void *y, int64_t S, int H, int D,
         return fail(CP_ERR_ALIGN, "x and y must not overlap");
     if (S == 0)
         return ok();
+    hipStream_t st = (hipStream_t)stream;
+    if (rank >= 0) {
+        const int rc = head_share_copy(to_head, x, y, S, H, D, P, rank, elem_bytes, st);
+        return rc ? rc : ok();
+    }
     UnitCopy c{};
     c.src = x;
     c.dst = y;
     c.unit_bytes = unit;
-    if (rank < 0) {
-        c.n_units = (int64_t)P * S;  // u = p*S + t
-        c.per = S;
-        if (to_head) {  // y[p][t] <- x[t][p*Hp]
-            c.src_base = 0, c.src_a = unit, c.src_b = row;
-            c.dst_base = 0, c.dst_a = S * unit, c.dst_b = unit;
-        } else {        // y[t][p*Hp] <- x[p][t]
-            c.src_base = 0, c.src_a = S * unit, c.src_b = unit;
-            c.dst_base = 0, c.dst_a = unit, c.dst_b = row;
-        }
-    } else {
-        c.n_units = S;  // u = t
-        c.per = S;
-        if (to_head) {  // y[t] <- x[t][rank*Hp]
-            c.src_base = rank * unit, c.src_a = 0, c.src_b = row;
-            c.dst_base = 0, c.dst_a = 0, c.dst_b = unit;
-        } else {        // y[t][rank*Hp] <- x[t]
-            c.src_base = 0, c.src_a = 0, c.src_b = unit;
-            c.dst_base = rank * unit, c.dst_a = 0, c.dst_b = row;
-        }
+    c.n_units = (int64_t)P * S;  // u = p*S + t
+    c.per = S;
+    if (to_head) {  // y[p][t] <- x[t][p*Hp]
+        c.src_base = 0, c.src_a = unit, c.src_b = row;
+        c.dst_base = 0, c.dst_a = S * unit, c.dst_b = unit;
+    } else {        // y[t][p*Hp] <- x[p][t]
+        c.src_base = 0, c.src_a = S * unit, c.src_b = unit;
+        c.dst_base = 0, c.dst_a = unit, c.dst_b = row;
     }
-    hipStream_t st = (hipStream_t)stream;
     int rc = timed_launch(CP_KERNEL_PERMUTE, st, [&] { return launch_unit_copy(c, st); });
     return rc ? rc : ok();
 }
@@ -758,6 +775,134 @@ int cp_head_to_seq(const void *x, void *y, int64_t S, int H, int D, int P, int r
                    size_t elem_bytes, void *stream)
 {
     return repack(false, x, y, S, H, D, P, rank, elem_bytes, stream);
+}
+
+// ------------------------------------------------------------------ USP
+// Sizes of one USP call: the head shares and the workspace carve-up.
+struct UspPlan {
+    int Hp, Hkvp;
+    size_t eb;
+    int64_t rows_out;
+    size_t off_k, off_v, off_out, total;
+};
+
+static int usp_plan(int64_t S, int Hq, int Hkv, int D, int P_u, int P_r, cp_layout layout,
+                    int rank, cp_dtype dtype, UspPlan *pl)
+{
+    if (P_u < 1 || P_r < 1)
+        return fail(CP_ERR_SHAPE, "need P_u >= 1 and P_r >= 1 (P_u=%d, P_r=%d)", P_u, P_r);
+    if ((int64_t)P_u * P_r > (1 << 20))
+        return fail(CP_ERR_SHAPE, "P_u * P_r too large");
+    const int P = P_u * P_r;
+    if (rank < -1 || rank >= P)
+        return fail(CP_ERR_SHAPE, "rank must be -1 or in [0, P_u*P_r) (rank=%d)", rank);
+    int rc = check_ring_shape(S, P_r, layout, rank < 0 ? -1 : rank / P_u);
+    if (rc)
+        return rc;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return fail(CP_ERR_SHAPE, "need Hkv dividing Hq (Hq=%d, Hkv=%d)", Hq, Hkv);
+    if (Hkv % P_u != 0)
+        return fail(CP_ERR_SHAPE,
+                    "every Ulysses rank needs whole KV heads: P_u must divide Hkv (Hkv=%d, P_u=%d)",
+                    Hkv, P_u);
+    if ((S / P_r) % P_u != 0)
+        return fail(CP_ERR_SHAPE, "P_u must divide the S/P_r rows of a ring group (S=%lld)",
+                    (long long)S);
+    if (dtype != CP_BF16 && dtype != CP_F32)
+        return fail(CP_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    pl->Hp = Hq / P_u;
+    pl->Hkvp = Hkv / P_u;
+    pl->eb = dtype == CP_BF16 ? 2 : 4;
+    pl->rows_out = rank < 0 ? S : S / P_r;
+    const size_t qb = up((size_t)S * pl->Hp * D * pl->eb);
+    const size_t kb = up((size_t)S * pl->Hkvp * D * pl->eb);
+    pl->off_k = qb;
+    pl->off_v = qb + kb;
+    pl->off_out = qb + 2 * kb;
+    pl->total = pl->off_out + up((size_t)pl->rows_out * pl->Hp * D * 4);
+    return CP_OK;
+}
+
+int cp_usp_fwd_workspace(int64_t S, int Hq, int Hkv, int D, int P_u, int P_r, cp_layout layout,
+                         int rank, cp_dtype dtype, size_t *bytes)
+{
+    if (!bytes)
+        return fail(CP_ERR_NULL, "bytes must be non-NULL");
+    UspPlan pl{};
+    const int rc = usp_plan(S, Hq, Hkv, D, P_u, P_r, layout, rank, dtype, &pl);
+    if (rc)
+        return rc;
+    *bytes = S == 0 ? 0 : pl.total;
+    return ok();
+}
+
+int cp_usp_fwd(const void *q, const void *k, const void *v, float *out, float *lse, int64_t S,
+               int Hq, int Hkv, int D, int P_u, int P_r, cp_layout layout, int rank, int causal,
+               cp_dtype dtype, void *workspace, size_t workspace_bytes, void *stream)
+{
+    UspPlan pl{};
+    int rc = usp_plan(S, Hq, Hkv, D, P_u, P_r, layout, rank, dtype, &pl);
+    if (rc)
+        return rc;
+    rc = check_attn_common(q, k, v, out, lse, pl.rows_out, S, Hq, Hkv, D, dtype);
+    if (rc)
+        return rc;
+    if (S == 0)
+        return ok();
+    if (!workspace)
+        return fail(CP_ERR_NULL, "workspace must be non-NULL");
+    if (workspace_bytes < pl.total)
+        return fail(CP_ERR_WORKSPACE, "workspace holds %zu bytes, the call needs %zu",
+                    workspace_bytes, pl.total);
+    if (!aligned(workspace, 256))
+        return fail(CP_ERR_ALIGN, "workspace must be 256-byte aligned");
+    {
+        const size_t qb = (size_t)S * Hq * D * pl.eb, kb = (size_t)S * Hkv * D * pl.eb;
+        const size_t ob = (size_t)pl.rows_out * Hq * D * 4, lb = (size_t)pl.rows_out * Hq * 4;
+        if (overlaps(workspace, pl.total, q, qb) || overlaps(workspace, pl.total, k, kb) ||
+            overlaps(workspace, pl.total, v, kb) || overlaps(workspace, pl.total, out, ob) ||
+            overlaps(workspace, pl.total, lse, lb) || overlaps(q, qb, out, ob) ||
+            overlaps(k, kb, out, ob) || overlaps(v, kb, out, ob) || overlaps(out, ob, lse, lb))
+            return fail(CP_ERR_ALIGN, "workspace, inputs and outputs must not overlap");
+    }
+    hipStream_t st = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    void *ws_q = ws, *ws_k = ws + pl.off_k, *ws_v = ws + pl.off_v;
+    float *ws_out = (float *)(ws + pl.off_out);
+    const int r = rank < 0 ? -1 : rank / P_u;
+    const size_t qrow = (size_t)Hq * D * pl.eb, qrow_p = (size_t)pl.Hp * D * pl.eb;
+    for (int u = (rank < 0 ? 0 : rank % P_u); u < (rank < 0 ? P_u : rank % P_u + 1); ++u) {
+        // 1. the all-to-all inside the ring group: query rows of the group(s)
+        //    computed here, head share u
+        if (r < 0) {
+            rc = head_share_copy(true, q, ws_q, S, Hq, D, P_u, u, pl.eb, st);
+        } else {
+            RingPair rp[4];
+            const int m = ring_step_pairs(layout, S, P_r, r, r, causal, rp);
+            for (int i = 0; i < m && !rc; ++i) {
+                if (rp[i].kc != rp[i].qc)   // one pair per query chunk of the group
+                    continue;
+                rc = head_share_copy(true, (const char *)q + rp[i].q_row * qrow,
+                                     (char *)ws_q + rp[i].q_row * qrow_p, rp[i].len, Hq, D, P_u,
+                                     u, pl.eb, st);
+            }
+        }
+        // key and value rows of every group: the group's own by the
+        // all-to-all, the others as the ring delivers them
+        if (rc || (rc = head_share_copy(true, k, ws_k, S, Hkv, D, P_u, u, pl.eb, st)) ||
+            (rc = head_share_copy(true, v, ws_v, S, Hkv, D, P_u, u, pl.eb, st)))
+            return rc;
+        // 2. the ring over the P_r groups on head share u
+        rc = cp_ring_fwd(ws_q, ws_k, ws_v, ws_out, lse + (size_t)u * pl.Hp * pl.rows_out, S,
+                         pl.Hp, pl.Hkvp, D, P_r, layout, r, causal, dtype, stream);
+        if (rc)
+            return rc;
+        // 3. the all-to-all back: head share u of the output rows
+        if ((rc = head_share_copy(false, ws_out, out, pl.rows_out, Hq, D, P_u, u, 4, st)))
+            return rc;
+    }
+    return ok();
 }
 
 int cp_timing_enable(int enable)

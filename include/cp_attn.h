@@ -54,7 +54,8 @@ typedef enum {
     CP_ERR_UNSUPPORTED = 3, /* valid request this build does not implement      */
     CP_ERR_CAPACITY = 4,    /* caller-provided host array too small             */
     CP_ERR_HIP = 5,         /* a HIP runtime call or kernel launch failed       */
-    CP_ERR_ALIGN = 6        /* pointer alignment or aliasing rule broken        */
+    CP_ERR_ALIGN = 6,       /* pointer alignment or aliasing rule broken        */
+    CP_ERR_WORKSPACE = 7    /* caller-provided device workspace too small       */
 } cp_status;
 
 typedef enum { CP_F32 = 0, CP_BF16 = 1 } cp_dtype;
@@ -242,6 +243,47 @@ int cp_seq_to_head(const void *x, void *y, int64_t S, int H, int D, int P, int r
                    size_t elem_bytes, void *stream);
 int cp_head_to_seq(const void *x, void *y, int64_t S, int H, int D, int P, int rank,
                    size_t elem_bytes, void *stream);
+
+/*
+ * cp_usp_fwd -- the hybrid the handbook names in its comparison of the two
+ * schemes and in its GQA exercise (Ulysses inside a node, Ring Attention
+ * across nodes: 32 query heads on 8 KV heads over 16 ranks as 8-way Ulysses
+ * x 2-way ring), played by P = P_u * P_r virtual ranks on one GPU.
+ * Rank numbering: rank = r * P_u + u, the P_u ranks of ring group r are
+ * consecutive.  The sequence is split over the P_r ring groups with
+ * `layout` (as cp_ring_fwd with P = P_r); inside group r its S/P_r rows, in
+ * the group's local order, are cut into P_u consecutive shards.  Per head
+ * share u (query heads [u*Hq/P_u, (u+1)*Hq/P_u), KV heads [u*Hkv/P_u, ...)):
+ *   1. seq_to_head inside each group (the P_u-way all-to-all);
+ *   2. the ring over the P_r groups on that head share (cp_ring_fwd);
+ *   3. head_to_seq inside each group.
+ * q [S][Hq][D], k/v [S][Hkv][D] of dtype, in natural order (striped order
+ * for the striped layout), as cp_ring_fwd.
+ *   rank == -1: every rank; out [S][Hq][D] and lse [Hq][S] in the inputs'
+ *   order (equal to the single pass).
+ *   rank == r*P_u + u: out [S/P_r][Hq][D] and lse [Hq][S/P_r] hold ring
+ *   group r's rows in the group's local order (cp_layout_index with P_r);
+ *   only query heads of share u are written, so the P_u ranks of a group
+ *   together fill them (as cp_head_to_seq with a rank).  On one GPU the
+ *   share's key/value head slices of every group are copied too: the
+ *   group's own by the all-to-all, the others standing for the blocks the
+ *   ring delivers.
+ * workspace: caller-provided device memory, 256-byte aligned, of the size
+ * cp_usp_fwd_workspace returns (head shares of q, k, v for the whole
+ * sequence, and the ring's float32 output); reused across head shares, so
+ * calls on one workspace must be ordered (same stream).
+ * Errors: as cp_ring_fwd (with P_r), plus CP_ERR_SHAPE when P_u < 1, rank
+ * outside [-1, P_u*P_r), P_u not dividing Hkv (every Ulysses rank needs whole
+ * KV heads) or not dividing S/P_r; CP_ERR_NULL / CP_ERR_WORKSPACE /
+ * CP_ERR_ALIGN for a missing, short or misaligned workspace or one that
+ * overlaps the tensors.
+ */
+int cp_usp_fwd_workspace(int64_t S, int Hq, int Hkv, int D, int P_u, int P_r,
+                         cp_layout layout, int rank, cp_dtype dtype, size_t *bytes);
+int cp_usp_fwd(const void *q, const void *k, const void *v, float *out, float *lse,
+               int64_t S, int Hq, int Hkv, int D, int P_u, int P_r, cp_layout layout,
+               int rank, int causal, cp_dtype dtype, void *workspace,
+               size_t workspace_bytes, void *stream);
 
 /*
  * cp_layout_index -- host only, synchronous.  idx[j] (j < S/P) receives the

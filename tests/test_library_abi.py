@@ -236,3 +236,47 @@ def test_ring_bwd_argument_errors():
     assert f(*b, 32, 8, 8, 16, 4, cp.CP_LAYOUT_ZIGZAG, -1, 1, cp.CP_F32, None) == cp.CP_ERR_ALIGN
     assert f(None, None, None, None, None, None, None, None, None, None, 0, 8, 8, 16, 4,
              cp.CP_LAYOUT_ZIGZAG, -1, 1, cp.CP_F32, None) == cp.CP_OK
+
+
+# ------------------------------------------------------------- USP hybrid
+def rc_usp(ws=FAKE * 2 ** 12, ws_bytes=1 << 40, **kw):
+    args = dict(S=4096, Hq=32, Hkv=8, D=128, P_u=8, P_r=2, layout=cp.CP_LAYOUT_ZIGZAG, rank=-1,
+                causal=1, dtype=cp.CP_BF16)
+    args.update(kw)
+    return cp.lib.cp_usp_fwd(FAKE, FAKE * 2 ** 8, FAKE * 2 ** 9, FAKE * 2 ** 10, FAKE * 2 ** 11,
+                             args["S"], args["Hq"], args["Hkv"], args["D"], args["P_u"],
+                             args["P_r"], args["layout"], args["rank"], args["causal"],
+                             args["dtype"], ws, ws_bytes, None)
+
+
+def test_usp_workspace_sizes():
+    """q, k, v head shares over the whole sequence plus the ring's float32
+    output rows, each rounded up to 256 bytes."""
+    S, Hq, Hkv, D, P_u, P_r = 131072, 32, 8, 128, 8, 2
+    up = lambda b: (b + 255) // 256 * 256
+    for rank, rows in ((-1, S), (13, S // P_r)):
+        want = up(S * 4 * D * 2) + 2 * up(S * 1 * D * 2) + up(rows * 4 * D * 4)
+        assert cp.cp_usp_fwd_workspace(S, Hq, Hkv, D, P_u, P_r, "zigzag", rank, cp.CP_BF16) == want
+    assert cp.cp_usp_fwd_workspace(0, Hq, Hkv, D, P_u, P_r, "zigzag", -1, cp.CP_BF16) == 0
+
+
+def test_usp_argument_errors():
+    assert rc_usp(P_u=3) == cp.CP_ERR_SHAPE                 # 3 does not divide Hkv = 8
+    assert "whole KV heads" in cp.cp_last_error()
+    assert rc_usp(P_u=16, P_r=1) == cp.CP_ERR_SHAPE         # more Ulysses ranks than KV heads
+    assert rc_usp(P_u=0) == cp.CP_ERR_SHAPE
+    assert rc_usp(P_r=0) == cp.CP_ERR_SHAPE
+    assert rc_usp(rank=16) == cp.CP_ERR_SHAPE
+    assert rc_usp(rank=-2) == cp.CP_ERR_SHAPE
+    assert rc_usp(S=4092) == cp.CP_ERR_SHAPE                # 2 P_r does not divide S
+    assert rc_usp(S=40, layout=cp.CP_LAYOUT_CONTIGUOUS) == cp.CP_ERR_SHAPE   # 8 !| 40/2
+    assert rc_usp(layout=7) == cp.CP_ERR_SHAPE
+    assert rc_usp(Hq=30) == cp.CP_ERR_SHAPE
+    assert rc_usp(D=64) == cp.CP_ERR_UNSUPPORTED
+    assert rc_usp(dtype=9) == cp.CP_ERR_UNSUPPORTED
+    assert rc_usp(ws=None) == cp.CP_ERR_NULL
+    assert rc_usp(ws_bytes=1024) == cp.CP_ERR_WORKSPACE
+    assert "needs" in cp.cp_last_error()
+    assert rc_usp(ws=FAKE * 2 ** 12 + 16) == cp.CP_ERR_ALIGN
+    assert rc_usp(ws=FAKE * 2 ** 8) == cp.CP_ERR_ALIGN      # overlaps k
+    assert rc_usp(S=0) == cp.CP_OK
