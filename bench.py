@@ -21,10 +21,12 @@ The CPU oracle is timed on a bounded sample of the ring share's rows.
 
 ``--layout striped`` (or contiguous) times the ring share with that split
 instead (striped: q, k, v permuted to striped order once, before timing);
-``--part ring|ulysses|bwd`` times one share, or the backward pass.
+``--part ring|ulysses|bwd|usp`` times one share, the backward pass, or one
+rank of the USP hybrid (8-way Ulysses x 2-way ring).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--part both|ring|ulysses|bwd] [--layout zigzag|striped|contiguous]
+                    [--part both|ring|ulysses|bwd|usp] [--layout zigzag|striped|contiguous]
+                    [--rank r]
 """
 from __future__ import annotations
 
@@ -234,23 +236,117 @@ def backward(args, cp, torch, q_host, dq, dk, dv, dku, dvu, ql, kl, vl, uly_out_
     print(json.dumps(result))
 
 
+def usp(args, cp, torch, dq, dku, dvu, stream):
+    """One rank's share of the USP hybrid (one JSON line): 32 query heads on
+    8 KV heads over 16 ranks as 8-way Ulysses x 2-way ring (the handbook's
+    GQA exercise), S = 131072.  The share: seq->head of its ring group's
+    query rows and of the key/value rows (head share u), the 2-step ring on
+    4 query heads and 1 KV head, head->seq of the output rows.  FLOP: the
+    ring share of the head share (diagonal chunk half), 2^43 per step."""
+    P_u, P_r = 8, 2
+    rank = args.rank
+    u, r = rank % P_u, rank // P_u
+    hp, hkp = HQ // P_u, HKV_ULY // P_u
+    rows = S // P_r
+    dev = "cuda:0"
+    qx, kx, vx = dq, dku, dvu
+    if args.layout == "striped":
+        order = torch.cat([torch.from_numpy(cp.cp_layout_index("striped", S, P_r, g).astype("int64"))
+                           for g in range(P_r)]).to(dev)
+        qx, kx, vx = (x[order].contiguous() for x in (dq, dku, dvu))
+        del order
+    out = torch.empty(rows, HQ, D, device=dev, dtype=torch.float32)
+    lse = torch.empty(HQ, rows, device=dev, dtype=torch.float32)
+    ws = torch.empty(cp.cp_usp_fwd_workspace(S, HQ, HKV_ULY, D, P_u, P_r, args.layout, rank,
+                                             cp.CP_BF16), device=dev, dtype=torch.uint8)
+
+    def step():
+        cp.cp_usp_fwd(qx, kx, vx, P_u, P_r, args.layout, rank, out=out, lse=lse, workspace=ws,
+                      stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    cp.cp_timing_enable(True)
+    cp.cp_timing_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    attn_ms, attn_n = cp.cp_timing_read(cp.CP_KERNEL_ATTN_BF16)
+    perm_ms, perm_n = cp.cp_timing_read(cp.CP_KERNEL_PERMUTE)
+    cp.cp_timing_enable(False)
+    flop_step = ring_share_flop(S, hp, D, P_r, args.layout, r)
+    # each head-share copy reads and writes its bytes once
+    perm_bytes = 2 * (rows * hp * D * 2 + 2 * S * hkp * D * 2 + rows * hp * D * 4)
+    kern = flop_step * args.steps / (attn_ms * 1e-3) / 1e12 if attn_ms > 0 else None
+    result = {
+        "metric": "causal block-attn fwd TFLOP/s + % bf16 MFMA peak, USP 8x2, S=128K H=32/8 D=128",
+        "value": round(flop_step * args.steps / elapsed / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"one rank's share of the USP hybrid: rank {rank} (u={u}, r={r}) of "
+                         f"8-way Ulysses x 2-way {args.layout} ring, S=131072, Hq=32, Hkv=8, "
+                         "D=128; bf16 inputs, fp32 out + lse"),
+            "parts": "usp",
+            "ring_layout": args.layout,
+            "usp_rank": rank,
+            "flop_per_step": flop_step,
+            "flop_convention": "4*D*Hq_share per visible (q,k) pair, diagonal chunk counted half",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_bf16_kernel",
+            "achieved": round(kern, 2) if kern else None,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(kern / PEAK_BF16_TFLOPS, 4) if kern else None,
+            "traffic": None,
+            "launches": attn_n,
+            "avg_launch_ms": round(attn_ms / max(attn_n, 1), 4),
+        },
+        "breakdown": {
+            "attn_ms_per_step": round(attn_ms / args.steps, 3),
+            "repack_ms_per_step": round(perm_ms / args.steps, 3),
+            "repack_launches_per_step": perm_n // max(args.steps, 1),
+            "repack_GBps": round(perm_bytes * args.steps / (perm_ms * 1e-3) / 1e9, 1)
+            if perm_ms > 0 else None,
+        },
+    }
+    print(json.dumps(result))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--part", choices=["both", "ring", "ulysses", "bwd"], default="both",
-                    help="bwd: time the backward pass of both shares instead")
+    ap.add_argument("--part", choices=["both", "ring", "ulysses", "bwd", "usp"], default="both",
+                    help="bwd: time the backward pass of both shares instead; usp: one rank "
+                         "of the 8-way Ulysses x 2-way ring hybrid")
     ap.add_argument("--layout", choices=["zigzag", "striped", "contiguous"], default="zigzag",
                     help="split of the ring share (striped: inputs permuted to striped order "
                          "once, before timing)")
-    ap.add_argument("--rank", type=int, default=RING_RANK, choices=range(P),
-                    help="the virtual ring rank whose share is timed")
+    ap.add_argument("--rank", type=int, default=RING_RANK, choices=range(2 * P),
+                    help="the virtual rank whose share is timed (ring: 0..7, usp: 0..15)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="before warm-up, copy 1 GiB device to device once (a plain copy "
                          "kernel of known size that scales HBM byte counters)")
     args = ap.parse_args()
+    if args.part != "usp" and args.rank >= P:
+        ap.error(f"--rank must be below {P} for the ring share")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the ring and Ulysses ranks are virtual and "
               "played on a single MI355X; run it with --gpus 1.", file=sys.stderr)
@@ -310,6 +406,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.part == "usp":
+        usp(args, cp, torch, dq, dku, dvu, stream)
+        return
     if args.part == "bwd":
         backward(args, cp, torch, q, rq, rk, rv, dku, dvu, ql, kl, vl, uly_out_l, uly_lse,
                  ring_out, ring_lse, stream, dq)
