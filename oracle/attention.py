@@ -193,11 +193,13 @@ def _bwd_masked(q, k, v, dout, out, lse, visible):
     return dq, dk, dv
 
 
-def attention_at(q, k, v, qpos, kpos, causal: bool = True):
+def attention_at(q, k, v, qpos, kpos, causal: bool = True, kvalid=None):
     """``attention`` with explicit absolute positions: key j is visible to
     query i iff kpos[j] <= qpos[i] (the handbook's mask, whose positions are
     q_offset + i and k_offset + j, for any position arrays -- needed when a
     rank's rows are not one contiguous run, as in the striped split).
+    ``kvalid`` (bool per key, optional) removes the keys marked False from
+    every row's visible set (padding keys).
     Returns (out [Sq, Hq, D], lse [Hq, Sq]) like ``attention``.
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
@@ -207,6 +209,8 @@ def attention_at(q, k, v, qpos, kpos, causal: bool = True):
     qp = np.asarray(qpos, dtype=np.int64)[:, None]
     kp = np.asarray(kpos, dtype=np.int64)[None, :]
     visible = (kp <= qp) if causal else np.ones((Sq, Sk), dtype=bool)
+    if kvalid is not None:
+        visible = visible & np.asarray(kvalid, dtype=bool)[None, :]
     out = np.zeros((Sq, Hq, D))
     lse = np.full((Hq, Sq), NEG_INF)
     for h in range(Hq):

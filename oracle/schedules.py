@@ -60,6 +60,14 @@ def work(query_chunks) -> float:
     return sum(q + 0.5 for q in query_chunks)
 
 
+def padded_length(S: int, P: int, layout: int) -> int:
+    """The practitioner blog's padding (section 7.1): when the split does
+    not divide S, the sequence is padded up to the next multiple of P (2P
+    for zigzag, whose chunks are 2P)."""
+    m = 2 * P if layout == ZIGZAG else P
+    return -(-S // m) * m
+
+
 def layout_index(layout: int, S: int, P: int, rank: int) -> np.ndarray:
     """Natural sequence position of each local row of ``rank``.
 
@@ -67,7 +75,10 @@ def layout_index(layout: int, S: int, P: int, rank: int) -> np.ndarray:
     Zigzag: the 2P-chunk split, chunks concatenated in the order listed.
     Striped: positions rank, rank + P, rank + 2P, ... (stripes of one token
     dealt round-robin, the reading stated in ``ring_striped``).
+    When the split does not divide S the layout is that of the padded
+    length (``padded_length``): positions >= S are padding rows.
     """
+    S = padded_length(S, P, layout)
     if layout == CONTIGUOUS:
         C = S // P
         return np.arange(rank * C, (rank + 1) * C, dtype=np.int64)
@@ -94,6 +105,19 @@ def ring_plan(S: int, P: int, layout: int, rank: int, causal: bool = True):
     """
     ranks = range(P) if rank < 0 else [rank]
     pairs = []
+    S_real, S = S, padded_length(S, P, layout)
+    if S != S_real:
+        # padded sequence: each chunk keeps its real rows only; a pair with
+        # no real query or key row is skipped
+        out = []
+        for p in ring_plan(S, P, layout, rank, causal):
+            (r, t, qc, kc, qo, ko, lq, lk, kind) = p
+            if layout == STRIPED:
+                lq, lk = _real_rows(S_real, P, qc, lq), _real_rows(S_real, P, kc, lk)
+            else:
+                lq, lk = min(max(S_real - qo, 0), lq), min(max(S_real - ko, 0), lk)
+            out.append((r, t, qc, kc, qo, ko, lq, lk, SKIP if lq == 0 or lk == 0 else kind))
+        return out
     if layout == STRIPED:
         # every rank's positions interleave with every other's: each pair is
         # computed, under the causal mask when causal; chunk id = rank id.
@@ -121,6 +145,11 @@ def ring_plan(S: int, P: int, layout: int, rank: int, causal: bool = True):
                         kind = SKIP
                     pairs.append((r, t, qc, kc, qc * C, kc * C, C, C, kind))
     return pairs
+
+
+def _real_rows(S: int, P: int, rank: int, C: int) -> int:
+    """Striped: how many of rank's C rows (positions rank + jP) lie below S."""
+    return int(np.sum(rank + P * np.arange(C) < S))
 
 
 # ---------------------------------------------------------------- the ring
@@ -224,6 +253,47 @@ def ring_striped(q, k, v, P: int, causal: bool = True):
     return outs, lses, work_pairs
 
 
+def ring_padded(q, k, v, P: int, layout: int, causal: bool = True):
+    """Ring attention when the split does not divide S (the practitioner
+    blog, section 7.1: pad up to a multiple of the CP degree, compute,
+    discard what the padding produced).
+
+    Reading: zero rows are appended at positions S .. S_pad-1
+    (``padded_length``); the padded sequence is split with ``layout``;
+    every rank runs the handbook's ring loop over all P steps (a block with
+    no visible key contributes (0, -inf), the merge's identity), attending
+    with true positions and with the padding keys removed from every row's
+    visible set; the rows at positions >= S are then discarded.
+
+    Returns (outs, lses, positions): per rank the out [n_r, Hq, D] and lse
+    [Hq, n_r] of its real rows, in local order, and their positions.
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) if not hasattr(x, "detach")
+               else x.detach().double().numpy() for x in (q, k, v))
+    S = q.shape[0]
+    S_pad = padded_length(S, P, layout)
+
+    def pad(x):
+        return np.concatenate([x, np.zeros((S_pad - S,) + x.shape[1:])])
+
+    qp, kp, vp = pad(q), pad(k), pad(v)
+    outs, lses, positions = [], [], []
+    for rank in range(P):
+        qpos = layout_index(layout, S_pad, P, rank)
+        state = None
+        for step in range(P):
+            src = (rank - step) % P
+            kpos = layout_index(layout, S_pad, P, src)
+            o, l = attention_at(qp[qpos], kp[kpos], vp[kpos], qpos, kpos, causal=causal,
+                                kvalid=kpos < S)
+            state = (o, l) if state is None else lse_merge(*state, o, l)
+        real = qpos < S
+        outs.append(state[0][real])
+        lses.append(state[1][:, real])
+        positions.append(qpos[real])
+    return outs, lses, positions
+
+
 def ring_bwd(q, k, v, dout, P: int, layout: int, causal: bool = True):
     """Backward pass through the ring (no algorithm on the pages; the
     plainest reading of running the forward ring backwards).
@@ -247,6 +317,7 @@ def ring_bwd(q, k, v, dout, P: int, layout: int, causal: bool = True):
             continue
         if layout == STRIPED:
             qi, ki = layout_index(STRIPED, S, P, r), layout_index(STRIPED, S, P, src)
+            qi, ki = qi[qi < S], ki[ki < S]
             gq, gk, gv = attention_bwd_at(q[qi], k[ki], v[ki], dout[qi], out[qi], lse[:, qi],
                                           qi, ki, causal=causal)
             dq[qi] += gq

@@ -51,9 +51,10 @@ def rand(shape, seed):
 
 
 # ----------------------------------------------------------- brute force
-def brute_force(q, k, v, causal, q_offset, k_offset, qpos=None, kpos=None):
+def brute_force(q, k, v, causal, q_offset, k_offset, qpos=None, kpos=None, kvalid=None):
     """Pure-Python loops: p_j = exp(s_j) / sum_j exp(s_j) over visible j.
-    Positions are q_offset + i and k_offset + j unless given explicitly."""
+    Positions are q_offset + i and k_offset + j unless given explicitly;
+    keys with kvalid[j] False are never visible."""
     Sq, Hq, D = q.shape
     Sk, Hkv, _ = k.shape
     group = Hq // Hkv
@@ -66,7 +67,7 @@ def brute_force(q, k, v, causal, q_offset, k_offset, qpos=None, kpos=None):
             for j in range(Sk):
                 pq = q_offset + i if qpos is None else int(qpos[i])
                 pk = k_offset + j if kpos is None else int(kpos[j])
-                if causal and pk > pq:
+                if (causal and pk > pq) or (kvalid is not None and not kvalid[j]):
                     continue
                 s = sum(float(q[i, h, d]) * float(k[j, g, d]) for d in range(D)) / math.sqrt(D)
                 e.append((j, math.exp(s)))
@@ -117,6 +118,12 @@ def pin_attention_at(attn_at, attn):
             assert np.array_equal(np.isinf(l), np.isinf(lb))
             np.testing.assert_allclose(np.where(np.isinf(lb), 0, l), np.where(np.isinf(lb), 0, lb),
                                        rtol=0, atol=1e-12)
+        kvalid = np.arange(Sk) % 3 != 1
+        for causal in (True, False):
+            o, l = attn_at(q, k, v, qpos, kpos, causal=causal, kvalid=kvalid)
+            ob, lb = brute_force(q, k, v, causal, 0, 0, qpos=qpos, kpos=kpos, kvalid=kvalid)
+            np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+            assert np.array_equal(np.isinf(l), np.isinf(lb))
         o, l = attn_at(q, k, v, np.arange(Sq) + 4, np.arange(Sk) + 2)
         o2, l2 = attn(q, k, v, causal=True, q_offset=4, k_offset=2)
         np.testing.assert_allclose(o, o2, atol=1e-14)
@@ -391,10 +398,20 @@ def pin_bwd_ring(ring_bwd, attn, attn_bwd, contiguous, zigzag, striped=None):
     dout = rand(q.shape, 121)
     out, lse = attn(q, k, v, causal=True)
     want = attn_bwd(q, k, v, dout, out, lse, causal=True)
-    for layout in (contiguous, zigzag) + ((striped,) if striped is not None else ()):
+    layouts = (contiguous, zigzag) + ((striped,) if striped is not None else ())
+    for layout in layouts:
         got = ring_bwd(q, k, v, dout, 4, layout, True)
         for g, w in zip(got, want):
             np.testing.assert_allclose(g, w, atol=1e-12)
+    # a length no split divides (padding): 30 rows over 4 ranks
+    q, k, v, dout = q[:30], k[:30], v[:30], dout[:30]
+    for causal in (True, False):
+        out, lse = attn(q, k, v, causal=causal)
+        want = attn_bwd(q, k, v, dout, out, lse, causal=causal)
+        for layout in layouts:
+            got = ring_bwd(q, k, v, dout, 4, layout, causal)
+            for g, w in zip(got, want):
+                np.testing.assert_allclose(g, w, atol=1e-12)
 
 
 # ------------------------------------------------------------ USP hybrid
@@ -438,3 +455,44 @@ def pin_usp(usp, ring_fns, ulysses, layout_ids, attn):
         pass
     else:
         raise AssertionError("P_u > Hkv accepted")
+
+
+# ---------------------------------------------------------------- padding
+def pin_padding(ring_padded, padded_length, layout_index, ring_plan, layouts, zigzag, attn,
+                rings):
+    """Padding (pad to a multiple of the split, compute, discard): the real
+    rows equal the single pass for every layout, causal or not, when the
+    split does not divide S -- including ranks made only of padding -- and
+    every real position is owned once; with no padding it is the plain ring;
+    the padded lengths round up to P (2P for zigzag); the plan's real row
+    counts add up to the real positions of each rank."""
+    assert padded_length(30, 4, layouts[0]) == 32 and padded_length(30, 4, zigzag) == 32
+    assert padded_length(37, 8, zigzag) == 48 and padded_length(37, 8, layouts[0]) == 40
+    assert padded_length(32, 4, zigzag) == 32 and padded_length(0, 4, zigzag) == 0
+    for n, (S, P) in enumerate([(30, 4), (37, 8), (5, 8), (13, 3)]):
+        q, k, v = rand((S, 4, 8), 700 + n), rand((S, 2, 8), 710 + n), rand((S, 2, 8), 720 + n)
+        for causal in (True, False):
+            ro, rl = attn(q, k, v, causal=causal)
+            for layout in layouts:
+                outs, lses, pos = ring_padded(q, k, v, P, layout, causal)
+                assert sorted(np.concatenate(pos).tolist()) == list(range(S))
+                for r, (o, l, p) in enumerate(zip(outs, lses, pos)):
+                    idx = layout_index(layout, S, P, r)
+                    assert idx.size == padded_length(S, P, layout) // P
+                    assert np.array_equal(p, idx[idx < S])
+                    np.testing.assert_allclose(o, ro[p], rtol=0, atol=1e-12)
+                    np.testing.assert_allclose(l, rl[:, p], rtol=0, atol=1e-12)
+                plan = ring_plan(S, P, layout, -1, causal)
+                for r in range(P):
+                    idx = layout_index(layout, S, P, r)
+                    lens = {}
+                    for (rr, _t, qc, _kc, _qo, _ko, lq, _lk, _kind) in plan:
+                        if rr == r:
+                            lens[qc] = lq
+                    assert sum(lens.values()) == int(np.sum(idx < S))
+    q, k, v = rand((32, 4, 8), 730), rand((32, 2, 8), 731), rand((32, 2, 8), 732)
+    for layout, ring in zip(layouts, rings):
+        outs, lses, _ = ring_padded(q, k, v, 4, layout, True)
+        r_outs, r_lses = ring(q, k, v, 4)[:2]
+        for a, b in zip(outs, r_outs):
+            np.testing.assert_allclose(a, b, atol=1e-13)

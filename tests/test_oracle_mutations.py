@@ -408,3 +408,46 @@ def test_usp_mutant_is_caught(name, old, new):
         except (AssertionError, ValueError, IndexError, ZeroDivisionError):
             failed += 1
     assert failed >= 1, f"no pin catches: {name}"
+
+
+PAD_MUTANTS = [
+    ("padding keys visible", "oracle/attention.py",
+     "visible = visible & np.asarray(kvalid, dtype=bool)[None, :]", "visible = visible"),
+    ("zigzag padded to a multiple of P", "oracle/schedules.py",
+     "m = 2 * P if layout == ZIGZAG else P", "m = P"),
+    ("padded rows kept", "oracle/schedules.py", "real = qpos < S", "real = qpos <= S"),
+    ("plan clips one row short", "oracle/schedules.py",
+     "lq, lk = min(max(S_real - qo, 0), lq), min(max(S_real - ko, 0), lk)",
+     "lq, lk = min(max(S_real - qo - 1, 0), lq), min(max(S_real - ko - 1, 0), lk)"),
+    ("striped real rows off by one", "oracle/schedules.py",
+     "return int(np.sum(rank + P * np.arange(C) < S))",
+     "return int(np.sum(rank + P * np.arange(C) <= S))"),
+    ("striped backward keeps padded rows", "oracle/schedules.py",
+     "qi, ki = qi[qi < S], ki[ki < S]", "qi, ki = qi[qi < S], ki"),
+]
+
+
+@pytest.mark.parametrize("name,relpath,old,new", PAD_MUTANTS, ids=[m[0] for m in PAD_MUTANTS])
+def test_padding_mutant_is_caught(name, relpath, old, new):
+    if relpath == "oracle/attention.py":
+        att = _load_mutant(relpath, old, new, "attention")
+        sch = _schedules_over(att)
+    else:
+        sch = _load_mutant(relpath, old, new, "schedules")
+        att = sys.modules["oracle_mutant.attention"]
+    failed = 0
+    for check in (
+        lambda: pins.pin_padding(sch.ring_padded, sch.padded_length, sch.layout_index,
+                                 sch.ring_plan, (sch.CONTIGUOUS, sch.ZIGZAG, sch.STRIPED),
+                                 sch.ZIGZAG, att.attention,
+                                 (sch.ring_contiguous, sch.ring_zigzag, sch.ring_striped)),
+        lambda: pins.pin_bwd_ring(sch.ring_bwd, att.attention, att.attention_bwd,
+                                  sch.CONTIGUOUS, sch.ZIGZAG, sch.STRIPED),
+        lambda: pins.pin_attention_at(att.attention_at, att.attention),
+    ):
+        try:
+            with np.errstate(all="ignore"):
+                check()
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    assert failed >= 1, f"no pin catches: {name}"

@@ -264,3 +264,10 @@ def test_usp_equals_single_pass_and_reduces():
 def test_usp_rank_numbering():
     """Ranks of one ring group are consecutive: rank = r * P_u + u."""
     assert [R.usp_rank(x, 8) for x in (0, 7, 8, 15)] == [(0, 0), (7, 0), (0, 1), (7, 1)]
+
+
+# ---------------------------------------------------------------- padding
+def test_padding_equals_single_pass():
+    pins.pin_padding(R.ring_padded, R.padded_length, R.layout_index, R.ring_plan,
+                     (R.CONTIGUOUS, R.ZIGZAG, R.STRIPED), R.ZIGZAG, A.attention,
+                     (R.ring_contiguous, R.ring_zigzag, R.ring_striped))
