@@ -148,20 +148,47 @@ def cp_lse_merge(o1, lse1, o2, lse2, o=None, lse=None, stream=None):
     return o, lse
 
 
+def padded_length(S: int, P: int, layout) -> int:
+    """S rounded up to a multiple of the split: P chunks, 2P for zigzag."""
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    m = 2 * P if lay == CP_LAYOUT_ZIGZAG else P
+    return -(-S // max(m, 1)) * m
+
+
+def _ring_rows(S: int, P: int, lay: int, rank: int):
+    """(rows of q/k/v, rows of out/lse/dq) of a ring call of real length S."""
+    Sp = padded_length(S, P, lay)
+    rows_in = Sp if lay == CP_LAYOUT_STRIPED else S
+    return rows_in, (rows_in if rank < 0 else Sp // max(P, 1))
+
+
+def _need(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise CpError(CP_ERR_SHAPE, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def cp_ring_fwd(q, k, v, P: int, layout="zigzag", rank: int = -1, causal: bool = True,
-                out=None, lse=None, stream=None):
+                out=None, lse=None, stream=None, seq_len=None):
     """Ring attention over P virtual ranks (rank=-1: all, in the inputs'
     order -- natural, or striped for the striped layout; rank=r: that
-    rank's share in its local order)."""
+    rank's share in its local order).  seq_len: the real length when the
+    split does not divide it (striped tensors then hold the padded length;
+    padding rows of the output come back as (0, -inf))."""
     import torch
-    S, Hq, D = q.shape
+    _, Hq, D = q.shape
     _, Hkv, _ = k.shape
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
-    rows = S if rank < 0 else S // max(P, 1)
+    S = q.shape[0] if seq_len is None else int(seq_len)
+    rows_in, rows = _ring_rows(S, P, lay, rank)
+    _need(q, (rows_in, Hq, D), "q")
+    _need(k, (rows_in, Hkv, D), "k")
+    _need(v, (rows_in, Hkv, D), "v")
     if out is None:
         out = torch.empty(rows, Hq, D, device=q.device, dtype=torch.float32)
     if lse is None:
         lse = torch.empty(Hq, rows, device=q.device, dtype=torch.float32)
+    _need(out, (rows, Hq, D), "out")
+    _need(lse, (Hq, rows), "lse")
     _dense(q, k, v, out, lse)
     _check(lib.cp_ring_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            lse.data_ptr(), S, Hq, Hkv, D, P, lay, rank, int(bool(causal)),
@@ -205,23 +232,32 @@ def cp_attn_block_bwd(q, k, v, dout, lse, dvec, dq=None, dk=None, dv=None, q_off
 
 
 def cp_ring_bwd(q, k, v, out, lse, dout, P: int, layout="zigzag", rank: int = -1,
-                causal: bool = True, dq=None, dk=None, dv=None, dvec=None, stream=None):
+                causal: bool = True, dq=None, dk=None, dv=None, dvec=None, stream=None,
+                seq_len=None):
     """Backward of cp_ring_fwd: dq in the forward's output layout, dk and dv
-    [S][Hkv][D] float32 in the inputs' order -- natural, or striped for the
-    striped layout (contributions of the rank(s) computed)."""
+    [rows of k][Hkv][D] float32 in the inputs' order -- natural, or striped
+    for the striped layout (contributions of the rank(s) computed)."""
     import torch
-    S, Hq, D = q.shape
+    _, Hq, D = q.shape
     _, Hkv, _ = k.shape
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
-    rows = S if rank < 0 else S // max(P, 1)
+    S = q.shape[0] if seq_len is None else int(seq_len)
+    rows_in, rows = _ring_rows(S, P, lay, rank)
+    for t, shape, name in ((q, (rows_in, Hq, D), "q"), (k, (rows_in, Hkv, D), "k"),
+                           (v, (rows_in, Hkv, D), "v"), (out, (rows, Hq, D), "out"),
+                           (lse, (Hq, rows), "lse"), (dout, (rows, Hq, D), "dout")):
+        _need(t, shape, name)
     if dq is None:
         dq = torch.empty(rows, Hq, D, device=q.device, dtype=torch.float32)
     if dk is None:
-        dk = torch.empty(S, Hkv, D, device=q.device, dtype=torch.float32)
+        dk = torch.empty(rows_in, Hkv, D, device=q.device, dtype=torch.float32)
     if dv is None:
-        dv = torch.empty(S, Hkv, D, device=q.device, dtype=torch.float32)
+        dv = torch.empty(rows_in, Hkv, D, device=q.device, dtype=torch.float32)
     if dvec is None:
         dvec = torch.empty(Hq, rows, device=q.device, dtype=torch.float32)
+    for t, shape, name in ((dq, (rows, Hq, D), "dq"), (dk, (rows_in, Hkv, D), "dk"),
+                           (dv, (rows_in, Hkv, D), "dv"), (dvec, (Hq, rows), "dvec")):
+        _need(t, shape, name)
     _dense(q, k, v, out, lse, dout, dq, dk, dv, dvec)
     _check(lib.cp_ring_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
@@ -251,11 +287,15 @@ def cp_usp_fwd(q, k, v, P_u: int, P_r: int, layout="zigzag", rank: int = -1,
     _, Hkv, _ = k.shape
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
     rows = S if rank < 0 else S // max(P_r, 1)
+    need = cp_usp_fwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, _dtype_code(q))
+    _need(k, (S, Hkv, D), "k")
+    _need(v, (S, Hkv, D), "v")
     if out is None:
         out = torch.empty(rows, Hq, D, device=q.device, dtype=torch.float32)
     if lse is None:
         lse = torch.empty(Hq, rows, device=q.device, dtype=torch.float32)
-    need = cp_usp_fwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, _dtype_code(q))
+    _need(out, (rows, Hq, D), "out")
+    _need(lse, (Hq, rows), "lse")
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
     _dense(q, k, v, out, lse, workspace)
@@ -291,8 +331,10 @@ def cp_head_to_seq(x, y, P: int, rank: int = -1, stream=None):
 
 
 def cp_layout_index(layout, S: int, P: int, rank: int) -> np.ndarray:
+    """Natural positions of rank's local rows (padded_length / P entries;
+    positions >= S are padding rows)."""
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
-    n = S // max(P, 1)
+    n = padded_length(S, P, lay) // max(P, 1)
     idx = np.empty(max(n, 1), dtype=np.int32)
     _check(lib.cp_layout_index(lay, S, P, rank, idx.ctypes.data))
     return idx[:n]

@@ -193,6 +193,17 @@ __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float *p, int64_t n
         p[i] = 0.f;
 }
 
+// p[r * ld + c] = value for r < n_rows, c < n_cols (padding rows of an
+// output: out rows are one run, lse entries one run per head).
+__global__ __launch_bounds__(kThreads) void fill_2d_kernel(float *p, int64_t ld, int64_t n_rows,
+                                                           int64_t n_cols, float value)
+{
+    const int64_t n = n_rows * n_cols;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
+        p[(i / n_cols) * ld + i % n_cols] = value;
+}
+
 int64_t blocks_for_waves(int64_t n_waves) { return (n_waves + kThreads / 64 - 1) / (kThreads / 64); }
 
 }  // namespace
@@ -215,6 +226,18 @@ hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream)
         return hipSuccess;
     const int64_t blocks = std::min<int64_t>((n + kThreads - 1) / kThreads, 256 * 32);
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_2d(float *p, int64_t ld, int64_t n_rows, int64_t n_cols, float value,
+                          hipStream_t stream)
+{
+    const int64_t n = n_rows * n_cols;
+    if (n == 0)
+        return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + kThreads - 1) / kThreads, 256 * 32);
+    hipLaunchKernelGGL(fill_2d_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p, ld,
+                       n_rows, n_cols, value);
     return hipGetLastError();
 }
 

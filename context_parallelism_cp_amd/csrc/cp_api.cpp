@@ -17,10 +17,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <limits>
 #include <vector>
 
 using namespace cpattn;
@@ -232,6 +234,17 @@ int fill_zero(float *p, int64_t n, hipStream_t stream)
     return e == hipSuccess ? CP_OK : fail(CP_ERR_HIP, "fill launch failed: %s", hipGetErrorString(e));
 }
 
+// Output rows [row0, row0 + n) of out [rows][H][D] and lse [H][rows] (ld =
+// rows) set to the padding value (0, -inf).
+int fill_pad_rows(float *out, float *lse, int64_t rows, int H, int D, int64_t row0, int64_t n,
+                  hipStream_t st)
+{
+    hipError_t e = launch_fill_2d(out + (size_t)row0 * H * D, 0, 1, n * H * D, 0.f, st);
+    if (e == hipSuccess)
+        e = launch_fill_2d(lse + row0, rows, H, n, -std::numeric_limits<float>::infinity(), st);
+    return e == hipSuccess ? CP_OK : fail(CP_ERR_HIP, "fill launch failed: %s", hipGetErrorString(e));
+}
+
 // ------------------------------------------------------------ ring helpers
 int check_ring_shape(int64_t S, int P, cp_layout layout, int rank)
 {
@@ -241,18 +254,28 @@ int check_ring_shape(int64_t S, int P, cp_layout layout, int rank)
         return fail(CP_ERR_SHAPE, "rank must be -1 or in [0, P) (rank=%d, P=%d)", rank, P);
     if (S < 0)
         return fail(CP_ERR_SHAPE, "negative sequence length");
-    if (layout == CP_LAYOUT_CONTIGUOUS || layout == CP_LAYOUT_STRIPED) {
-        if (S % P != 0)
-            return fail(CP_ERR_SHAPE, "%s layout needs P | S (S=%lld, P=%d)",
-                        layout == CP_LAYOUT_STRIPED ? "striped" : "contiguous", (long long)S, P);
-    } else if (layout == CP_LAYOUT_ZIGZAG) {
-        if (S % (2 * (int64_t)P) != 0)
-            return fail(CP_ERR_SHAPE, "zigzag layout needs 2P | S (S=%lld, P=%d)",
-                        (long long)S, P);
-    } else {
+    if (layout != CP_LAYOUT_CONTIGUOUS && layout != CP_LAYOUT_ZIGZAG &&
+        layout != CP_LAYOUT_STRIPED)
         return fail(CP_ERR_SHAPE, "unknown layout %d", (int)layout);
-    }
+    if (S > ((int64_t)1 << 40))
+        return fail(CP_ERR_SHAPE, "sequence too long");
     return CP_OK;
+}
+
+// Length of the padded sequence: S rounded up to a multiple of the split
+// (P chunks; 2P for zigzag).  Positions >= S are padding: never read,
+// never visible as keys, and their output rows are written as (0, -inf).
+int64_t padded_len(int64_t S, int P, cp_layout layout)
+{
+    const int64_t m = layout == CP_LAYOUT_ZIGZAG ? 2 * (int64_t)P : P;
+    return (S + m - 1) / m * m;
+}
+
+// Rows of the q / k / v tensors: the real length in natural order, the
+// padded length in striped order (every shard has S_pad / P rows).
+int64_t input_rows(int64_t S, int P, cp_layout layout)
+{
+    return layout == CP_LAYOUT_STRIPED ? padded_len(S, P, layout) : S;
 }
 
 int pair_kind(int causal, int qc, int kc)
@@ -266,17 +289,32 @@ int pair_kind(int causal, int qc, int kc)
 int n_slots(cp_layout layout) { return layout == CP_LAYOUT_ZIGZAG ? 2 : 1; }
 
 // One (query chunk, key chunk) pair of a ring step: where its rows sit in the
-// q / k tensors and the positions the causal mask compares.
+// q / k tensors, how many of them are real, and the positions the causal
+// mask compares.
 struct RingPair {
     int slot;            // local query slot of the rank
     int qc, kc;          // chunk ids (striped: the rank ids)
-    int64_t q_row, k_row, len;
+    int64_t q_row, k_row;
+    int64_t cap;         // rows of a chunk in the padded split
+    int64_t len_q, len_k;  // real rows of the query and key chunk
     int64_t q_pos, k_pos;
     int kind;
 };
 
+int64_t clip_rows(int64_t S, int64_t row0, int64_t cap)
+{
+    return std::min(std::max<int64_t>(S - row0, 0), cap);
+}
+
+// Striped: rank r's real rows, positions r + jP < S for j < cap.
+int64_t striped_rows(int64_t S, int P, int r, int64_t cap)
+{
+    return S > r ? std::min<int64_t>(cap, (S - r + P - 1) / P) : 0;
+}
+
 // The pairs of rank r at the step where it holds rank src's KV block, in
-// order query slot, then key chunk.
+// order query slot, then key chunk, for the real length S (split as the
+// padded length; a pair with no real query or key row is SKIP).
 //  contiguous / zigzag: chunks of C rows at their natural positions, the
 //    tensors in natural order;
 //  striped: rank r's local row j is position r + jP, the tensors are the
@@ -287,27 +325,32 @@ struct RingPair {
 int ring_step_pairs(cp_layout layout, int64_t S, int P, int r, int src, int causal,
                     RingPair out[4])
 {
-    if (layout == CP_LAYOUT_STRIPED) {
-        const int64_t C = S / P;
-        out[0] = RingPair{0, r, src, (int64_t)r * C, (int64_t)src * C, C, 0, src > r ? 1 : 0,
-                          causal ? CP_PAIR_DIAG : CP_PAIR_FULL};
-        return 1;
-    }
+    const int64_t Sp = padded_len(S, P, layout);
     int n = 0;
-    if (layout == CP_LAYOUT_CONTIGUOUS) {
-        const int64_t C = S / P;
-        out[n++] = RingPair{0, r, src, r * C, src * C, C, r * C, src * C, pair_kind(causal, r, src)};
-        return n;
+    if (layout == CP_LAYOUT_STRIPED) {
+        const int64_t C = Sp / P;
+        out[n++] = RingPair{0, r, src, (int64_t)r * C, (int64_t)src * C, C,
+                            striped_rows(S, P, r, C), striped_rows(S, P, src, C), 0,
+                            src > r ? 1 : 0, causal ? CP_PAIR_DIAG : CP_PAIR_FULL};
+    } else if (layout == CP_LAYOUT_CONTIGUOUS) {
+        const int64_t C = Sp / P;
+        out[n++] = RingPair{0, r, src, r * C, src * C, C, clip_rows(S, r * C, C),
+                            clip_rows(S, src * C, C), r * C, src * C, pair_kind(causal, r, src)};
+    } else {
+        const int64_t C = Sp / (2 * P);
+        const int mine[2] = {r, 2 * P - 1 - r};
+        const int theirs[2] = {src, 2 * P - 1 - src};
+        for (int slot = 0; slot < 2; ++slot)
+            for (int kc : theirs) {
+                const int qc = mine[slot];
+                out[n++] = RingPair{slot, qc, kc, qc * C, kc * C, C, clip_rows(S, qc * C, C),
+                                    clip_rows(S, kc * C, C), qc * C, kc * C,
+                                    pair_kind(causal, qc, kc)};
+            }
     }
-    const int64_t C = S / (2 * P);
-    const int mine[2] = {r, 2 * P - 1 - r};
-    const int theirs[2] = {src, 2 * P - 1 - src};
-    for (int slot = 0; slot < 2; ++slot)
-        for (int kc : theirs) {
-            const int qc = mine[slot];
-            out[n++] = RingPair{slot, qc, kc, qc * C, kc * C, C, qc * C, kc * C,
-                                pair_kind(causal, qc, kc)};
-        }
+    for (int i = 0; i < n; ++i)
+        if (out[i].len_q == 0 || out[i].len_k == 0)
+            out[i].kind = CP_PAIR_SKIP;
     return n;
 }
 
@@ -316,7 +359,14 @@ int ring_step_pairs(cp_layout layout, int64_t S, int P, int r, int src, int caus
 // back), the rank's local order otherwise.
 int64_t out_row_of(int rank_arg, const RingPair &p)
 {
-    return rank_arg < 0 ? p.q_row : (int64_t)p.slot * p.len;
+    return rank_arg < 0 ? p.q_row : (int64_t)p.slot * p.cap;
+}
+
+// Output rows of a ring call: every rank in the inputs' order, or one rank's
+// padded share.
+int64_t ring_rows_out(int64_t S, int P, cp_layout layout, int rank)
+{
+    return rank < 0 ? input_rows(S, P, layout) : padded_len(S, P, layout) / P;
 }
 
 }  // namespace
@@ -397,9 +447,10 @@ int cp_layout_index(cp_layout layout, int64_t S, int P, int rank, int32_t *idx)
         return rc;
     if (rank < 0)
         return fail(CP_ERR_SHAPE, "cp_layout_index needs a rank in [0, P)");
-    if (S >= (int64_t(1) << 31))
-        return fail(CP_ERR_SHAPE, "cp_layout_index needs S < 2^31");
-    const int64_t rows = S / P;
+    const int64_t Sp = padded_len(S, P, layout);
+    if (Sp >= (int64_t(1) << 31))
+        return fail(CP_ERR_SHAPE, "cp_layout_index needs a padded length below 2^31");
+    const int64_t rows = Sp / P;
     for (int64_t j = 0; j < rows; ++j) {
         int64_t pos;
         if (layout == CP_LAYOUT_CONTIGUOUS)
@@ -452,8 +503,8 @@ int cp_ring_plan(int64_t S, int P, cp_layout layout, int rank, int causal,
                 p.k_chunk = rp[i].kc;
                 p.q_offset = rp[i].q_pos;
                 p.k_offset = rp[i].k_pos;
-                p.len_q = rp[i].len;
-                p.len_k = rp[i].len;
+                p.len_q = rp[i].len_q;
+                p.len_k = rp[i].len_k;
                 p.kind = rp[i].kind;
                 p.reserved = 0;
             }
@@ -469,17 +520,21 @@ int cp_ring_fwd(const void *q, const void *k, const void *v, float *out, float *
     int rc = check_ring_shape(S, P, layout, rank);
     if (rc)
         return rc;
-    const int64_t rows_out = rank < 0 ? S : S / P;
-    // q, k, v span the whole sequence; out and lse span rows_out rows.
+    const int64_t rows_in = input_rows(S, P, layout);
+    const int64_t rows_out = ring_rows_out(S, P, layout, rank);
+    // q, k, v span rows_in rows; out and lse span rows_out rows.
     if (S > 0 && (!q || !k || !v || !out || !lse))
         return fail(CP_ERR_NULL, "q, k, v, out and lse must be non-NULL");
-    rc = check_attn_common(q, k, v, out, lse, rows_out, S, Hq, Hkv, D, dtype);
+    rc = check_attn_common(q, k, v, out, lse, rows_out, rows_in, Hq, Hkv, D, dtype);
     if (rc)
         return rc;
     {
         const size_t eb = dtype == CP_BF16 ? 2 : 4;
-        const size_t qb = (size_t)S * Hq * D * eb, ob = (size_t)rows_out * Hq * D * 4;
-        if (overlaps(q, qb, out, ob) || overlaps(q, qb, lse, (size_t)rows_out * Hq * 4))
+        const size_t qb = (size_t)rows_in * Hq * D * eb, kb = (size_t)rows_in * Hkv * D * eb;
+        const size_t ob = (size_t)rows_out * Hq * D * 4, lb = (size_t)rows_out * Hq * 4;
+        if (overlaps(q, qb, out, ob) || overlaps(q, qb, lse, lb) || overlaps(k, kb, out, ob) ||
+            overlaps(k, kb, lse, lb) || overlaps(v, kb, out, ob) || overlaps(v, kb, lse, lb) ||
+            overlaps(out, ob, lse, lb))
             return fail(CP_ERR_ALIGN, "q, k, v, out and lse must not overlap");
     }
     if (S == 0)
@@ -523,11 +578,11 @@ int cp_ring_fwd(const void *q, const void *k, const void *v, float *out, float *
                         continue;
                     seg.row0 = rp[i].q_row;
                     seg.pos0 = rp[i].q_pos;
-                    seg.len = rp[i].len;
+                    seg.len = rp[i].len_q;
                     seg.out_row0 = out_row_of(rank, rp[i]);
                     if (rp[i].kind == CP_PAIR_SKIP)
                         continue;
-                    seg.kv[seg.n_kv++] = KvSeg{rp[i].k_row, rp[i].k_pos, rp[i].len};
+                    seg.kv[seg.n_kv++] = KvSeg{rp[i].k_row, rp[i].k_pos, rp[i].len_k};
                 }
                 if (seg.n_kv == 0)
                     continue;
@@ -541,12 +596,25 @@ int cp_ring_fwd(const void *q, const void *k, const void *v, float *out, float *
         if ((rc = flush()))
             return rc;
     }
-    // Every query chunk sees its own (diagonal) chunk at step 0, so every
-    // output row has been written.
-    for (int r = r_begin; r < r_end; ++r)
-        for (int slot = 0; slot < n_slots(layout); ++slot)
-            if (!started[r][slot])
+    // Every query chunk with real rows sees its own (diagonal) chunk at step
+    // 0, so every real output row has been written; the padding rows of the
+    // output get (0, -inf).
+    for (int r = r_begin; r < r_end; ++r) {
+        RingPair rp[4];
+        const int m = ring_step_pairs(layout, S, P, r, r, causal, rp);
+        for (int slot = 0; slot < n_slots(layout); ++slot) {
+            const RingPair *p = nullptr;
+            for (int i = 0; i < m && !p; ++i)
+                if (rp[i].slot == slot)
+                    p = &rp[i];
+            if (p->len_q > 0 && !started[r][slot])
                 return fail(CP_ERR_HIP, "internal: ring left rank %d slot %d unwritten", r, slot);
+            const int64_t o0 = out_row_of(rank, *p) + p->len_q;
+            const int64_t pad = std::min(p->cap - p->len_q, rows_out - o0);
+            if (pad > 0 && (rc = fill_pad_rows(out, lse, rows_out, Hq, D, o0, pad, st)))
+                return rc;
+        }
+    }
     return ok();
 }
 
@@ -617,17 +685,18 @@ int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out, c
     int rc = check_ring_shape(S, P, layout, rank);
     if (rc)
         return rc;
-    const int64_t rows_out = rank < 0 ? S : S / P;
+    const int64_t rows_in = input_rows(S, P, layout);
+    const int64_t rows_out = ring_rows_out(S, P, layout, rank);
     if (S > 0 && (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !dvec))
         return fail(CP_ERR_NULL, "every pointer of cp_ring_bwd must be non-NULL");
-    // dq, dout, lse and dvec span rows_out rows; q, k, v, dk and dv span S rows
-    rc = check_bwd(q, k, v, dout, lse, dvec, dq, dk, dv, rows_out, S, Hq, Hkv, D, dtype);
+    // dq, dout, lse and dvec span rows_out rows; q, k, v, dk and dv span rows_in rows
+    rc = check_bwd(q, k, v, dout, lse, dvec, dq, dk, dv, rows_out, rows_in, Hq, Hkv, D, dtype);
     if (rc)
         return rc;
     {
         const size_t eb = dtype == CP_BF16 ? 2 : 4;
-        const size_t qb = (size_t)S * Hq * D * eb, ob = (size_t)rows_out * Hq * D * 4;
-        const size_t gk = (size_t)S * Hkv * D * 4;
+        const size_t qb = (size_t)rows_in * Hq * D * eb, ob = (size_t)rows_out * Hq * D * 4;
+        const size_t gk = (size_t)rows_in * Hkv * D * 4;
         if (overlaps(q, qb, dq, ob) || overlaps(q, qb, dk, gk) || overlaps(q, qb, dv, gk) ||
             overlaps(out, ob, dq, ob) || overlaps(out, ob, dk, gk) || overlaps(out, ob, dv, gk) ||
             overlaps(dvec, (size_t)rows_out * Hq * 4, out, ob) ||
@@ -645,8 +714,8 @@ int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out, c
     });
     if (rc)
         return rc;
-    if ((rc = fill_zero(dq, rows_out * Hq * D, st)) || (rc = fill_zero(dk, S * Hkv * D, st)) ||
-        (rc = fill_zero(dv, S * Hkv * D, st)))
+    if ((rc = fill_zero(dq, rows_out * Hq * D, st)) ||
+        (rc = fill_zero(dk, rows_in * Hkv * D, st)) || (rc = fill_zero(dv, rows_in * Hkv * D, st)))
         return rc;
     const size_t eb = dtype == CP_BF16 ? 2 : 4;
     const int r_begin = rank < 0 ? 0 : rank;
@@ -672,8 +741,8 @@ int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out, c
                 b.dq = dq + (size_t)orow * Hq * D;
                 b.dk = dk + (size_t)p.k_row * Hkv * D;
                 b.dv = dv + (size_t)p.k_row * Hkv * D;
-                b.Sq = p.len;
-                b.Sk = p.len;
+                b.Sq = p.len_q;
+                b.Sk = p.len_k;
                 b.Hq = Hq;
                 b.Hkv = Hkv;
                 b.D = D;
@@ -799,6 +868,9 @@ static int usp_plan(int64_t S, int Hq, int Hkv, int D, int P_u, int P_r, cp_layo
     int rc = check_ring_shape(S, P_r, layout, rank < 0 ? -1 : rank / P_u);
     if (rc)
         return rc;
+    if (padded_len(S, P_r, layout) != S)
+        return fail(CP_ERR_SHAPE, "USP needs the ring split to divide S (S=%lld, P_r=%d)",
+                    (long long)S, P_r);
     if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
         return fail(CP_ERR_SHAPE, "need Hkv dividing Hq (Hq=%d, Hkv=%d)", Hq, Hkv);
     if (Hkv % P_u != 0)
@@ -884,8 +956,8 @@ int cp_usp_fwd(const void *q, const void *k, const void *v, float *out, float *l
                 if (rp[i].kc != rp[i].qc)   // one pair per query chunk of the group
                     continue;
                 rc = head_share_copy(true, (const char *)q + rp[i].q_row * qrow,
-                                     (char *)ws_q + rp[i].q_row * qrow_p, rp[i].len, Hq, D, P_u,
-                                     u, pl.eb, st);
+                                     (char *)ws_q + rp[i].q_row * qrow_p, rp[i].len_q, Hq, D,
+                                     P_u, u, pl.eb, st);
             }
         }
         // key and value rows of every group: the group's own by the

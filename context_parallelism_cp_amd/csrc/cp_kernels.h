@@ -100,6 +100,9 @@ hipError_t launch_bwd_dvec(const float *out, const void *dout, int dout_bf16, fl
 hipError_t launch_bwd_f32(const BwdLaunch &b, hipStream_t stream);
 // p[0, n) = 0 (a kernel, so that the library records no memset)
 hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
+// p[r * ld + c] = value for r < n_rows, c < n_cols.
+hipError_t launch_fill_2d(float *p, int64_t ld, int64_t n_rows, int64_t n_cols, float value,
+                          hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdLaunch &b, hipStream_t stream);
 
 }  // namespace cpattn

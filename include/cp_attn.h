@@ -69,6 +69,14 @@ typedef enum { CP_F32 = 0, CP_BF16 = 1 } cp_dtype;
  *               r, r+P, r+2P, ... in that local order.  Sequence tensors for
  *               this layout are given in striped order: the ranks' S/P-row
  *               shards back to back (row r*S/P + j is position r + j*P). */
+/* Lengths the split does not divide ([CP] section 7.1: pad up to a multiple
+ * of the CP degree, compute, discard): the split is that of the padded
+ * length S_pad = S rounded up to a multiple of P (2P for zigzag); positions
+ * >= S are padding rows.  Padding is never read, never visible as a key and
+ * costs no compute; a padding row of an output is written as out = 0,
+ * lse = -inf (of a gradient: 0).  Natural-order tensors keep their S rows;
+ * striped-order tensors hold S_pad rows (shard r, S_pad/P rows, ends in its
+ * padding rows, whose contents are ignored). */
 typedef enum {
     CP_LAYOUT_CONTIGUOUS = 0,
     CP_LAYOUT_ZIGZAG = 1,
@@ -141,14 +149,16 @@ int cp_lse_merge(const float *o1, const float *lse1, const float *o2, const floa
  * rank src (position src + jP) iff j <= i when src <= r and j <= i - 1 when
  * src > r, which is the causal mask at local offsets 0 and (src > r).
  * q, k, v are the whole sequence: q [S][Hq][D], k/v [S][Hkv][D], in natural
- * order (contiguous, zigzag) or striped order (striped).
- *   rank == -1: every rank; out [S][Hq][D] and lse [Hq][S] in the order of
- *   the inputs.
- *   0 <= rank < P: that rank's share only; out [S/P][Hq][D] and lse
- *   [Hq][S/P] in the rank's local row order (see cp_layout_index).
+ * order (contiguous, zigzag) or striped order (striped; S_pad rows when
+ * padded).  S is the real length and need not be divisible by the split.
+ *   rank == -1: every rank; out [rows][Hq][D] and lse [Hq][rows] in the
+ *   order of the inputs (rows = S, or S_pad for striped).
+ *   0 <= rank < P: that rank's share only; out [S_pad/P][Hq][D] and lse
+ *   [Hq][S_pad/P] in the rank's local row order (see cp_layout_index),
+ *   padding rows (0, -inf).
  * The merge is fused into the attention epilogue; no workspace is needed.
  * Errors: as cp_attn_block_fwd, plus CP_ERR_SHAPE when P < 1, rank outside
- * [-1, P), S not divisible by P (contiguous, striped) or by 2P (zigzag).
+ * [-1, P), S negative or above 2^40, or an unknown layout.
  */
 int cp_ring_fwd(const void *q, const void *k, const void *v, float *out, float *lse,
                 int64_t S, int Hq, int Hkv, int D, int P, cp_layout layout, int rank,
@@ -210,8 +220,8 @@ int cp_attn_block_bwd(const void *q, const void *k, const void *v, const void *d
  * -1 the inputs' order ([S][Hq][D], [Hq][S]); 0 <= rank < P that rank's
  * local order ([S/P][Hq][D], [Hq][S/P]).  dout has dtype; out and lse are
  * float32 (cp_ring_fwd's results).  dq is overwritten.  dk and dv are
- * [S][Hkv][D] float32 in the inputs' order and are overwritten with the
- * contributions of the rank(s) computed.  dvec is a
+ * [rows of k][Hkv][D] float32 in the inputs' order and are overwritten with
+ * the contributions of the rank(s) computed (padding rows 0).  dvec is a
  * caller-provided float32 scratch buffer of Hq * (rows of out) elements.
  * Errors: as cp_ring_fwd and cp_attn_block_bwd.
  */
@@ -272,7 +282,8 @@ int cp_head_to_seq(const void *x, void *y, int64_t S, int H, int D, int P, int r
  * cp_usp_fwd_workspace returns (head shares of q, k, v for the whole
  * sequence, and the ring's float32 output); reused across head shares, so
  * calls on one workspace must be ordered (same stream).
- * Errors: as cp_ring_fwd (with P_r), plus CP_ERR_SHAPE when P_u < 1, rank
+ * Errors: as cp_ring_fwd (with P_r), plus CP_ERR_SHAPE when the ring split
+ * does not divide S (no padding here), P_u < 1, rank
  * outside [-1, P_u*P_r), P_u not dividing Hkv (every Ulysses rank needs whole
  * KV heads) or not dividing S/P_r; CP_ERR_NULL / CP_ERR_WORKSPACE /
  * CP_ERR_ALIGN for a missing, short or misaligned workspace or one that
@@ -291,7 +302,8 @@ int cp_usp_fwd(const void *q, const void *k, const void *v, float *out, float *l
  *   contiguous: rank*S/P + j;
  *   zigzag (C = S/(2P)): j < C ? rank*C + j : (2P-1-rank)*C + (j - C);
  *   striped: rank + j*P.
- * idx is a host array of S/P int32 (so S must be below 2^31).
+ * idx is a host array of S_pad/P int32 (S_pad below 2^31); entries >= S
+ * are padding rows.
  * Errors: CP_ERR_NULL, CP_ERR_SHAPE.
  */
 int cp_layout_index(cp_layout layout, int64_t S, int P, int rank, int32_t *idx);
@@ -305,7 +317,8 @@ int cp_layout_index(cp_layout layout, int64_t S, int P, int rank, int32_t *idx);
  * step (P-way chunks); zigzag: four pairs per step (2P-way chunks);
  * striped: one pair per step, DIAG when causal (every shard holds early and
  * late positions), with the local offsets q_offset = 0 and k_offset =
- * (k_chunk > q_chunk) that its mask uses.
+ * (k_chunk > q_chunk) that its mask uses.  When S is padded, len_q and
+ * len_k count the real rows of the chunks and a pair with none is SKIP.
  * *n_pairs is the capacity of `pairs` on entry and the number of pairs on
  * return; pairs == NULL only queries the count.
  * Errors: CP_ERR_NULL (n_pairs), CP_ERR_SHAPE, CP_ERR_CAPACITY (the needed

@@ -45,7 +45,8 @@ def test_struct_layout_matches_header():
 
 
 @pytest.mark.parametrize("layout", [R.CONTIGUOUS, R.ZIGZAG, R.STRIPED])
-@pytest.mark.parametrize("S,P", [(32, 4), (64, 8), (48, 3), (16, 1), (131072, 8)])
+@pytest.mark.parametrize("S,P", [(32, 4), (64, 8), (48, 3), (16, 1), (131072, 8), (30, 4), (37, 8),
+                                 (5, 8), (100001, 8)])
 def test_layout_index_matches_oracle(layout, S, P):
     for r in range(P):
         got = cp.cp_layout_index(layout, S, P, r)
@@ -55,7 +56,8 @@ def test_layout_index_matches_oracle(layout, S, P):
 
 @pytest.mark.parametrize("layout", [R.CONTIGUOUS, R.ZIGZAG, R.STRIPED])
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("S,P", [(32, 4), (64, 8), (24, 3), (8, 1), (32768, 8)])
+@pytest.mark.parametrize("S,P", [(32, 4), (64, 8), (24, 3), (8, 1), (32768, 8), (30, 4), (37, 8),
+                                 (5, 8), (13, 3)])
 def test_ring_plan_matches_oracle(layout, causal, S, P):
     for rank in [-1] + list(range(P)):
         got = cp.cp_ring_plan(S, P, layout, rank, causal)
@@ -120,10 +122,9 @@ def test_ring_argument_errors():
     assert rc_ring(P=0) == cp.CP_ERR_SHAPE
     assert rc_ring(rank=4) == cp.CP_ERR_SHAPE
     assert rc_ring(rank=-2) == cp.CP_ERR_SHAPE
-    assert rc_ring(S=60) == cp.CP_ERR_SHAPE              # 2P does not divide S
-    assert rc_ring(S=62, layout=cp.CP_LAYOUT_CONTIGUOUS) == cp.CP_ERR_SHAPE
-    assert rc_ring(S=62, layout=cp.CP_LAYOUT_STRIPED) == cp.CP_ERR_SHAPE
-    assert "striped" in cp.cp_last_error()
+    assert rc_ring(S=-2) == cp.CP_ERR_SHAPE
+    assert rc_ring(S=-2, layout=cp.CP_LAYOUT_STRIPED) == cp.CP_ERR_SHAPE
+    assert "negative" in cp.cp_last_error()
     assert rc_ring(S=0, layout=cp.CP_LAYOUT_STRIPED) == cp.CP_OK
     assert rc_ring(layout=5) == cp.CP_ERR_SHAPE
     assert rc_ring(Hq=6, Hkv=4) == cp.CP_ERR_SHAPE
@@ -168,8 +169,8 @@ def test_gqa_ulysses_limit_from_the_page():
 
 def test_python_binding_raises_with_message():
     with pytest.raises(cp.CpError) as e:
-        cp.cp_layout_index("zigzag", 30, 4, 0)
-    assert e.value.code == cp.CP_ERR_SHAPE and "2P | S" in str(e.value)
+        cp.cp_layout_index("zigzag", 30, 4, 4)
+    assert e.value.code == cp.CP_ERR_SHAPE and "rank" in str(e.value)
 
 
 def test_timing_api_without_launches():
@@ -225,7 +226,7 @@ def test_dvec_argument_errors():
 def test_ring_bwd_argument_errors():
     f = cp.lib.cp_ring_bwd
     a = [FAKE * i for i in range(1, 11)]   # q k v out lse dout dq dk dv dvec
-    assert f(*a, 30, 8, 8, 16, 4, cp.CP_LAYOUT_ZIGZAG, -1, 1, cp.CP_F32, None) == cp.CP_ERR_SHAPE
+    assert f(*a, -30, 8, 8, 16, 4, cp.CP_LAYOUT_ZIGZAG, -1, 1, cp.CP_F32, None) == cp.CP_ERR_SHAPE
     assert f(*a, 32, 8, 8, 16, 4, cp.CP_LAYOUT_ZIGZAG, 4, 1, cp.CP_F32, None) == cp.CP_ERR_SHAPE
     assert f(None, *a[1:], 32, 8, 8, 16, 4, cp.CP_LAYOUT_ZIGZAG, -1, 1, cp.CP_F32,
              None) == cp.CP_ERR_NULL
@@ -280,3 +281,28 @@ def test_usp_argument_errors():
     assert rc_usp(ws=FAKE * 2 ** 12 + 16) == cp.CP_ERR_ALIGN
     assert rc_usp(ws=FAKE * 2 ** 8) == cp.CP_ERR_ALIGN      # overlaps k
     assert rc_usp(S=0) == cp.CP_OK
+
+
+def test_padded_shapes_in_the_binding():
+    """Real length S, padded split: q/k/v rows and output rows of each call."""
+    assert cp.padded_length(30, 4, "zigzag") == 32 and cp.padded_length(37, 8, "zigzag") == 48
+    assert cp.padded_length(37, 8, "striped") == 40 and cp.padded_length(32, 4, "contiguous") == 32
+    assert cp._ring_rows(37, 8, cp.CP_LAYOUT_ZIGZAG, -1) == (37, 37)
+    assert cp._ring_rows(37, 8, cp.CP_LAYOUT_ZIGZAG, 2) == (37, 6)
+    assert cp._ring_rows(37, 8, cp.CP_LAYOUT_STRIPED, -1) == (40, 40)
+    assert cp._ring_rows(37, 8, cp.CP_LAYOUT_STRIPED, 7) == (40, 5)
+    for layout in ("contiguous", "zigzag", "striped"):
+        for r in range(8):
+            idx = cp.cp_layout_index(layout, 37, 8, r)
+            assert idx.size == cp.padded_length(37, 8, layout) // 8
+    # a wrong buffer size is refused before the library is called
+    import torch
+    q = torch.zeros(37, 2, 16)
+    with pytest.raises(cp.CpError) as e:
+        cp.cp_ring_fwd(q, q, q, 8, "striped", -1, seq_len=37)
+    assert "q must have shape (40, 2, 16)" in str(e.value)
+
+
+def test_usp_needs_an_exact_split():
+    assert rc_usp(S=4097) == cp.CP_ERR_SHAPE
+    assert "divide S" in cp.cp_last_error()
