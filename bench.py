@@ -60,6 +60,17 @@ def ring_share_flop(S, H, D, P, layout="zigzag", rank=0):
     return 4.0 * D * H * (rank + 0.5) * C * C
 
 
+def plan_flop(cp, S, H, D, P, layout, rank):
+    """The same convention counted over the library's ring plan: 4*D*H per
+    pair of real rows, FULL pairs whole, DIAG pairs half (exact for padded
+    lengths too)."""
+    units = 0.0
+    for (_r, _t, _qc, _kc, _qo, _ko, lq, lk, kind) in cp.cp_ring_plan(S, P, layout, rank, True):
+        units += lq * lk if kind == cp.CP_PAIR_FULL else (lq * lk / 2.0 if kind == cp.CP_PAIR_DIAG
+                                                         else 0.0)
+    return 4.0 * D * H * units
+
+
 def ulysses_share_flop(S, H_local, D):
     """Full-sequence causal attention of H_local heads, diagonal counted half."""
     return 4.0 * D * H_local * S * S / 2.0
@@ -339,6 +350,9 @@ def main():
     ap.add_argument("--layout", choices=["zigzag", "striped", "contiguous"], default="zigzag",
                     help="split of the ring share (striped: inputs permuted to striped order "
                          "once, before timing)")
+    ap.add_argument("--seq", type=int, default=S,
+                    help="sequence length of the ring share (--part ring only; lengths the "
+                         "split does not divide are padded)")
     ap.add_argument("--rank", type=int, default=RING_RANK, choices=range(2 * P),
                     help="the virtual rank whose share is timed (ring: 0..7, usp: 0..15)")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -347,6 +361,10 @@ def main():
     args = ap.parse_args()
     if args.part != "usp" and args.rank >= P:
         ap.error(f"--rank must be below {P} for the ring share")
+    if args.seq != S and args.part != "ring":
+        ap.error("--seq applies to --part ring only")
+    if not 1 <= args.seq <= S:
+        ap.error(f"--seq must be in [1, {S}]")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the ring and Ulysses ranks are virtual and "
               "played on a single MI355X; run it with --gpus 1.", file=sys.stderr)
@@ -366,16 +384,18 @@ def main():
     dku, dvu = ku.to(dev), vu.to(dev)
     print(f"# inputs generated and resident in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr)
 
+    seq = args.seq
     if args.layout == "striped":
-        # a striped rank holds its shard in striped order: permute once
-        order = torch.cat([torch.from_numpy(cp.cp_layout_index("striped", S, P, r).astype("int64"))
-                           for r in range(P)]).to(dev)
+        # a striped rank holds its shard in striped order: permute once (the
+        # padding rows, if any, repeat the last row; they are never read)
+        order = torch.cat([torch.from_numpy(cp.cp_layout_index("striped", seq, P, r).astype("int64"))
+                           for r in range(P)]).clamp_(max=seq - 1).to(dev)
         rq, rk, rv = dq[order].contiguous(), dk[order].contiguous(), dv[order].contiguous()
         del order
     else:
-        rq, rk, rv = dq, dk, dv
+        rq, rk, rv = dq[:seq], dk[:seq], dv[:seq]
 
-    rows = S // P
+    rows = cp.padded_length(seq, P, args.layout) // P
     ring_out = torch.empty(rows, HQ, D, device=dev, dtype=torch.float32)
     ring_lse = torch.empty(HQ, rows, device=dev, dtype=torch.float32)
     hp, hkp = HQ // P, HKV_ULY // P
@@ -390,7 +410,7 @@ def main():
     def step():
         if args.part in ("both", "ring"):
             cp.cp_ring_fwd(rq, rk, rv, P, args.layout, args.rank, out=ring_out, lse=ring_lse,
-                           stream=stream)
+                           stream=stream, seq_len=seq)
         if args.part in ("both", "ulysses"):
             cp.cp_seq_to_head(dq, P, ULY_RANK, y=ql, stream=stream)
             cp.cp_seq_to_head(dku, P, ULY_RANK, y=kl, stream=stream)
@@ -430,7 +450,7 @@ def main():
     perm_ms, perm_n = cp.cp_timing_read(cp.CP_KERNEL_PERMUTE)
     cp.cp_timing_enable(False)
 
-    flop_ring = (ring_share_flop(S, HQ, D, P, args.layout, args.rank)
+    flop_ring = (plan_flop(cp, seq, HQ, D, P, args.layout, args.rank)
                  if args.part in ("both", "ring") else 0.0)
     flop_uly = ulysses_share_flop(S, hp, D) if args.part in ("both", "ulysses") else 0.0
     flop_step = flop_ring + flop_uly
@@ -460,12 +480,13 @@ def main():
                          "rank (S=131072, Hq=Hkv=32, D=128, P=8, 16 chunks of 8192) plus "
                          "Ulysses GQA rank (Hq=32, Hkv=8, P=8 -> 4 q heads on 1 KV head over "
                          "all 131072 tokens); bf16 inputs, fp32 out + lse"
-                         if (args.layout, args.rank) == ("zigzag", RING_RANK) else
+                         if (args.layout, args.rank, seq) == ("zigzag", RING_RANK, S) else
                          f"as the default workload with ring rank {args.rank} of the "
-                         f"{args.layout} split"),
+                         f"{args.layout} split over {seq} tokens"),
             "parts": args.part,
             "ring_layout": args.layout,
             "ring_rank": args.rank,
+            "ring_seq": seq,
             "S": S, "Hq": HQ, "Hkv_ring": HQ, "Hkv_ulysses": HKV_ULY, "D": D, "P": P,
             "flop_per_step": flop_step,
             "flop_convention": "4*D*Hq per visible (q,k) pair, diagonal chunk counted half",
