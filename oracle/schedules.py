@@ -431,3 +431,24 @@ def usp_attention(q, k, v, P_u: int, P_r: int, layout: int = ZIGZAG, causal: boo
             lses[r * P_u + u] = l[u][:, :, 0].T
             positions[r * P_u + u] = group_rows[r][u * Sl:(u + 1) * Sl]
     return outs, lses, positions
+
+
+def usp_bwd(q, k, v, dout, P_u: int, P_r: int, layout: int = ZIGZAG, causal: bool = True):
+    """Backward of ``usp_attention`` (the pages give no algorithm; the
+    plainest reading): per head share u the ring backward over the P_r
+    groups (``ring_bwd``) on that share's query heads and KV heads -- the
+    all-to-alls only move rows between ranks and leave every gradient where
+    the forward's rows came from.  Returns dq, dk, dv in natural order."""
+    q, k, v, dout = (np.asarray(x, dtype=np.float64) if not hasattr(x, "detach")
+                     else x.detach().double().numpy() for x in (q, k, v, dout))
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if Hkv % P_u or Hq % Hkv:
+        raise ValueError("USP needs P_u | Hkv and Hkv | Hq")
+    Hp, Hkp = Hq // P_u, Hkv // P_u
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for u in range(P_u):
+        hs, ks = slice(u * Hp, (u + 1) * Hp), slice(u * Hkp, (u + 1) * Hkp)
+        gq, gk, gv = ring_bwd(q[:, hs], k[:, ks], v[:, ks], dout[:, hs], P_r, layout, causal)
+        dq[:, hs], dk[:, ks], dv[:, ks] = gq, gk, gv
+    return dq, dk, dv

@@ -496,3 +496,19 @@ def pin_padding(ring_padded, padded_length, layout_index, ring_plan, layouts, zi
         r_outs, r_lses = ring(q, k, v, 4)[:2]
         for a, b in zip(outs, r_outs):
             np.testing.assert_allclose(a, b, atol=1e-13)
+
+
+def pin_usp_bwd(usp_bwd, attn, attn_bwd, layouts):
+    """The USP backward equals the single-pass gradient for every layout,
+    GQA included (8 query heads on 4 KV heads over 2 x 2 and 4 x 2 ranks)."""
+    for n, (S, Hq, Hkv, P_u, P_r) in enumerate([(32, 8, 4, 2, 2), (32, 8, 4, 4, 2),
+                                                (48, 4, 2, 2, 3)]):
+        q, k, v = rand((S, Hq, 8), 800 + n), rand((S, Hkv, 8), 810 + n), rand((S, Hkv, 8), 820 + n)
+        dout = rand((S, Hq, 8), 830 + n)
+        for causal in (True, False):
+            out, lse = attn(q, k, v, causal=causal)
+            want = attn_bwd(q, k, v, dout, out, lse, causal=causal)
+            for layout in layouts:
+                got = usp_bwd(q, k, v, dout, P_u, P_r, layout, causal)
+                for g, w in zip(got, want):
+                    np.testing.assert_allclose(g, w, atol=1e-12)

@@ -451,3 +451,15 @@ def test_padding_mutant_is_caught(name, relpath, old, new):
         except (AssertionError, ValueError, IndexError):
             failed += 1
     assert failed >= 1, f"no pin catches: {name}"
+
+
+@pytest.mark.parametrize("old,new", [
+    ("dq[:, hs], dk[:, ks], dv[:, ks] = gq, gk, gv", "dq[:, hs], dk[:, ks], dv[:, ks] = gq, gv, gk"),
+    ("hs, ks = slice(u * Hp, (u + 1) * Hp), slice(u * Hkp, (u + 1) * Hkp)",
+     "hs, ks = slice(u * Hp, (u + 1) * Hp), slice(0, Hkp)"),
+])
+def test_usp_bwd_mutant_is_caught(old, new):
+    sch = _load_mutant("oracle/schedules.py", old, new, "schedules")
+    with pytest.raises(AssertionError):
+        pins.pin_usp_bwd(sch.usp_bwd, sch.attention, sch.attention_bwd,
+                         (sch.CONTIGUOUS, sch.ZIGZAG, sch.STRIPED))

@@ -271,3 +271,7 @@ def test_padding_equals_single_pass():
     pins.pin_padding(R.ring_padded, R.padded_length, R.layout_index, R.ring_plan,
                      (R.CONTIGUOUS, R.ZIGZAG, R.STRIPED), R.ZIGZAG, A.attention,
                      (R.ring_contiguous, R.ring_zigzag, R.ring_striped))
+
+
+def test_usp_bwd_equals_single_pass():
+    pins.pin_usp_bwd(R.usp_bwd, A.attention, A.attention_bwd, (R.CONTIGUOUS, R.ZIGZAG, R.STRIPED))
