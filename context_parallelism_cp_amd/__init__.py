@@ -62,6 +62,10 @@ SIGNATURES = {
     "cp_usp_fwd_workspace": [_I64, _I, _I, _I, _I, _I, _I, _I, _I,
                              ctypes.POINTER(ctypes.c_size_t)],
     "cp_usp_fwd": [_P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _SZ, _P],
+    "cp_usp_bwd_workspace": [_I64, _I, _I, _I, _I, _I, _I, _I, _I,
+                             ctypes.POINTER(ctypes.c_size_t)],
+    "cp_usp_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I, _I,
+                   _I, _P, _SZ, _P],
     "cp_layout_index": [_I, _I64, _I, _I, _P],
     "cp_ring_plan": [_I64, _I, _I, _I, _I, _P, ctypes.POINTER(ctypes.c_int)],
     "cp_last_error": [],
@@ -304,6 +308,50 @@ def cp_usp_fwd(q, k, v, P_u: int, P_r: int, layout="zigzag", rank: int = -1,
                           _dtype_code(q), workspace.data_ptr(), workspace.numel(),
                           _stream(q, stream)))
     return out, lse
+
+
+def cp_usp_bwd_workspace(S: int, Hq: int, Hkv: int, D: int, P_u: int, P_r: int, layout,
+                         rank: int, dtype) -> int:
+    """Workspace bytes of cp_usp_bwd (dtype: CP_F32 / CP_BF16 or a torch dtype)."""
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    code = dtype if isinstance(dtype, int) else (CP_BF16 if str(dtype) == "torch.bfloat16"
+                                                 else CP_F32)
+    n = ctypes.c_size_t(0)
+    _check(lib.cp_usp_bwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, code, ctypes.byref(n)))
+    return n.value
+
+
+def cp_usp_bwd(q, k, v, out, lse, dout, P_u: int, P_r: int, layout="zigzag", rank: int = -1,
+               causal: bool = True, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward of cp_usp_fwd: dq in its output layout, dk and dv [S][Hkv][D]
+    (a rank writes only its head share)."""
+    import torch
+    S, Hq, D = q.shape
+    _, Hkv, _ = k.shape
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    rows = S if rank < 0 else S // max(P_r, 1)
+    need = cp_usp_bwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, _dtype_code(q))
+    f32 = dict(device=q.device, dtype=torch.float32)
+    if dq is None:
+        dq = torch.empty(rows, Hq, D, **f32)
+    if dk is None:
+        dk = torch.empty(S, Hkv, D, **f32)
+    if dv is None:
+        dv = torch.empty(S, Hkv, D, **f32)
+    for t, shape, name in ((k, (S, Hkv, D), "k"), (v, (S, Hkv, D), "v"),
+                           (out, (rows, Hq, D), "out"), (lse, (Hq, rows), "lse"),
+                           (dout, (rows, Hq, D), "dout"), (dq, (rows, Hq, D), "dq"),
+                           (dk, (S, Hkv, D), "dk"), (dv, (S, Hkv, D), "dv")):
+        _need(t, shape, name)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _dense(q, k, v, out, lse, dout, dq, dk, dv, workspace)
+    _check(lib.cp_usp_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                          dv.data_ptr(), S, Hq, Hkv, D, P_u, P_r, lay, rank, int(bool(causal)),
+                          _dtype_code(q), workspace.data_ptr(), workspace.numel(),
+                          _stream(q, stream)))
+    return dq, dk, dv
 
 
 def cp_seq_to_head(x, P: int, rank: int = -1, y=None, stream=None):

@@ -977,6 +977,131 @@ int cp_usp_fwd(const void *q, const void *k, const void *v, float *out, float *l
     return ok();
 }
 
+// Workspace of the USP backward: head shares of q, k, v (whole sequence),
+// of dout and out (output rows), and the ring backward's dq, dk, dv and
+// dvec for that share.
+struct UspBwdPlan {
+    size_t off_k, off_v, off_dout, off_out, off_dq, off_dk, off_dv, off_dvec, total;
+};
+
+static UspBwdPlan usp_bwd_plan(const UspPlan &pl, int64_t S, int D)
+{
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    UspBwdPlan b{};
+    const size_t qb = up((size_t)S * pl.Hp * D * pl.eb), kb = up((size_t)S * pl.Hkvp * D * pl.eb);
+    const size_t rows = (size_t)pl.rows_out;
+    b.off_k = qb;
+    b.off_v = b.off_k + kb;
+    b.off_dout = b.off_v + kb;
+    b.off_out = b.off_dout + up(rows * pl.Hp * D * pl.eb);
+    b.off_dq = b.off_out + up(rows * pl.Hp * D * 4);
+    b.off_dk = b.off_dq + up(rows * pl.Hp * D * 4);
+    b.off_dv = b.off_dk + up((size_t)S * pl.Hkvp * D * 4);
+    b.off_dvec = b.off_dv + up((size_t)S * pl.Hkvp * D * 4);
+    b.total = b.off_dvec + up(rows * pl.Hp * 4);
+    return b;
+}
+
+int cp_usp_bwd_workspace(int64_t S, int Hq, int Hkv, int D, int P_u, int P_r, cp_layout layout,
+                         int rank, cp_dtype dtype, size_t *bytes)
+{
+    if (!bytes)
+        return fail(CP_ERR_NULL, "bytes must be non-NULL");
+    UspPlan pl{};
+    const int rc = usp_plan(S, Hq, Hkv, D, P_u, P_r, layout, rank, dtype, &pl);
+    if (rc)
+        return rc;
+    *bytes = S == 0 ? 0 : usp_bwd_plan(pl, S, D).total;
+    return ok();
+}
+
+int cp_usp_bwd(const void *q, const void *k, const void *v, const float *out, const float *lse,
+               const void *dout, float *dq, float *dk, float *dv, int64_t S, int Hq, int Hkv,
+               int D, int P_u, int P_r, cp_layout layout, int rank, int causal, cp_dtype dtype,
+               void *workspace, size_t workspace_bytes, void *stream)
+{
+    UspPlan pl{};
+    int rc = usp_plan(S, Hq, Hkv, D, P_u, P_r, layout, rank, dtype, &pl);
+    if (rc)
+        return rc;
+    if (S > 0 && (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv))
+        return fail(CP_ERR_NULL, "every pointer of cp_usp_bwd must be non-NULL");
+    rc = check_bwd(q, k, v, dout, lse, lse, dq, dk, dv, pl.rows_out, S, Hq, Hkv, D, dtype);
+    if (rc)
+        return rc;
+    if (S == 0)
+        return ok();
+    const UspBwdPlan bp = usp_bwd_plan(pl, S, D);
+    if (!workspace)
+        return fail(CP_ERR_NULL, "workspace must be non-NULL");
+    if (workspace_bytes < bp.total)
+        return fail(CP_ERR_WORKSPACE, "workspace holds %zu bytes, the call needs %zu",
+                    workspace_bytes, bp.total);
+    if (!aligned(workspace, 256) || !aligned(out, 4))
+        return fail(CP_ERR_ALIGN, "workspace must be 256-byte aligned and out 4-byte aligned");
+    {
+        const size_t qb = (size_t)S * Hq * D * pl.eb, kb = (size_t)S * Hkv * D * pl.eb;
+        const size_t rows = (size_t)pl.rows_out;
+        const size_t ob = rows * Hq * D * 4, db = rows * Hq * D * pl.eb, lb = rows * Hq * 4;
+        const size_t gk = (size_t)S * Hkv * D * 4;
+        const void *ins[6] = {q, k, v, out, lse, dout};
+        const size_t inb[6] = {qb, kb, kb, ob, lb, db};
+        void *outs[3] = {dq, dk, dv};
+        const size_t outb[3] = {ob, gk, gk};
+        for (int i = 0; i < 6; ++i) {
+            if (overlaps(workspace, bp.total, ins[i], inb[i]))
+                return fail(CP_ERR_ALIGN, "workspace, inputs and gradients must not overlap");
+            for (int j = 0; j < 3; ++j)
+                if (overlaps(outs[j], outb[j], ins[i], inb[i]))
+                    return fail(CP_ERR_ALIGN, "workspace, inputs and gradients must not overlap");
+        }
+        for (int j = 0; j < 3; ++j)
+            if (overlaps(workspace, bp.total, outs[j], outb[j]) ||
+                overlaps(outs[j], outb[j], outs[(j + 1) % 3], outb[(j + 1) % 3]))
+                return fail(CP_ERR_ALIGN, "workspace, inputs and gradients must not overlap");
+    }
+    hipStream_t st = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    void *ws_q = ws, *ws_k = ws + bp.off_k, *ws_v = ws + bp.off_v, *ws_dout = ws + bp.off_dout;
+    float *ws_out = (float *)(ws + bp.off_out), *ws_dq = (float *)(ws + bp.off_dq);
+    float *ws_dk = (float *)(ws + bp.off_dk), *ws_dv = (float *)(ws + bp.off_dv);
+    float *ws_dvec = (float *)(ws + bp.off_dvec);
+    const int r = rank < 0 ? -1 : rank / P_u;
+    const size_t qrow = (size_t)Hq * D * pl.eb, qrow_p = (size_t)pl.Hp * D * pl.eb;
+    for (int u = (rank < 0 ? 0 : rank % P_u); u < (rank < 0 ? P_u : rank % P_u + 1); ++u) {
+        // head share u of the query rows computed here, of every key and
+        // value row, and of the output rows' out and dout
+        if (r < 0) {
+            rc = head_share_copy(true, q, ws_q, S, Hq, D, P_u, u, pl.eb, st);
+        } else {
+            RingPair rp[4];
+            const int m = ring_step_pairs(layout, S, P_r, r, r, causal, rp);
+            for (int i = 0; i < m && !rc; ++i)
+                if (rp[i].kc == rp[i].qc)
+                    rc = head_share_copy(true, (const char *)q + rp[i].q_row * qrow,
+                                         (char *)ws_q + rp[i].q_row * qrow_p, rp[i].len_q, Hq,
+                                         D, P_u, u, pl.eb, st);
+        }
+        if (rc || (rc = head_share_copy(true, k, ws_k, S, Hkv, D, P_u, u, pl.eb, st)) ||
+            (rc = head_share_copy(true, v, ws_v, S, Hkv, D, P_u, u, pl.eb, st)) ||
+            (rc = head_share_copy(true, dout, ws_dout, pl.rows_out, Hq, D, P_u, u, pl.eb, st)) ||
+            (rc = head_share_copy(true, out, ws_out, pl.rows_out, Hq, D, P_u, u, 4, st)))
+            return rc;
+        // the ring backward over the P_r groups on head share u
+        rc = cp_ring_bwd(ws_q, ws_k, ws_v, ws_out, lse + (size_t)u * pl.Hp * pl.rows_out,
+                         ws_dout, ws_dq, ws_dk, ws_dv, ws_dvec, S, pl.Hp, pl.Hkvp, D, P_r, layout,
+                         r, causal, dtype, stream);
+        if (rc)
+            return rc;
+        // gradients back into head share u
+        if ((rc = head_share_copy(false, ws_dq, dq, pl.rows_out, Hq, D, P_u, u, 4, st)) ||
+            (rc = head_share_copy(false, ws_dk, dk, S, Hkv, D, P_u, u, 4, st)) ||
+            (rc = head_share_copy(false, ws_dv, dv, S, Hkv, D, P_u, u, 4, st)))
+            return rc;
+    }
+    return ok();
+}
+
 int cp_timing_enable(int enable)
 {
     Timing &t = timing();

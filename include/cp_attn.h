@@ -297,6 +297,32 @@ int cp_usp_fwd(const void *q, const void *k, const void *v, float *out, float *l
                size_t workspace_bytes, void *stream);
 
 /*
+ * cp_usp_bwd -- the backward pass of cp_usp_fwd (no algorithm on the pages;
+ * the plainest reading): per head share u, the head-share copies of q (the
+ * rows computed here), k, v (every row), dout and out (output rows), the
+ * ring backward over the P_r groups on that share (cp_ring_bwd), and the
+ * copies of dq, dk, dv back into head share u.
+ * q, k, v as cp_usp_fwd; out, lse, dout and dq in cp_usp_fwd's output
+ * layout (rank == -1: [S] rows in the inputs' order; a rank: its ring
+ * group's S/P_r rows in local order); out and lse are cp_usp_fwd's float32
+ * results with every head written (rank == -1, or all P_u ranks of the
+ * group); dout has dtype.  dq [rows][Hq][D], dk and dv [S][Hkv][D] float32:
+ * rank == -1 writes the whole gradient; a rank writes only head share u of
+ * dq and of dk, dv, where dk and dv hold that rank's contributions (its
+ * group's queries), the other heads untouched.
+ * workspace: 256-byte aligned, cp_usp_bwd_workspace bytes; calls sharing
+ * one workspace must be ordered.
+ * Errors: as cp_usp_fwd and cp_ring_bwd.
+ */
+int cp_usp_bwd_workspace(int64_t S, int Hq, int Hkv, int D, int P_u, int P_r,
+                         cp_layout layout, int rank, cp_dtype dtype, size_t *bytes);
+int cp_usp_bwd(const void *q, const void *k, const void *v, const float *out,
+               const float *lse, const void *dout, float *dq, float *dk, float *dv,
+               int64_t S, int Hq, int Hkv, int D, int P_u, int P_r, cp_layout layout,
+               int rank, int causal, cp_dtype dtype, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/*
  * cp_layout_index -- host only, synchronous.  idx[j] (j < S/P) receives the
  * natural sequence position of rank `rank`'s local row j:
  *   contiguous: rank*S/P + j;

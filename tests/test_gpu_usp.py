@@ -138,3 +138,95 @@ def test_full_usp_rank_share_128k(layout, rank):
     o = out.t[lt][:, hs].double().cpu().numpy()
     lv = lse.t[hs][:, lt].double().cpu().numpy()
     compare(o, lv, ro[:, hs], rl[hs], BF16_OUT_TOL, BF16_LSE_TOL, f"128K USP {layout} rank {rank}")
+
+
+# ------------------------------------------------------------- backward
+from test_gpu_bwd import BF16_GRAD_REL, F32_GRAD_TOL, grads_compare, ring_rank_oracle  # noqa: E402
+
+
+def usp_rank_bwd_oracle(q, k, v, dout, P_u, P_r, layout, rank):
+    """dq of the rank's group rows (head share u) and its dk / dv (head share
+    u), from the oracle ring backward on the head-sliced tensors."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    u, r = rank % P_u, rank // P_u
+    hs = slice(u * Hq // P_u, (u + 1) * Hq // P_u)
+    ks = slice(u * Hkv // P_u, (u + 1) * Hkv // P_u)
+    gq, gk, gv = ring_rank_oracle(q[:, hs].contiguous(), k[:, ks].contiguous(),
+                                  v[:, ks].contiguous(), dout[:, hs].contiguous(), P_r,
+                                  cp.LAYOUTS[layout], r)
+    return hs, ks, gq, gk, gv
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "striped"])
+@pytest.mark.parametrize("P_u,P_r", [(2, 2), (4, 2)])
+def test_f32_usp_bwd_page_inputs(layout, P_u, P_r):
+    announce(f"f32 USP bwd P_u={P_u} P_r={P_r} {layout} on make_qkv() (Hkv=4)")
+    q, _, _ = make_qkv()
+    _, k, v = make_qkv(H=4, seed=3)
+    dout = make_qkv(seed=5)[0]
+    S = 32
+    order = input_order(layout, S, P_r)
+    ot = torch.from_numpy(order)
+    qd, kd, vd = dev(q[ot], k[ot], v[ot])
+    # every rank at once against the single-pass gradient
+    out, lse = cp.cp_usp_fwd(qd, kd, vd, P_u, P_r, layout, -1)
+    dq, dk, dv = Guarded(S, 8, 16), Guarded(S, 4, 16), Guarded(S, 4, 16)
+    cp.cp_usp_bwd(qd, kd, vd, out, lse, dout[ot].to(DEV).contiguous(), P_u, P_r, layout, -1,
+                  dq=dq.t, dk=dk.t, dv=dv.t)
+    torch.cuda.synchronize()
+    for g in (dq, dk, dv):
+        g.check()
+    qn, kn, vn, dn = (x.double().numpy() for x in (q, k, v, dout))
+    ro, rl = OA.attention(qn, kn, vn)
+    want = OA.attention_bwd(qn, kn, vn, dn, ro, rl)
+    grads_compare((dq.t, dk.t, dv.t), [w[order] for w in want], F32_GRAD_TOL, f"{layout} all")
+    np.testing.assert_allclose(OS.usp_bwd(q, k, v, dout, P_u, P_r, cp.LAYOUTS[layout])[0],
+                               want[0], atol=1e-12)
+    # each rank: its group's forward rows, its head share of the gradients
+    lay = cp.LAYOUTS[layout]
+    for rank in range(P_u * P_r):
+        r = rank // P_u
+        o, l = run_group(qd, kd, vd, P_u, P_r, layout, r)
+        idx = torch.from_numpy(OS.layout_index(lay, S, P_r, r).astype(np.int64))
+        gq = torch.full((S // P_r, 8, 16), 7.0, device=DEV)
+        gk = torch.full((S, 4, 16), 7.0, device=DEV)
+        gv = torch.full((S, 4, 16), 7.0, device=DEV)
+        cp.cp_usp_bwd(qd, kd, vd, o, l, dout[idx].to(DEV).contiguous(), P_u, P_r, layout, rank,
+                      dq=gq, dk=gk, dv=gv)
+        torch.cuda.synchronize()
+        hs, ks, wq, wk, wv = usp_rank_bwd_oracle(q, k, v, dout, P_u, P_r, layout, rank)
+        grads_compare((gq[:, hs], gk[:, ks], gv[:, ks]), (wq, wk, wv), F32_GRAD_TOL,
+                      f"{layout} rank {rank}")
+        other = torch.ones(8, dtype=torch.bool)
+        other[hs] = False
+        assert bool((gq[:, other] == 7.0).all())
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "striped"])
+def test_bf16_usp_bwd_gqa_exercise_2k(layout):
+    """32 query heads on 8 KV heads, 8 x 2 ranks, 2048 tokens: every rank
+    at once against the single-pass gradient, and rank 13 alone."""
+    S, Hq, Hkv, P_u, P_r = 2048, 32, 8, 8, 2
+    announce(f"bf16 USP bwd S={S} Hq={Hq} Hkv={Hkv} {P_u}x{P_r} {layout}")
+    q, k, v = make_qkv(S=S, H=Hq, D=128, seed=41, dtype=torch.bfloat16, Hkv=Hkv)
+    dout = make_qkv(S=S, H=Hq, D=128, seed=42, dtype=torch.bfloat16)[0]
+    order = input_order(layout, S, P_r)
+    ot = torch.from_numpy(order)
+    qd, kd, vd = dev(q[ot], k[ot], v[ot])
+    out, lse = cp.cp_usp_fwd(qd, kd, vd, P_u, P_r, layout, -1)
+    dq, dk, dv = cp.cp_usp_bwd(qd, kd, vd, out, lse, dout[ot].to(DEV).contiguous(), P_u, P_r,
+                               layout, -1)
+    torch.cuda.synchronize()
+    want = OS.usp_bwd(q, k, v, dout, P_u, P_r, cp.LAYOUTS[layout])
+    grads_compare((dq, dk, dv), [w[order] for w in want], BF16_GRAD_REL, f"{layout} all",
+                  rel=True)
+    rank = 13
+    r = rank // P_u
+    o, l = run_group(qd, kd, vd, P_u, P_r, layout, r)
+    idx = torch.from_numpy(OS.layout_index(cp.LAYOUTS[layout], S, P_r, r).astype(np.int64))
+    gq, gk, gv = cp.cp_usp_bwd(qd, kd, vd, o, l, dout[idx].to(DEV).contiguous(), P_u, P_r,
+                               layout, rank)
+    torch.cuda.synchronize()
+    hs, ks, wq, wk, wv = usp_rank_bwd_oracle(q, k, v, dout, P_u, P_r, layout, rank)
+    grads_compare((gq[:, hs], gk[:, ks], gv[:, ks]), (wq, wk, wv), BF16_GRAD_REL,
+                  f"{layout} rank {rank}", rel=True)

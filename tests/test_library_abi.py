@@ -306,3 +306,31 @@ def test_padded_shapes_in_the_binding():
 def test_usp_needs_an_exact_split():
     assert rc_usp(S=4097) == cp.CP_ERR_SHAPE
     assert "divide S" in cp.cp_last_error()
+
+
+def rc_usp_bwd(ws=FAKE * 2 ** 14, ws_bytes=1 << 40, **kw):
+    args = dict(S=4096, Hq=32, Hkv=8, D=128, P_u=8, P_r=2, layout=cp.CP_LAYOUT_ZIGZAG, rank=-1,
+                causal=1, dtype=cp.CP_BF16)
+    args.update(kw)
+    p = [FAKE * 2 ** i for i in range(4, 13)]
+    return cp.lib.cp_usp_bwd(*p, args["S"], args["Hq"], args["Hkv"], args["D"], args["P_u"],
+                             args["P_r"], args["layout"], args["rank"], args["causal"],
+                             args["dtype"], ws, ws_bytes, None)
+
+
+def test_usp_bwd_workspace_and_errors():
+    S, Hq, Hkv, D, P_u, P_r = 131072, 32, 8, 128, 8, 2
+    up = lambda b: (b + 255) // 256 * 256
+    rows = S // P_r
+    want = (up(S * 4 * D * 2) + 2 * up(S * D * 2) + up(rows * 4 * D * 2) + 2 * up(rows * 4 * D * 4)
+            + 2 * up(S * D * 4) + up(rows * 4 * 4))
+    assert cp.cp_usp_bwd_workspace(S, Hq, Hkv, D, P_u, P_r, "zigzag", 13, cp.CP_BF16) == want
+    assert rc_usp_bwd(P_u=3) == cp.CP_ERR_SHAPE
+    assert rc_usp_bwd(S=4097) == cp.CP_ERR_SHAPE
+    assert rc_usp_bwd(rank=16) == cp.CP_ERR_SHAPE
+    assert rc_usp_bwd(D=64) == cp.CP_ERR_UNSUPPORTED
+    assert rc_usp_bwd(ws=None) == cp.CP_ERR_NULL
+    assert rc_usp_bwd(ws_bytes=4096) == cp.CP_ERR_WORKSPACE
+    assert rc_usp_bwd(ws=FAKE * 2 ** 14 + 64) == cp.CP_ERR_ALIGN
+    assert rc_usp_bwd(ws=FAKE * 2 ** 4) == cp.CP_ERR_ALIGN     # the workspace is q
+    assert rc_usp_bwd(S=0) == cp.CP_OK
