@@ -21,11 +21,13 @@ The CPU oracle is timed on a bounded sample of the ring share's rows.
 
 ``--layout striped`` (or contiguous) times the ring share with that split
 instead (striped: q, k, v permuted to striped order once, before timing);
-``--part ring|ulysses|bwd|usp`` times one share, the backward pass, or one
-rank of the USP hybrid (8-way Ulysses x 2-way ring).
+``--part ring|ulysses|bwd|usp|usp_bwd`` times one share, the backward pass,
+or one rank of the USP hybrid (8-way Ulysses x 2-way ring), forward or
+backward.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--part both|ring|ulysses|bwd|usp] [--layout zigzag|striped|contiguous]
+                    [--part both|ring|ulysses|bwd|usp|usp_bwd]
+                    [--layout zigzag|striped|contiguous]
                     [--rank r]
 """
 from __future__ import annotations
@@ -247,6 +249,105 @@ def backward(args, cp, torch, q_host, dq, dk, dv, dku, dvu, ql, kl, vl, uly_out_
     print(json.dumps(result))
 
 
+def usp_bwd(args, cp, torch, dq, dku, dvu, stream):
+    """Backward of one rank's USP share (one JSON line): the forward of the
+    rank's whole ring group once, untimed (its out and lse), then per step
+    cp_usp_bwd of the rank (head-share copies, the ring backward on 4 query
+    heads and 1 KV head, the gradients copied back).  FLOP: 2.5x the
+    forward share's."""
+    from seeded_inputs import make_qkv
+    P_u, P_r = 8, 2
+    rank = args.rank
+    u, r = rank % P_u, rank // P_u
+    hp = HQ // P_u
+    rows = S // P_r
+    dev = "cuda:0"
+    qx, kx, vx = dq, dku, dvu
+    if args.layout == "striped":
+        order = torch.cat([torch.from_numpy(cp.cp_layout_index("striped", S, P_r, g).astype("int64"))
+                           for g in range(P_r)]).to(dev)
+        qx, kx, vx = (x[order].contiguous() for x in (dq, dku, dvu))
+        del order
+    out = torch.empty(rows, HQ, D, device=dev, dtype=torch.float32)
+    lse = torch.empty(HQ, rows, device=dev, dtype=torch.float32)
+    ws_f = torch.empty(cp.cp_usp_fwd_workspace(S, HQ, HKV_ULY, D, P_u, P_r, args.layout, rank,
+                                               cp.CP_BF16), device=dev, dtype=torch.uint8)
+    for uu in range(P_u):
+        cp.cp_usp_fwd(qx, kx, vx, P_u, P_r, args.layout, r * P_u + uu, out=out, lse=lse,
+                      workspace=ws_f, stream=stream)
+    del ws_f
+    idx = torch.from_numpy(cp.cp_layout_index(args.layout, S, P_r, r).astype("int64"))
+    dout = make_qkv(S=S, H=HQ, D=D, seed=1, dtype=torch.bfloat16)[0][idx].to(dev).contiguous()
+    f32 = dict(device=dev, dtype=torch.float32)
+    g_q, g_k, g_v = (torch.empty(rows, HQ, D, **f32), torch.empty(S, HKV_ULY, D, **f32),
+                     torch.empty(S, HKV_ULY, D, **f32))
+    ws = torch.empty(cp.cp_usp_bwd_workspace(S, HQ, HKV_ULY, D, P_u, P_r, args.layout, rank,
+                                             cp.CP_BF16), device=dev, dtype=torch.uint8)
+
+    def step():
+        cp.cp_usp_bwd(qx, kx, vx, out, lse, dout, P_u, P_r, args.layout, rank, dq=g_q, dk=g_k,
+                      dv=g_v, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    cp.cp_timing_enable(True)
+    cp.cp_timing_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    bwd_ms, bwd_n = cp.cp_timing_read(cp.CP_KERNEL_BWD_BF16)
+    perm_ms, perm_n = cp.cp_timing_read(cp.CP_KERNEL_PERMUTE)
+    dvec_ms, _ = cp.cp_timing_read(cp.CP_KERNEL_BWD_DVEC)
+    cp.cp_timing_enable(False)
+    flop_step = 2.5 * plan_flop(cp, S, hp, D, P_r, args.layout, r)
+    kern = flop_step * args.steps / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 else None
+    print(json.dumps({
+        "metric": "causal block-attn bwd TFLOP/s + % bf16 MFMA peak, USP 8x2, S=128K H=32/8 D=128",
+        "value": round(flop_step * args.steps / elapsed / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"backward of one rank's USP share: rank {rank} (u={u}, r={r}) of 8-way "
+                         f"Ulysses x 2-way {args.layout} ring, S=131072, Hq=32, Hkv=8, D=128; "
+                         "bf16 q, k, v, dout; fp32 gradients"),
+            "parts": "usp_bwd",
+            "ring_layout": args.layout,
+            "usp_rank": rank,
+            "flop_per_step": flop_step,
+            "flop_convention": "2.5 x (4*D*Hq_share per visible (q,k) pair, diagonal chunk half)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "bwd_dq_kernel + bwd_dkdv_kernel",
+            "achieved": round(kern, 2) if kern else None,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(kern / PEAK_BF16_TFLOPS, 4) if kern else None,
+            "traffic": None,
+            "launches": bwd_n,
+            "avg_launch_ms": round(bwd_ms / max(bwd_n, 1), 4),
+        },
+        "breakdown": {
+            "bwd_kernels_ms_per_step": round(bwd_ms / args.steps, 3),
+            "dvec_ms_per_step": round(dvec_ms / args.steps, 3),
+            "repack_ms_per_step": round(perm_ms / args.steps, 3),
+            "repack_launches_per_step": perm_n // max(args.steps, 1),
+        },
+    }))
+
+
 def usp(args, cp, torch, dq, dku, dvu, stream):
     """One rank's share of the USP hybrid (one JSON line): 32 query heads on
     8 KV heads over 16 ranks as 8-way Ulysses x 2-way ring (the handbook's
@@ -344,7 +445,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--part", choices=["both", "ring", "ulysses", "bwd", "usp"], default="both",
+    ap.add_argument("--part", choices=["both", "ring", "ulysses", "bwd", "usp", "usp_bwd"],
+                    default="both",
                     help="bwd: time the backward pass of both shares instead; usp: one rank "
                          "of the 8-way Ulysses x 2-way ring hybrid")
     ap.add_argument("--layout", choices=["zigzag", "striped", "contiguous"], default="zigzag",
@@ -359,7 +461,7 @@ def main():
                     help="before warm-up, copy 1 GiB device to device once (a plain copy "
                          "kernel of known size that scales HBM byte counters)")
     args = ap.parse_args()
-    if args.part != "usp" and args.rank >= P:
+    if args.part not in ("usp", "usp_bwd") and args.rank >= P:
         ap.error(f"--rank must be below {P} for the ring share")
     if args.seq != S and args.part != "ring":
         ap.error("--seq applies to --part ring only")
@@ -428,6 +530,9 @@ def main():
 
     if args.part == "usp":
         usp(args, cp, torch, dq, dku, dvu, stream)
+        return
+    if args.part == "usp_bwd":
+        usp_bwd(args, cp, torch, dq, dku, dvu, stream)
         return
     if args.part == "bwd":
         backward(args, cp, torch, q, rq, rk, rv, dku, dvu, ql, kl, vl, uly_out_l, uly_lse,
