@@ -16,8 +16,8 @@
 //
 // Two kernels, each owning its outputs (no atomics):
 //   * bwd_dq_kernel: a workgroup of 8 wavefronts owns 256 query rows of one
-//     head (32 per wavefront) and streams the KV block through LDS 64 keys
-//     at a time (3-stage ring of direct buffer->LDS loads).  Per 32-key half
+//     head (32 per wavefront) and streams the KV block through LDS 32 keys
+//     at a time (3-stage ring of direct buffer->LDS loads).  Per 32-key
 //     tile: S^T = K Q^T and dP^T = V dO^T (A = K or V fragments read from
 //     LDS, B = Q^T or dO^T kept in VGPRs), ds in registers, then
 //     dQ^T += K^T ds^T with K^T from transpose reads of the same K tile.  The
@@ -25,11 +25,14 @@
 //   * bwd_dkdv_kernel: a workgroup of 4 wavefronts (one per SIMD, so each
 //     has 512 registers and dK, dV stay in accumulation registers) owns 128
 //     keys of one KV head (32 per wavefront) and streams the query rows of
-//     every head of its group through LDS 64 at a time (q, dout, lse and
-//     dvec).  Per 32-query half tile: S = Q K^T and dP = dO V^T (A = Q or dO
-//     fragments from LDS, B = K^T or V^T in VGPRs), then dV += P^T dO and
-//     dK += ds^T Q with P and ds from registers and dO, Q from transpose
-//     reads.
+//     every head of its group through LDS 32 at a time (q, dout, lse and
+//     dvec; 4-stage ring).  Per 32-query tile: S = Q K^T and dP = dO V^T
+//     (A = Q or dO fragments from LDS, B = K^T or V^T in VGPRs), then
+//     dV += P^T dO and dK += ds^T Q with P and ds from registers and dO, Q
+//     from transpose reads.  The loop is software-pipelined: the MFMAs of
+//     the next tile's S and dP are interleaved (scheduling groups) with this
+//     tile's exponentials and ds, which a single wavefront per SIMD could
+//     not otherwise overlap.
 // Tiles use the forward kernel's layout: 256-byte rows with a 16-byte-chunk
 // XOR swizzle that keeps ds_read_b128 row fragments and ds_read_b64_tr_b16
 // column fragments free of bank conflicts.
@@ -373,7 +376,7 @@ constexpr int kStatBytes = 64 * 4;                     // one float per lane of 
 constexpr int kKvStage = 2 * kTileBytes + 2 * kStatBytes;   // q, dout, lse, dvec
 
 // the ring's three stages: q tile, dout tile, lse, dvec in each
-__shared__ __attribute__((aligned(1024))) char g_kv[3 * kKvStage];
+__shared__ __attribute__((aligned(1024))) char g_kv[4 * kKvStage];
 constexpr int kKvLoads = 2 * (kTileRows / 4) / kKvWaves;   // tile loads per wavefront
 constexpr int kKvLoads0 = kKvLoads + 2;                     // wavefront 0 also loads lse, dvec
 
@@ -426,7 +429,7 @@ void bwd_dkdv_kernel(BwdLaunch b)
         if (it < n_iter) {
             const int h = g * group + it / n_qt;
             const int64_t q0 = (int64_t)(qt_begin + it % n_qt) * kTileRows;
-            const uint32_t st = ring + (uint32_t)(it % 3) * kKvStage;
+            const uint32_t st = ring + (uint32_t)(it % 4) * kKvStage;
             load_two_tiles<kKvWaves>(st, st + kTileBytes, (const __bf16 *)b.q + h * HD,
                                      (const __bf16 *)b.dout + h * HD, q_stride, q0, b.Sq, wave,
                                      lane);
@@ -449,10 +452,36 @@ void bwd_dkdv_kernel(BwdLaunch b)
         dva[i] = f32x16{};
     }
 
-    auto tile_step = [&](int it) {
-        // tile it landed in every wavefront (tile it+1 may still be in
-        // flight); the stage of tile it-1, which takes tile it+2, is free
-        if (it + 1 < n_iter) {
+    // S = Q K^T and dP = dO V^T of query tile it (its stage in the ring)
+    auto scores = [&](int it, f32x16 &s, f32x16 &dp) {
+        const char LDS_AS *qt = (const char LDS_AS *)g_kv + (it % 4) * kKvStage;
+        const char LDS_AS *dt = qt + kTileBytes;
+        s = f32x16{};
+        dp = f32x16{};
+        bf16x8 qa[8];
+#pragma unroll
+        for (int sd = 0; sd < 8; ++sd)
+            qa[sd] = lds_b128(qt, fo.rowf[sd]);
+#pragma unroll
+        for (int sd = 0; sd < 8; ++sd)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[sd], kf[sd], s, 0, 0, 0);
+        bf16x8 da[8];
+#pragma unroll
+        for (int sd = 0; sd < 8; ++sd)
+            da[sd] = lds_b128(dt, fo.rowf[sd]);
+#pragma unroll
+        for (int sd = 0; sd < 8; ++sd)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[sd], vf[sd], dp, 0, 0, 0);
+    };
+    // waits until tile `it` is complete in every wavefront, `ahead` later
+    // tiles may still be in flight
+    auto wait_tile = [&](int ahead) {
+        if (ahead >= 2) {
+            if (wave == 0)
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads0));
+            else
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads));
+        } else if (ahead == 1) {
             if (wave == 0)
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads0));
             else
@@ -461,103 +490,114 @@ void bwd_dkdv_kernel(BwdLaunch b)
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         }
         lds_barrier();
-        issue(it + 2);
-        const char LDS_AS *qt = (const char LDS_AS *)g_kv + (it % 3) * kKvStage;
+    };
+
+    // Software pipeline over query tiles: step it runs S and dP of tile it+1
+    // on the matrix cores while the VALU turns tile it's S and dP into P and
+    // dS, then dV += P^T dO and dK += dS^T Q for tile it.  Four ring stages:
+    // tiles it and it+1 are read, it+2 is in flight, it+3 is issued into the
+    // stage of it-1.
+    f32x16 s_cur, dp_cur;
+    issue(0);
+    issue(1);
+    issue(2);
+    if (n_iter > 0) {
+        wait_tile(min(n_iter - 1, 2));
+        scores(0, s_cur, dp_cur);
+    }
+    // one pipeline step: consumes tile it's S and dP (s_c, dp_c), produces
+    // tile it+1's (s_n, dp_n; recomputed from tile it on the last step, and
+    // unused) -- unconditional, so the scheduler sees the MFMAs and the VALU
+    // work in one block
+    auto step = [&](int it, f32x16 &s_c, f32x16 &dp_c, f32x16 &s_n, f32x16 &dp_n) {
+        if (it + 1 < n_iter) {
+            // outstanding: tiles it+1 and (if any) it+2
+            wait_tile(min(n_iter - 2 - it, 1));
+            issue(it + 3);
+        }
+        const char LDS_AS *qt = (const char LDS_AS *)g_kv + (it % 4) * kKvStage;
         const char LDS_AS *dt = qt + kTileBytes;
         const float LDS_AS *lt = (const float LDS_AS *)(qt + 2 * kTileBytes);
         const float LDS_AS *vt = lt + kStatBytes / 4;
+        f32x4 l4s[4], d4s[4];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            l4s[i4] = *(const f32x4 LDS_AS *)(lt + 8 * i4 + 4 * hi);
+            d4s[i4] = *(const f32x4 LDS_AS *)(vt + 8 * i4 + 4 * hi);
+        }
+        scores(it + 1 < n_iter ? it + 1 : it, s_n, dp_n);
         const int64_t q0 = (int64_t)(qt_begin + it % n_qt) * kTileRows;
+        const int64_t qpos0 = b.q_offset + q0;
+        const bool need_mask = b.causal && first_key_pos + kKvRows - 1 > qpos0;
+        int lim = -1;
+        if (need_mask)
+            lim = (int)min(max(b.k_offset + my_key - qpos0, (int64_t)-1), (int64_t)64);
+        bf16x8 pf[2], sf[2];
 #pragma unroll
-        for (int half = 0; half < kTileRows / 32; ++half) {
-            // S = Q K^T, then dP = dO V^T, for the 32 query rows of this half
-            f32x16 s = f32x16{}, dp = f32x16{};
-            {
-                bf16x8 qa[8];
+        for (int i4 = 0; i4 < 4; ++i4) {
+            const f32x4 l4 = l4s[i4];
+            const f32x4 d4 = d4s[i4];
 #pragma unroll
-                for (int sd = 0; sd < 8; ++sd)
-                    qa[sd] = lds_b128(qt + half * 32 * 256, fo.rowf[sd]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int sd = 0; sd < 8; ++sd)
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[sd], kf[sd], s, 0, 0, 0);
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * i4 + e;
+                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_c[i], c, -l4[e] * kLog2e));
+                const int qi = 8 * i4 + 4 * hi + e;
+                p = qi >= lim ? p : 0.f;
+                pf[i >> 3][i & 7] = (__bf16)p;
+                sf[i >> 3][i & 7] = (__bf16)(p * (dp_c[i] - d4[e]));
             }
-            {
-                bf16x8 da[8];
+        }
+        // interleave: the 16 MFMAs of the next tile's S and dP, each followed
+        // by a share of this tile's VALU work
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
-                for (int sd = 0; sd < 8; ++sd)
-                    da[sd] = lds_b128(dt + half * 32 * 256, fo.rowf[sd]);
-                __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 8; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-                for (int sd = 0; sd < 8; ++sd)
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[sd], vf[sd], dp, 0, 0, 0);
-            }
-            // causal mask: query row q of the half sees key my_key iff
-            // k_offset + my_key <= q_offset + q0 + half*32 + q
-            const int64_t qpos0 = b.q_offset + q0 + half * 32;
-            const bool need_mask = b.causal && first_key_pos + kKvRows - 1 > qpos0;
-            int lim = 64;     // register i is visible iff its query index >= lim
-            if (need_mask)
-                lim = (int)min(max(b.k_offset + my_key - qpos0, (int64_t)-1), (int64_t)64);
-            // register i holds query 8*(i/4) + 4*hi + i%4 of the half: its lse
-            // and dvec come four consecutive rows per read
-            bf16x8 pf[2], sf[2];
+        for (int j = 0; j < 8; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            bf16x8 dc[2][4];
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const int r = half * 32 + 8 * i4 + 4 * hi;
-                const f32x4 l4 = *(const f32x4 LDS_AS *)(lt + r);
-                const f32x4 d4 = *(const f32x4 LDS_AS *)(vt + r);
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * i4 + e;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l4[e] * kLog2e));
-                    if (need_mask) {
-                        const int qi = 8 * i4 + 4 * hi + e;
-                        p = qi >= lim ? p : 0.f;
-                    }
-                    pf[i >> 3][i & 7] = (__bf16)p;
-                    sf[i >> 3][i & 7] = (__bf16)(p * (dp[i] - d4[e]));
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // dV += P^T dO and dK += ds^T Q with dO, Q column fragments
-            {
-                bf16x8 dc[2][4];
+                for (int db = 0; db < 4; ++db)
+                    dc[kh][db] = col_frag(dt, fo, kh, db);
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                    for (int db = 0; db < 4; ++db)
-                        dc[kh][db] = col_frag(dt, fo, 2 * half + kh, db);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int db = 0; db < 4; ++db)
+                    dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[kh], dc[kh][db], dva[db],
+                                                                     0, 0, 0);
+        }
+        {
+            bf16x8 qc[2][4];
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                    for (int db = 0; db < 4; ++db)
-                        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[kh], dc[kh][db],
-                                                                         dva[db], 0, 0, 0);
-            }
-            {
-                bf16x8 qc[2][4];
+                for (int db = 0; db < 4; ++db)
+                    qc[kh][db] = col_frag(qt, fo, kh, db);
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                    for (int db = 0; db < 4; ++db)
-                        qc[kh][db] = col_frag(qt, fo, 2 * half + kh, db);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int db = 0; db < 4; ++db)
-                        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf[kh], qc[kh][db],
-                                                                         dka[db], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+                for (int db = 0; db < 4; ++db)
+                    dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf[kh], qc[kh][db], dka[db],
+                                                                     0, 0, 0);
         }
     };
-
-    issue(0);
-    issue(1);
-    for (int it = 0; it < n_iter; ++it)
-        tile_step(it);
+    f32x16 s_alt, dp_alt;
+    for (int it = 0; it < n_iter; it += 2) {
+        step(it, s_cur, dp_cur, s_alt, dp_alt);
+        if (it + 1 >= n_iter)
+            break;
+        step(it + 1, s_alt, dp_alt, s_cur, dp_cur);
+    }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no tile load outlives the loop
 
     // epilogue: lane holds dK[key = 8*(i/4) + 4*hi + i%4][d = 32*db + l32]
