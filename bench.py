@@ -80,20 +80,23 @@ def ulysses_share_flop(S, H_local, D):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_128k_rank_share_hbm_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "context_parallelism_cp_amd", "csrc", "attn_bf16.hip")
+BWD_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bwd_128k_rank_share_hbm_traffic.md")
+BWD_KERNEL_SOURCE = os.path.join(ROOT, "context_parallelism_cp_amd", "csrc", "bwd_bf16.hip")
 
 
-def recorded_traffic():
-    """HBM bytes per attention launch from the committed FETCH_SIZE/WRITE_SIZE
-    summary, or None when the kernel source changed since it was taken."""
+def recorded_traffic(profile=TRAFFIC_PROFILE, source=KERNEL_SOURCE):
+    """HBM bytes per launch (or launch pair) from a committed FETCH_SIZE /
+    WRITE_SIZE summary, or None when the kernel source changed since it was
+    taken."""
     import hashlib
     try:
         fields = {}
-        with open(TRAFFIC_PROFILE, encoding="utf-8") as f:
+        with open(profile, encoding="utf-8") as f:
             for line in f:
                 if ":" in line and not line.startswith(("|", "#", "`")):
                     key, _, val = line.partition(":")
                     fields[key.strip()] = val.strip()
-        with open(KERNEL_SOURCE, "rb") as f:
+        with open(source, "rb") as f:
             current = hashlib.sha256(f.read()).hexdigest()
         if fields.get("kernel_source_sha256") != current:
             return None
@@ -236,7 +239,9 @@ def backward(args, cp, torch, q_host, dq, dk, dv, dku, dvu, ql, kl, vl, uly_out_
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4) if kern_tflops else None,
-            "traffic": None,
+            "traffic": (recorded_traffic(BWD_TRAFFIC_PROFILE, BWD_KERNEL_SOURCE)
+                        if (args.layout, args.rank) == ("zigzag", RING_RANK) else None),
+            "traffic_unit": "bytes per dq + dk/dv launch pair (HBM read + write, calibrated)",
             "launches": bwd_n,
             "avg_launch_ms": round(bwd_ms / max(bwd_n, 1), 4),
         },
