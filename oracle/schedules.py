@@ -355,12 +355,27 @@ def head_to_seq(head_x, P: int):
     return [r.transpose(1, 0, 2, 3).reshape(S // P, P * Hp, D) for r in all_to_all(sends)]
 
 
+def replicate_kv(x, P: int):
+    """The exercise's way past the KV-head limit: when P exceeds the KV head
+    count, every KV head is copied P/Hkv times (consecutive copies) before
+    the all-to-all, so rank p receives KV head p // (P/Hkv)."""
+    H = x.shape[1]
+    if H >= P:
+        return x
+    if P % H:
+        raise ValueError("KV replication needs Hkv | P")
+    return np.repeat(x, P // H, axis=1)
+
+
 def ulysses_attention(q, k, v, P: int, causal: bool = True):
     """Ulysses on P virtual ranks: split rows, seq_to_head q, k, v, local
-    full-sequence attention on each rank's head share, head_to_seq.
+    full-sequence attention on each rank's head share, head_to_seq.  With
+    fewer KV heads than ranks the KV heads are replicated first
+    (``replicate_kv``).
     Returns (per-rank local outputs, per-rank attention-time q shapes)."""
     q, k, v = (np.asarray(x, dtype=np.float64) if not hasattr(x, "detach")
                else x.detach().double().numpy() for x in (q, k, v))
+    k, v = replicate_kv(k, P), replicate_kv(v, P)
     S = q.shape[0]
     C = S // P
     rows = [slice(r * C, (r + 1) * C) for r in range(P)]

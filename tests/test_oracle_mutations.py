@@ -463,3 +463,19 @@ def test_usp_bwd_mutant_is_caught(old, new):
     with pytest.raises(AssertionError):
         pins.pin_usp_bwd(sch.usp_bwd, sch.attention, sch.attention_bwd,
                          (sch.CONTIGUOUS, sch.ZIGZAG, sch.STRIPED))
+
+
+@pytest.mark.parametrize("old,new", [
+    ("return np.repeat(x, P // H, axis=1)", "return np.tile(x, (1, P // H, 1))"),
+    ("k, v = replicate_kv(k, P), replicate_kv(v, P)", "k, v = replicate_kv(k, P), replicate_kv(k, P)"),
+])
+def test_kv_replication_mutant_is_caught(old, new):
+    import test_oracle_pins as T
+    sch = _load_mutant("oracle/schedules.py", old, new, "schedules")
+    real = T.R
+    T.R = sch
+    try:
+        with pytest.raises(AssertionError):
+            T.test_ulysses_kv_replication_exercise()
+    finally:
+        T.R = real

@@ -201,6 +201,24 @@ def test_ulysses_gqa_pins_head_mapping():
     assert lim["max_degree"][0] == lim["Hkv"][0]
 
 
+def test_ulysses_kv_replication_exercise():
+    """The exercise's answer for 16-way Ulysses on 32 query heads and 8 KV
+    heads: copy every KV head to two ranks before the all-to-all.  Rank p
+    then holds query heads 2p, 2p+1 and KV head p // 2, and the result is
+    the single pass."""
+    q, k, v = make_qkv(S=32, H=32, D=4, seed=5, Hkv=8)
+    outs, shapes = R.ulysses_attention(q, k, v, P=16)
+    ref_o, _ = A.attention(q, k, v)
+    for r in range(16):
+        np.testing.assert_allclose(outs[r], ref_o[2 * r:2 * (r + 1)], atol=1e-12)
+    assert all(s_ == (32, 2, 4) for s_ in shapes)
+    kr = R.replicate_kv(k.double().numpy(), 16)
+    for p in range(16):
+        assert np.array_equal(kr[:, p], k.double().numpy()[:, p // 2])
+    with pytest.raises(ValueError):
+        R.replicate_kv(np.zeros((4, 3, 2)), 8)
+
+
 # ------------------------------------------------------------- backward
 def test_bwd_finite_differences():
     pins.pin_bwd_finite_differences(A.attention, A.attention_bwd)
