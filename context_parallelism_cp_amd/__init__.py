@@ -66,6 +66,7 @@ SIGNATURES = {
                              ctypes.POINTER(ctypes.c_size_t)],
     "cp_usp_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I, _I,
                    _I, _P, _SZ, _P],
+    "cp_kv_seq_to_head": [_P, _P, _I64, _I, _I, _I, _I, _SZ, _P],
     "cp_layout_index": [_I, _I64, _I, _I, _P],
     "cp_ring_plan": [_I64, _I, _I, _I, _I, _P, ctypes.POINTER(ctypes.c_int)],
     "cp_last_error": [],
@@ -365,6 +366,22 @@ def cp_seq_to_head(x, P: int, rank: int = -1, y=None, stream=None):
     _dense(x, y)
     _check(lib.cp_seq_to_head(x.data_ptr(), y.data_ptr(), S, H, D, P, rank, x.element_size(),
                               _stream(x, stream)))
+    return y
+
+
+def cp_kv_seq_to_head(x, P: int, rank: int = -1, y=None, stream=None):
+    """K or V natural [S,H,D] -> [P,S,Hp,D] (rank=-1) or [S,Hp,D] (rank=p);
+    with P > H every head is replicated P/H times (Hp = 1)."""
+    import torch
+    S, H, D = x.shape
+    Hp = H // P if P <= H else 1
+    if y is None:
+        shape = (P, S, Hp, D) if rank < 0 else (S, Hp, D)
+        y = torch.empty(shape, device=x.device, dtype=x.dtype)
+    _need(y, (P, S, Hp, D) if rank < 0 else (S, Hp, D), "y")
+    _dense(x, y)
+    _check(lib.cp_kv_seq_to_head(x.data_ptr(), y.data_ptr(), S, H, D, P, rank,
+                                 x.element_size(), _stream(x, stream)))
     return y
 
 

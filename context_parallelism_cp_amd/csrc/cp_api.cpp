@@ -1102,6 +1102,43 @@ int cp_usp_bwd(const void *q, const void *k, const void *v, const float *out, co
     return ok();
 }
 
+int cp_kv_seq_to_head(const void *x, void *y, int64_t S, int H, int D, int P, int rank,
+                      size_t elem_bytes, void *stream)
+{
+    if (P >= 1 && H >= 1 && P <= H)
+        return repack(true, x, y, S, H, D, P, rank, elem_bytes, stream);
+    if (S != 0 && (!x || !y))
+        return fail(CP_ERR_NULL, "x and y must be non-NULL");
+    if (S < 0 || H < 1 || D < 1 || P < 1)
+        return fail(CP_ERR_SHAPE, "need S >= 0, H >= 1, D >= 1, P >= 1");
+    if (P % H != 0)
+        return fail(CP_ERR_SHAPE, "KV replication needs H | P (H=%d, P=%d)", H, P);
+    if (S % P != 0)
+        return fail(CP_ERR_SHAPE, "P must divide S (S=%lld, P=%d)", (long long)S, P);
+    if (rank < -1 || rank >= P)
+        return fail(CP_ERR_SHAPE, "rank must be -1 or in [0, P)");
+    if (elem_bytes != 2 && elem_bytes != 4)
+        return fail(CP_ERR_UNSUPPORTED, "elem_bytes must be 2 or 4");
+    if (!aligned(x, elem_bytes) || !aligned(y, elem_bytes))
+        return fail(CP_ERR_ALIGN, "x and y must be aligned to elem_bytes");
+    const size_t xb = (size_t)S * H * D * elem_bytes, share = (size_t)S * D * elem_bytes;
+    if (overlaps(x, xb, y, rank < 0 ? share * P : share))
+        return fail(CP_ERR_ALIGN, "x and y must not overlap");
+    if (S == 0)
+        return ok();
+    // rank p receives KV head p / (P/H): the head share of rank p/(P/H) in
+    // an H-way split (one head each)
+    hipStream_t st = (hipStream_t)stream;
+    const int rep = P / H;
+    for (int p = (rank < 0 ? 0 : rank); p < (rank < 0 ? P : rank + 1); ++p) {
+        void *dst = (char *)y + (rank < 0 ? (size_t)p * share : 0);
+        const int rc = head_share_copy(true, x, dst, S, H, D, H, p / rep, elem_bytes, st);
+        if (rc)
+            return rc;
+    }
+    return ok();
+}
+
 int cp_timing_enable(int enable)
 {
     Timing &t = timing();

@@ -255,6 +255,21 @@ int cp_head_to_seq(const void *x, void *y, int64_t S, int H, int D, int P, int r
                    size_t elem_bytes, void *stream);
 
 /*
+ * cp_kv_seq_to_head -- seq_to_head for K and V past the KV-head limit
+ * ([HB], section "练习", first exercise: with 8 KV heads Ulysses reaches
+ * 8-way at most; for 16-way, copy every KV head to two ranks before the
+ * all-to-all).  With P <= H it is cp_seq_to_head.  With P > H (H | P) every
+ * KV head is replicated P/H times, consecutive copies, so rank p receives
+ * KV head p / (P/H):
+ *   rank == -1: y = [P][S][1][D], y[p][t][0] = x[t][p / (P/H)];
+ *   rank == p : y = [S][1][D].
+ * Elements are copied bit for bit.  Errors: as cp_seq_to_head, plus
+ * CP_ERR_SHAPE when neither P | H nor H | P.
+ */
+int cp_kv_seq_to_head(const void *x, void *y, int64_t S, int H, int D, int P, int rank,
+                      size_t elem_bytes, void *stream);
+
+/*
  * cp_usp_fwd -- the hybrid the handbook names in its comparison of the two
  * schemes and in its GQA exercise (Ulysses inside a node, Ring Attention
  * across nodes: 32 query heads on 8 KV heads over 16 ranks as 8-way Ulysses

@@ -421,3 +421,32 @@ def test_full_ulysses_gqa_128k():
     # the same rows from the GQA definition over all 32 query heads (head h reads KV h // 4)
     ro_all, _ = oracle_rows(q, k, v, rows[:4])
     np.testing.assert_allclose(ro_all[:, 4 * p:4 * p + 4], ro[:4], atol=1e-12)
+
+
+def test_ulysses_16way_with_kv_replication():
+    """The handbook exercise's 16-way Ulysses on 32 query heads and 8 KV heads:
+    KV heads copied to two ranks each (bit-exact), every rank's local
+    attention, and head->seq back; equal to the single pass."""
+    S, Hq, Hkv, P = 2048, 32, 8, 16
+    announce(f"Ulysses {P}-way with KV replication S={S} Hq={Hq} Hkv={Hkv}")
+    q, k, v = make_qkv(S=S, H=Hq, D=128, seed=23, dtype=torch.bfloat16, Hkv=Hkv)
+    dq, dk, dv = dev(q, k, v)
+    kr = cp.cp_kv_seq_to_head(dk, P, -1)
+    torch.cuda.synchronize()
+    for p in range(P):
+        assert torch.equal(kr[p][:, 0], dk[:, p // 2])
+    ro, rl = oracle_rows(q, k, v, None)
+    out = Guarded(S, Hq, 128)
+    for p in range(P):
+        ql = cp.cp_seq_to_head(dq, P, p)
+        kl = cp.cp_kv_seq_to_head(dk, P, p)
+        vl = cp.cp_kv_seq_to_head(dv, P, p)
+        assert torch.equal(kl, kr[p])
+        o, l = cp.cp_attn_block_fwd(ql, kl, vl)
+        cp.cp_head_to_seq(o, out.t, P, p)
+        torch.cuda.synchronize()
+        compare(o, l, ro[:, 2 * p:2 * p + 2], rl[2 * p:2 * p + 2], BF16_OUT_TOL, BF16_LSE_TOL,
+                f"rank {p}")
+    out.check()
+    o = out.t.double().cpu().numpy()
+    assert float(np.abs(o - ro).max()) <= BF16_OUT_TOL

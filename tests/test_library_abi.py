@@ -334,3 +334,17 @@ def test_usp_bwd_workspace_and_errors():
     assert rc_usp_bwd(ws=FAKE * 2 ** 14 + 64) == cp.CP_ERR_ALIGN
     assert rc_usp_bwd(ws=FAKE * 2 ** 4) == cp.CP_ERR_ALIGN     # the workspace is q
     assert rc_usp_bwd(S=0) == cp.CP_OK
+
+
+def test_kv_seq_to_head_argument_errors():
+    f = cp.lib.cp_kv_seq_to_head
+    # 16-way on 8 KV heads is what replication allows; 12-way on 8 is neither split
+    assert f(FAKE, FAKE * 2 ** 20, 64, 8, 128, 12, -1, 2, None) == cp.CP_ERR_SHAPE
+    assert "H | P" in cp.cp_last_error()
+    assert f(FAKE, FAKE * 2 ** 20, 60, 8, 128, 16, -1, 2, None) == cp.CP_ERR_SHAPE   # 16 !| 60
+    assert f(FAKE, FAKE * 2 ** 20, 64, 8, 128, 16, 16, 2, None) == cp.CP_ERR_SHAPE   # rank
+    assert f(FAKE, FAKE * 2 ** 20, 64, 8, 128, 16, -1, 3, None) == cp.CP_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE + 2 ** 10, 64, 8, 128, 16, -1, 2, None) == cp.CP_ERR_ALIGN   # overlap
+    assert f(FAKE, FAKE * 2 ** 20, 0, 8, 128, 16, -1, 2, None) == cp.CP_OK
+    # P <= H is the plain seq_to_head, with its own checks
+    assert f(FAKE, FAKE * 2 ** 20, 64, 8, 128, 3, -1, 2, None) == cp.CP_ERR_SHAPE
