@@ -467,3 +467,28 @@ def usp_bwd(q, k, v, dout, P_u: int, P_r: int, layout: int = ZIGZAG, causal: boo
         gq, gk, gv = ring_bwd(q[:, hs], k[:, ks], v[:, ks], dout[:, hs], P_r, layout, causal)
         dq[:, hs], dk[:, ks], dv[:, ks] = gq, gk, gv
     return dq, dk, dv
+
+
+def usp_padded(q, k, v, P_u: int, P_r: int, layout: int = ZIGZAG, causal: bool = True):
+    """USP when the ring split does not divide S (the practitioner blog's
+    padding, section 7.1, applied to the ring groups): per head share u the
+    padded ring over the P_r groups (``ring_padded``) on that share's heads;
+    the all-to-all back then gives each group its real rows with every head.
+    (The Ulysses shards of a group's rows are then of unequal length; the
+    rows and their results are those of the padded ring.)
+
+    Returns (outs, lses, positions) per ring group: out [n_r, Hq, D], lse
+    [Hq, n_r] of the group's real rows in its local order, and their
+    positions."""
+    q, k, v = (np.asarray(x, dtype=np.float64) if not hasattr(x, "detach")
+               else x.detach().double().numpy() for x in (q, k, v))
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if Hkv % P_u or Hq % Hkv:
+        raise ValueError("USP needs P_u | Hkv and Hkv | Hq")
+    Hp, Hkp = Hq // P_u, Hkv // P_u
+    shares = [ring_padded(q[:, u * Hp:(u + 1) * Hp], k[:, u * Hkp:(u + 1) * Hkp],
+                          v[:, u * Hkp:(u + 1) * Hkp], P_r, layout, causal) for u in range(P_u)]
+    outs = [np.concatenate([shares[u][0][r] for u in range(P_u)], axis=1) for r in range(P_r)]
+    lses = [np.concatenate([shares[u][1][r] for u in range(P_u)], axis=0) for r in range(P_r)]
+    return outs, lses, shares[0][2]

@@ -512,3 +512,25 @@ def pin_usp_bwd(usp_bwd, attn, attn_bwd, layouts):
                 got = usp_bwd(q, k, v, dout, P_u, P_r, layout, causal)
                 for g, w in zip(got, want):
                     np.testing.assert_allclose(g, w, atol=1e-12)
+
+
+def pin_usp_padded(usp_padded, usp, attn, layouts):
+    """USP over a padded ring: the real rows equal the single pass for every
+    layout (GQA, causal or not); with no padding it gives usp_attention's
+    rows."""
+    for n, (S, P_u, P_r) in enumerate([(30, 2, 2), (37, 2, 4), (13, 4, 3)]):
+        q, k, v = rand((S, 8, 4), 900 + n), rand((S, 4, 4), 910 + n), rand((S, 4, 4), 920 + n)
+        for causal in (True, False):
+            ro, rl = attn(q, k, v, causal=causal)
+            for layout in layouts:
+                outs, lses, pos = usp_padded(q, k, v, P_u, P_r, layout, causal)
+                assert sorted(np.concatenate(pos).tolist()) == list(range(S))
+                for o, l, p in zip(outs, lses, pos):
+                    np.testing.assert_allclose(o, ro[p], rtol=0, atol=1e-12)
+                    np.testing.assert_allclose(l, rl[:, p], rtol=0, atol=1e-12)
+    q, k, v = rand((32, 8, 4), 930), rand((32, 4, 4), 931), rand((32, 4, 4), 932)
+    for layout in layouts:
+        outs, _, pos = usp_padded(q, k, v, 2, 2, layout)
+        u_outs, _, u_pos = usp(q, k, v, 2, 2, layout)
+        for r in range(2):
+            np.testing.assert_allclose(outs[r], np.concatenate(u_outs[2 * r:2 * r + 2]), atol=1e-13)

@@ -479,3 +479,16 @@ def test_kv_replication_mutant_is_caught(old, new):
             T.test_ulysses_kv_replication_exercise()
     finally:
         T.R = real
+
+
+@pytest.mark.parametrize("old,new", [
+    ("outs = [np.concatenate([shares[u][0][r] for u in range(P_u)], axis=1) for r in range(P_r)]",
+     "outs = [np.concatenate([shares[u][0][r] for u in range(P_u)][::-1], axis=1) for r in range(P_r)]"),
+    ("v[:, u * Hkp:(u + 1) * Hkp], P_r, layout, causal) for u in range(P_u)]",
+     "v[:, 0:Hkp], P_r, layout, causal) for u in range(P_u)]"),
+])
+def test_usp_padded_mutant_is_caught(old, new):
+    sch = _load_mutant("oracle/schedules.py", old, new, "schedules")
+    with pytest.raises(AssertionError):
+        pins.pin_usp_padded(sch.usp_padded, sch.usp_attention, sch.attention,
+                            (sch.CONTIGUOUS, sch.ZIGZAG, sch.STRIPED))

@@ -293,3 +293,8 @@ def test_padding_equals_single_pass():
 
 def test_usp_bwd_equals_single_pass():
     pins.pin_usp_bwd(R.usp_bwd, A.attention, A.attention_bwd, (R.CONTIGUOUS, R.ZIGZAG, R.STRIPED))
+
+
+def test_usp_padded_equals_single_pass():
+    pins.pin_usp_padded(R.usp_padded, R.usp_attention, A.attention,
+                        (R.CONTIGUOUS, R.ZIGZAG, R.STRIPED))
