@@ -283,18 +283,22 @@ def cp_usp_fwd_workspace(S: int, Hq: int, Hkv: int, D: int, P_u: int, P_r: int, 
 
 
 def cp_usp_fwd(q, k, v, P_u: int, P_r: int, layout="zigzag", rank: int = -1,
-               causal: bool = True, out=None, lse=None, workspace=None, stream=None):
+               causal: bool = True, out=None, lse=None, workspace=None, stream=None,
+               seq_len=None):
     """USP hybrid on P_u * P_r virtual ranks (rank = r * P_u + u).  rank=-1:
-    out [S,Hq,D], lse [Hq,S] in the inputs' order; rank: ring group r's
-    rows in its local order, head share u written."""
+    out, lse over the inputs' rows in their order; rank: ring group r's
+    rows in its local order, head share u written.  seq_len: the real length
+    when the ring split does not divide it (padded as cp_ring_fwd)."""
     import torch
-    S, Hq, D = q.shape
+    _, Hq, D = q.shape
     _, Hkv, _ = k.shape
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
-    rows = S if rank < 0 else S // max(P_r, 1)
+    S = q.shape[0] if seq_len is None else int(seq_len)
+    rows_in, rows = _ring_rows(S, P_r, lay, -1 if rank < 0 else rank // max(P_u, 1))
     need = cp_usp_fwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, _dtype_code(q))
-    _need(k, (S, Hkv, D), "k")
-    _need(v, (S, Hkv, D), "v")
+    _need(q, (rows_in, Hq, D), "q")
+    _need(k, (rows_in, Hkv, D), "k")
+    _need(v, (rows_in, Hkv, D), "v")
     if out is None:
         out = torch.empty(rows, Hq, D, device=q.device, dtype=torch.float32)
     if lse is None:
@@ -323,26 +327,29 @@ def cp_usp_bwd_workspace(S: int, Hq: int, Hkv: int, D: int, P_u: int, P_r: int, 
 
 
 def cp_usp_bwd(q, k, v, out, lse, dout, P_u: int, P_r: int, layout="zigzag", rank: int = -1,
-               causal: bool = True, dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """Backward of cp_usp_fwd: dq in its output layout, dk and dv [S][Hkv][D]
-    (a rank writes only its head share)."""
+               causal: bool = True, dq=None, dk=None, dv=None, workspace=None, stream=None,
+               seq_len=None):
+    """Backward of cp_usp_fwd: dq in its output layout, dk and dv over the
+    inputs' rows (a rank writes only its head share)."""
     import torch
-    S, Hq, D = q.shape
+    _, Hq, D = q.shape
     _, Hkv, _ = k.shape
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
-    rows = S if rank < 0 else S // max(P_r, 1)
+    S = q.shape[0] if seq_len is None else int(seq_len)
+    rows_in, rows = _ring_rows(S, P_r, lay, -1 if rank < 0 else rank // max(P_u, 1))
     need = cp_usp_bwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, _dtype_code(q))
     f32 = dict(device=q.device, dtype=torch.float32)
     if dq is None:
         dq = torch.empty(rows, Hq, D, **f32)
     if dk is None:
-        dk = torch.empty(S, Hkv, D, **f32)
+        dk = torch.empty(rows_in, Hkv, D, **f32)
     if dv is None:
-        dv = torch.empty(S, Hkv, D, **f32)
-    for t, shape, name in ((k, (S, Hkv, D), "k"), (v, (S, Hkv, D), "v"),
+        dv = torch.empty(rows_in, Hkv, D, **f32)
+    for t, shape, name in ((q, (rows_in, Hq, D), "q"), (k, (rows_in, Hkv, D), "k"),
+                           (v, (rows_in, Hkv, D), "v"),
                            (out, (rows, Hq, D), "out"), (lse, (Hq, rows), "lse"),
                            (dout, (rows, Hq, D), "dout"), (dq, (rows, Hq, D), "dq"),
-                           (dk, (S, Hkv, D), "dk"), (dv, (S, Hkv, D), "dv")):
+                           (dk, (rows_in, Hkv, D), "dk"), (dv, (rows_in, Hkv, D), "dv")):
         _need(t, shape, name)
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)

@@ -851,7 +851,7 @@ int cp_head_to_seq(const void *x, void *y, int64_t S, int H, int D, int P, int r
 struct UspPlan {
     int Hp, Hkvp;
     size_t eb;
-    int64_t rows_out;
+    int64_t rows_in, rows_out;
     size_t off_k, off_v, off_out, total;
 };
 
@@ -868,27 +868,25 @@ static int usp_plan(int64_t S, int Hq, int Hkv, int D, int P_u, int P_r, cp_layo
     int rc = check_ring_shape(S, P_r, layout, rank < 0 ? -1 : rank / P_u);
     if (rc)
         return rc;
-    if (padded_len(S, P_r, layout) != S)
-        return fail(CP_ERR_SHAPE, "USP needs the ring split to divide S (S=%lld, P_r=%d)",
-                    (long long)S, P_r);
     if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
         return fail(CP_ERR_SHAPE, "need Hkv dividing Hq (Hq=%d, Hkv=%d)", Hq, Hkv);
     if (Hkv % P_u != 0)
         return fail(CP_ERR_SHAPE,
                     "every Ulysses rank needs whole KV heads: P_u must divide Hkv (Hkv=%d, P_u=%d)",
                     Hkv, P_u);
-    if ((S / P_r) % P_u != 0)
-        return fail(CP_ERR_SHAPE, "P_u must divide the S/P_r rows of a ring group (S=%lld)",
-                    (long long)S);
     if (dtype != CP_BF16 && dtype != CP_F32)
         return fail(CP_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
     auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
     pl->Hp = Hq / P_u;
     pl->Hkvp = Hkv / P_u;
     pl->eb = dtype == CP_BF16 ? 2 : 4;
-    pl->rows_out = rank < 0 ? S : S / P_r;
-    const size_t qb = up((size_t)S * pl->Hp * D * pl->eb);
-    const size_t kb = up((size_t)S * pl->Hkvp * D * pl->eb);
+    // a ring split that does not divide S is padded as by the ring itself:
+    // rows_in rows of q, k, v (S, or S_pad in striped order), rows_out
+    // output rows (padding rows (0, -inf))
+    pl->rows_in = input_rows(S, P_r, layout);
+    pl->rows_out = ring_rows_out(S, P_r, layout, rank < 0 ? -1 : rank / P_u);
+    const size_t qb = up((size_t)pl->rows_in * pl->Hp * D * pl->eb);
+    const size_t kb = up((size_t)pl->rows_in * pl->Hkvp * D * pl->eb);
     pl->off_k = qb;
     pl->off_v = qb + kb;
     pl->off_out = qb + 2 * kb;
@@ -917,7 +915,7 @@ int cp_usp_fwd(const void *q, const void *k, const void *v, float *out, float *l
     int rc = usp_plan(S, Hq, Hkv, D, P_u, P_r, layout, rank, dtype, &pl);
     if (rc)
         return rc;
-    rc = check_attn_common(q, k, v, out, lse, pl.rows_out, S, Hq, Hkv, D, dtype);
+    rc = check_attn_common(q, k, v, out, lse, pl.rows_out, pl.rows_in, Hq, Hkv, D, dtype);
     if (rc)
         return rc;
     if (S == 0)
@@ -930,7 +928,8 @@ int cp_usp_fwd(const void *q, const void *k, const void *v, float *out, float *l
     if (!aligned(workspace, 256))
         return fail(CP_ERR_ALIGN, "workspace must be 256-byte aligned");
     {
-        const size_t qb = (size_t)S * Hq * D * pl.eb, kb = (size_t)S * Hkv * D * pl.eb;
+        const size_t qb = (size_t)pl.rows_in * Hq * D * pl.eb;
+        const size_t kb = (size_t)pl.rows_in * Hkv * D * pl.eb;
         const size_t ob = (size_t)pl.rows_out * Hq * D * 4, lb = (size_t)pl.rows_out * Hq * 4;
         if (overlaps(workspace, pl.total, q, qb) || overlaps(workspace, pl.total, k, kb) ||
             overlaps(workspace, pl.total, v, kb) || overlaps(workspace, pl.total, out, ob) ||
@@ -948,7 +947,7 @@ int cp_usp_fwd(const void *q, const void *k, const void *v, float *out, float *l
         // 1. the all-to-all inside the ring group: query rows of the group(s)
         //    computed here, head share u
         if (r < 0) {
-            rc = head_share_copy(true, q, ws_q, S, Hq, D, P_u, u, pl.eb, st);
+            rc = head_share_copy(true, q, ws_q, pl.rows_in, Hq, D, P_u, u, pl.eb, st);
         } else {
             RingPair rp[4];
             const int m = ring_step_pairs(layout, S, P_r, r, r, causal, rp);
@@ -962,8 +961,8 @@ int cp_usp_fwd(const void *q, const void *k, const void *v, float *out, float *l
         }
         // key and value rows of every group: the group's own by the
         // all-to-all, the others as the ring delivers them
-        if (rc || (rc = head_share_copy(true, k, ws_k, S, Hkv, D, P_u, u, pl.eb, st)) ||
-            (rc = head_share_copy(true, v, ws_v, S, Hkv, D, P_u, u, pl.eb, st)))
+        if (rc || (rc = head_share_copy(true, k, ws_k, pl.rows_in, Hkv, D, P_u, u, pl.eb, st)) ||
+            (rc = head_share_copy(true, v, ws_v, pl.rows_in, Hkv, D, P_u, u, pl.eb, st)))
             return rc;
         // 2. the ring over the P_r groups on head share u
         rc = cp_ring_fwd(ws_q, ws_k, ws_v, ws_out, lse + (size_t)u * pl.Hp * pl.rows_out, S,
@@ -988,7 +987,8 @@ static UspBwdPlan usp_bwd_plan(const UspPlan &pl, int64_t S, int D)
 {
     auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
     UspBwdPlan b{};
-    const size_t qb = up((size_t)S * pl.Hp * D * pl.eb), kb = up((size_t)S * pl.Hkvp * D * pl.eb);
+    const size_t qb = up((size_t)pl.rows_in * pl.Hp * D * pl.eb);
+    const size_t kb = up((size_t)pl.rows_in * pl.Hkvp * D * pl.eb);
     const size_t rows = (size_t)pl.rows_out;
     b.off_k = qb;
     b.off_v = b.off_k + kb;
@@ -996,8 +996,8 @@ static UspBwdPlan usp_bwd_plan(const UspPlan &pl, int64_t S, int D)
     b.off_out = b.off_dout + up(rows * pl.Hp * D * pl.eb);
     b.off_dq = b.off_out + up(rows * pl.Hp * D * 4);
     b.off_dk = b.off_dq + up(rows * pl.Hp * D * 4);
-    b.off_dv = b.off_dk + up((size_t)S * pl.Hkvp * D * 4);
-    b.off_dvec = b.off_dv + up((size_t)S * pl.Hkvp * D * 4);
+    b.off_dv = b.off_dk + up((size_t)pl.rows_in * pl.Hkvp * D * 4);
+    b.off_dvec = b.off_dv + up((size_t)pl.rows_in * pl.Hkvp * D * 4);
     b.total = b.off_dvec + up(rows * pl.Hp * 4);
     return b;
 }
@@ -1026,7 +1026,8 @@ int cp_usp_bwd(const void *q, const void *k, const void *v, const float *out, co
         return rc;
     if (S > 0 && (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv))
         return fail(CP_ERR_NULL, "every pointer of cp_usp_bwd must be non-NULL");
-    rc = check_bwd(q, k, v, dout, lse, lse, dq, dk, dv, pl.rows_out, S, Hq, Hkv, D, dtype);
+    rc = check_bwd(q, k, v, dout, lse, lse, dq, dk, dv, pl.rows_out, pl.rows_in, Hq, Hkv, D,
+                   dtype);
     if (rc)
         return rc;
     if (S == 0)
@@ -1040,10 +1041,11 @@ int cp_usp_bwd(const void *q, const void *k, const void *v, const float *out, co
     if (!aligned(workspace, 256) || !aligned(out, 4))
         return fail(CP_ERR_ALIGN, "workspace must be 256-byte aligned and out 4-byte aligned");
     {
-        const size_t qb = (size_t)S * Hq * D * pl.eb, kb = (size_t)S * Hkv * D * pl.eb;
+        const size_t qb = (size_t)pl.rows_in * Hq * D * pl.eb;
+        const size_t kb = (size_t)pl.rows_in * Hkv * D * pl.eb;
         const size_t rows = (size_t)pl.rows_out;
         const size_t ob = rows * Hq * D * 4, db = rows * Hq * D * pl.eb, lb = rows * Hq * 4;
-        const size_t gk = (size_t)S * Hkv * D * 4;
+        const size_t gk = (size_t)pl.rows_in * Hkv * D * 4;
         const void *ins[6] = {q, k, v, out, lse, dout};
         const size_t inb[6] = {qb, kb, kb, ob, lb, db};
         void *outs[3] = {dq, dk, dv};
@@ -1072,7 +1074,7 @@ int cp_usp_bwd(const void *q, const void *k, const void *v, const float *out, co
         // head share u of the query rows computed here, of every key and
         // value row, and of the output rows' out and dout
         if (r < 0) {
-            rc = head_share_copy(true, q, ws_q, S, Hq, D, P_u, u, pl.eb, st);
+            rc = head_share_copy(true, q, ws_q, pl.rows_in, Hq, D, P_u, u, pl.eb, st);
         } else {
             RingPair rp[4];
             const int m = ring_step_pairs(layout, S, P_r, r, r, causal, rp);
@@ -1082,8 +1084,8 @@ int cp_usp_bwd(const void *q, const void *k, const void *v, const float *out, co
                                          (char *)ws_q + rp[i].q_row * qrow_p, rp[i].len_q, Hq,
                                          D, P_u, u, pl.eb, st);
         }
-        if (rc || (rc = head_share_copy(true, k, ws_k, S, Hkv, D, P_u, u, pl.eb, st)) ||
-            (rc = head_share_copy(true, v, ws_v, S, Hkv, D, P_u, u, pl.eb, st)) ||
+        if (rc || (rc = head_share_copy(true, k, ws_k, pl.rows_in, Hkv, D, P_u, u, pl.eb, st)) ||
+            (rc = head_share_copy(true, v, ws_v, pl.rows_in, Hkv, D, P_u, u, pl.eb, st)) ||
             (rc = head_share_copy(true, dout, ws_dout, pl.rows_out, Hq, D, P_u, u, pl.eb, st)) ||
             (rc = head_share_copy(true, out, ws_out, pl.rows_out, Hq, D, P_u, u, 4, st)))
             return rc;
@@ -1095,8 +1097,8 @@ int cp_usp_bwd(const void *q, const void *k, const void *v, const float *out, co
             return rc;
         // gradients back into head share u
         if ((rc = head_share_copy(false, ws_dq, dq, pl.rows_out, Hq, D, P_u, u, 4, st)) ||
-            (rc = head_share_copy(false, ws_dk, dk, S, Hkv, D, P_u, u, 4, st)) ||
-            (rc = head_share_copy(false, ws_dv, dv, S, Hkv, D, P_u, u, 4, st)))
+            (rc = head_share_copy(false, ws_dk, dk, pl.rows_in, Hkv, D, P_u, u, 4, st)) ||
+            (rc = head_share_copy(false, ws_dv, dv, pl.rows_in, Hkv, D, P_u, u, 4, st)))
             return rc;
     }
     return ok();

@@ -297,10 +297,14 @@ int cp_kv_seq_to_head(const void *x, void *y, int64_t S, int H, int D, int P, in
  * cp_usp_fwd_workspace returns (head shares of q, k, v for the whole
  * sequence, and the ring's float32 output); reused across head shares, so
  * calls on one workspace must be ordered (same stream).
- * Errors: as cp_ring_fwd (with P_r), plus CP_ERR_SHAPE when the ring split
- * does not divide S (no padding here), P_u < 1, rank
+ * A ring split that does not divide S is padded as in cp_ring_fwd (with
+ * P_r): q, k, v then hold rows_in rows (S, or the padded length in striped
+ * order) and out/lse the padded output rows, padding rows (0, -inf); a
+ * group's Ulysses shards are then of unequal length, which the copies on
+ * one GPU never see.
+ * Errors: as cp_ring_fwd (with P_r), plus CP_ERR_SHAPE when P_u < 1, rank
  * outside [-1, P_u*P_r), P_u not dividing Hkv (every Ulysses rank needs whole
- * KV heads) or not dividing S/P_r; CP_ERR_NULL / CP_ERR_WORKSPACE /
+ * KV heads); CP_ERR_NULL / CP_ERR_WORKSPACE /
  * CP_ERR_ALIGN for a missing, short or misaligned workspace or one that
  * overlaps the tensors.
  */

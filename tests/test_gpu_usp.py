@@ -230,3 +230,71 @@ def test_bf16_usp_bwd_gqa_exercise_2k(layout):
     hs, ks, wq, wk, wv = usp_rank_bwd_oracle(q, k, v, dout, P_u, P_r, layout, rank)
     grads_compare((gq[:, hs], gk[:, ks], gv[:, ks]), (wq, wk, wv), BF16_GRAD_REL,
                   f"{layout} rank {rank}", rel=True)
+
+
+# ------------------------------------------------------------- padding
+from test_gpu_padding import expected, input_positions, out_positions, to_input  # noqa: E402
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "zigzag", "striped"])
+def test_f32_usp_padded_page_inputs(layout):
+    """29 rows of the page's make_qkv() (8 query heads on 4 KV heads) over
+    2 x 2 ranks: no ring split divides 29.  All ranks at once and every
+    group, real rows against the single pass and the padded-USP oracle,
+    padding rows (0, -inf); then the backward of all ranks."""
+    S, P_u, P_r = 29, 2, 2
+    announce(f"f32 USP padded S={S} P_u={P_u} P_r={P_r} {layout}")
+    q, _, _ = (x[:S] for x in make_qkv())
+    _, k, v = (x[:S] for x in make_qkv(H=4, seed=3))
+    dout = make_qkv(seed=5)[0][:S]
+    ipos = input_positions(layout, S, P_r)
+    qd, kd, vd = (to_input(x, ipos, S) for x in (q, k, v))
+    lay = cp.LAYOUTS[layout]
+    ro, rl = OA.attention(q, k, v)
+    po, pl, ppos = OS.usp_padded(q, k, v, P_u, P_r, lay)
+    out, lse = cp.cp_usp_fwd(qd, kd, vd, P_u, P_r, layout, -1, seq_len=S)
+    torch.cuda.synchronize()
+    wo, wl = expected(ro, rl, ipos, S)
+    compare(out, lse, wo, wl, F32_TOL, F32_TOL, f"{layout} all ranks")
+    for r in range(P_r):
+        opos = out_positions(layout, S, P_r, r)
+        rows = len(opos)
+        o, l = Guarded(rows, 8, 16), Guarded(8, rows)
+        for u in range(P_u):
+            cp.cp_usp_fwd(qd, kd, vd, P_u, P_r, layout, r * P_u + u, out=o.t, lse=l.t, seq_len=S)
+        torch.cuda.synchronize()
+        o.check(), l.check()
+        wo, wl = expected(ro, rl, opos, S)
+        compare(o.t, l.t, wo, wl, F32_TOL, F32_TOL, f"{layout} group {r}")
+        real = torch.from_numpy(np.nonzero(opos < S)[0])
+        compare(o.t[real], l.t[:, real], po[r], pl[r], F32_TOL, F32_TOL, f"{layout} group {r} oracle")
+    # backward of every rank at once: the single-pass gradient on the real rows
+    dd = to_input(dout, ipos, S)
+    dd = torch.where(torch.isnan(dd), torch.zeros_like(dd), dd)
+    gq, gk, gv = cp.cp_usp_bwd(qd, kd, vd, out, lse, dd, P_u, P_r, layout, -1, seq_len=S)
+    torch.cuda.synchronize()
+    qn, kn, vn, dn = (x.double().numpy() for x in (q, k, v, dout))
+    want = OA.attention_bwd(qn, kn, vn, dn, ro, rl)
+    real = np.nonzero(ipos < S)[0]
+    rt = torch.from_numpy(real)
+    grads_compare((gq[rt], gk[rt], gv[rt]), [w[ipos[real]] for w in want], F32_GRAD_TOL,
+                  f"{layout} bwd")
+    pad = torch.from_numpy(np.nonzero(ipos >= S)[0])
+    for g in (gq, gk, gv):
+        assert bool((g[pad] == 0).all())
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "striped"])
+def test_bf16_usp_padded_gqa_exercise(layout):
+    """1999 tokens, 32 query heads on 8 KV heads, 8 x 2 ranks (the ring
+    split padded): every rank at once against the C oracle."""
+    S, Hq, Hkv, P_u, P_r = 1999, 32, 8, 8, 2
+    announce(f"bf16 USP padded S={S} Hq={Hq} Hkv={Hkv} {P_u}x{P_r} {layout}")
+    q, k, v = make_qkv(S=S, H=Hq, D=128, seed=47, dtype=torch.bfloat16, Hkv=Hkv)
+    ro, rl = oracle_rows(q, k, v, None)
+    ipos = input_positions(layout, S, P_r)
+    qd, kd, vd = (to_input(x, ipos, S) for x in (q, k, v))
+    out, lse = cp.cp_usp_fwd(qd, kd, vd, P_u, P_r, layout, -1, seq_len=S)
+    torch.cuda.synchronize()
+    wo, wl = expected(ro, rl, ipos, S)
+    compare(out, lse, wo, wl, BF16_OUT_TOL, BF16_LSE_TOL, f"{layout} all ranks")

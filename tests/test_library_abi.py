@@ -269,8 +269,7 @@ def test_usp_argument_errors():
     assert rc_usp(P_r=0) == cp.CP_ERR_SHAPE
     assert rc_usp(rank=16) == cp.CP_ERR_SHAPE
     assert rc_usp(rank=-2) == cp.CP_ERR_SHAPE
-    assert rc_usp(S=4092) == cp.CP_ERR_SHAPE                # 2 P_r does not divide S
-    assert rc_usp(S=40, layout=cp.CP_LAYOUT_CONTIGUOUS) == cp.CP_ERR_SHAPE   # 8 !| 40/2
+    assert rc_usp(S=-4) == cp.CP_ERR_SHAPE
     assert rc_usp(layout=7) == cp.CP_ERR_SHAPE
     assert rc_usp(Hq=30) == cp.CP_ERR_SHAPE
     assert rc_usp(D=64) == cp.CP_ERR_UNSUPPORTED
@@ -303,9 +302,15 @@ def test_padded_shapes_in_the_binding():
     assert "q must have shape (40, 2, 16)" in str(e.value)
 
 
-def test_usp_needs_an_exact_split():
-    assert rc_usp(S=4097) == cp.CP_ERR_SHAPE
-    assert "divide S" in cp.cp_last_error()
+def test_usp_padded_workspace():
+    """A ring split that does not divide S: the head shares span the padded
+    striped order, the output rows the padded group."""
+    up = lambda b: (b + 255) // 256 * 256
+    S, P_u, P_r = 4097, 8, 2
+    Sp = 4098                                   # striped: a multiple of P_r
+    rows = Sp // P_r
+    want = up(Sp * 4 * 128 * 2) + 2 * up(Sp * 1 * 128 * 2) + up(rows * 4 * 128 * 4)
+    assert cp.cp_usp_fwd_workspace(S, 32, 8, 128, P_u, P_r, "striped", 3, cp.CP_BF16) == want
 
 
 def rc_usp_bwd(ws=FAKE * 2 ** 14, ws_bytes=1 << 40, **kw):
@@ -326,7 +331,7 @@ def test_usp_bwd_workspace_and_errors():
             + 2 * up(S * D * 4) + up(rows * 4 * 4))
     assert cp.cp_usp_bwd_workspace(S, Hq, Hkv, D, P_u, P_r, "zigzag", 13, cp.CP_BF16) == want
     assert rc_usp_bwd(P_u=3) == cp.CP_ERR_SHAPE
-    assert rc_usp_bwd(S=4097) == cp.CP_ERR_SHAPE
+    assert rc_usp_bwd(S=-1) == cp.CP_ERR_SHAPE
     assert rc_usp_bwd(rank=16) == cp.CP_ERR_SHAPE
     assert rc_usp_bwd(D=64) == cp.CP_ERR_UNSUPPORTED
     assert rc_usp_bwd(ws=None) == cp.CP_ERR_NULL
