@@ -450,3 +450,21 @@ def test_ulysses_16way_with_kv_replication():
     out.check()
     o = out.t.double().cpu().numpy()
     assert float(np.abs(o - ro).max()) <= BF16_OUT_TOL
+
+
+def test_one_million_tokens_rank_share():
+    """Large positions: 2^20 tokens, 4 heads, zigzag ring over 8 ranks, the
+    last rank's share (chunks 7 and 8 of 16, positions up to 589823 seeing up
+    to that many keys); sampled rows recomputed by the C oracle."""
+    S, H, P, rank = 1 << 20, 4, 8, 7
+    announce(f"bf16 ring S={S} H={H} P={P} zigzag rank {rank} (sampled rows)")
+    q, k, v = make_qkv(S=S, H=H, D=128, seed=3, dtype=torch.bfloat16)
+    dq, dk, dv = dev(q, k, v)
+    out, lse = Guarded(S // P, H, 128), Guarded(H, S // P)
+    cp.cp_ring_fwd(dq, dk, dv, P, "zigzag", rank, out=out.t, lse=lse.t)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    del dq, dk, dv
+    rows = chunk_edge_rows(S // P, S // (2 * P), 6, seed=13)
+    check_share(out.t, lse.t, q, k, v, OS.layout_index(cp.CP_LAYOUT_ZIGZAG, S, P, rank), rows,
+                "1M zigzag rank 7")
