@@ -75,6 +75,7 @@ constexpr int kStages = 3;
 constexpr int kTileBytes = BN * HD * 2;             // 16 KiB per K or V tile
 constexpr int kStageBytes = 2 * kTileBytes;         // K then V
 constexpr float kTau = 8.0f;            // lazy-rescale threshold, log2 units
+constexpr float kSumBound = 256.0f;     // 2^kTau
 constexpr int kMaxOrder = 768;          // tiles of the heaviest-first table
 constexpr int kXcds = 8;
 
@@ -369,7 +370,13 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
         __syncthreads();
         issue(t + 2, std::integral_constant<int, (ST + 2) % 3>{});
         const TileRef r = tile_ref(t);
-        const KvSeg &kv = qs.kv[r.seg];
+        // The segment's length and position are read here, while no LDS read
+        // is in flight, and pinned in scalar registers: read at their first
+        // use (after the V fragment requests) the argument-block load's wait
+        // would also drain those LDS reads before the softmax.
+        int64_t kv_len = qs.kv[r.seg].len;
+        int64_t kv_pos0 = qs.kv[r.seg].pos0;
+        __asm__ volatile("" : "+s"(kv_len), "+s"(kv_pos0));
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             f32x16 cur[QB];
@@ -385,16 +392,14 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
                     vfr[kh][db] = v_frag(vt, 2 * half + kh, db);
             __builtin_amdgcn_sched_barrier(0);
             const int64_t key0 = r.key0 + half * 32;      // first key of the half tile
-            const bool need_mask = (key0 + 32 > kv.len) ||
-                                   (a.causal && kv.pos0 + key0 + 31 > first_pos);
-            float alpha[QB];
-            bool any_rescale = false;
+            const bool need_mask = (key0 + 32 > kv_len) ||
+                                   (a.causal && kv_pos0 + key0 + 31 > first_pos);
+            if (need_mask) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                if (need_mask) {
+                for (int qb = 0; qb < QB; ++qb) {
                     // key k of the half tile (0..31) is visible iff k <= lim
-                    const int tail = (int)min(max(kv.len - 1 - key0, (int64_t)-1), (int64_t)64);
-                    const int base_c = (int)min(max(first_pos - kv.pos0 - key0, (int64_t)-512),
+                    const int tail = (int)min(max(kv_len - 1 - key0, (int64_t)-1), (int64_t)64);
+                    const int base_c = (int)min(max(first_pos - kv_pos0 - key0, (int64_t)-512),
                                                 (int64_t)512);
                     const int lim = a.causal ? min(tail, base_c + row_off[qb]) : tail;
                     const int lim_l = max(lim, -1) - 4 * hi;
@@ -405,42 +410,71 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
                         cur[qb][i] = kc > lim_l ? -INFINITY : cur[qb][i];
                     }
                 }
-                float mx = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    mx = fmaxf(mx, cur[qb][i]);
-                mx = max_xor32(mx) * scale_log2;
-                const bool up = mx > m_run[qb] + kTau;
-                any_rescale |= up;
-                const float m_new = up ? mx : m_run[qb];
-                alpha[qb] = up ? __builtin_amdgcn_exp2f(m_run[qb] - m_new) : 1.f;
-                m_run[qb] = m_new;
             }
-            if (__any(any_rescale)) {
+            // Exponentials against the running max as it stands.  They are
+            // kept when every lane's partial sum stays below 2^kTau: then
+            // every exponential does, i.e. no score exceeds the running max
+            // by kTau and the max would not have been raised.  Otherwise
+            // the wavefront takes the exact path: half-tile max, lazy raise,
+            // rescale, exponentials again.
+            bf16x8 pf[QB][2];
+            float rs[QB];
+            auto exps = [&](bool first) {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
-                    l_run[qb] *= alpha[qb];
+                    // A row without a finite running max yet gives +inf or NaN
+                    // exponentials on the first pass (-m_run = +inf), which
+                    // fails the sum test below; the exact pass uses 0 instead.
+                    const float m_use =
+                        first ? m_run[qb] : (m_run[qb] == -INFINITY ? 0.f : m_run[qb]);
 #pragma unroll
-                    for (int db = 0; db < 4; ++db)
-                        o_acc[qb][db] *= alpha[qb];
+                    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const float p = __builtin_amdgcn_exp2f(
+                                __builtin_fmaf(cur[qb][8 * kh + j], scale_log2, -m_use));
+                            rs[qb] = (kh == 0 && j == 0) ? p : rs[qb] + p;
+                            pf[qb][kh][j] = (__bf16)p;
+                        }
                 }
-            }
-            bf16x8 pf[QB][2];
+            };
+            exps(true);
+            bool exact = false;
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-                float rs = 0.f;
+            for (int qb = 0; qb < QB; ++qb)
+                exact |= !(rs[qb] < kSumBound);   // also true for NaN
+            if (__any(exact)) {
+                float alpha[QB];
+                bool any_rescale = false;
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
+                for (int qb = 0; qb < QB; ++qb) {
+                    float mx = -INFINITY;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float p = __builtin_amdgcn_exp2f(
-                            __builtin_fmaf(cur[qb][8 * kh + j], scale_log2, -m_use));
-                        rs += p;
-                        pf[qb][kh][j] = (__bf16)p;
+                    for (int i = 0; i < 16; ++i)
+                        mx = fmaxf(mx, cur[qb][i]);
+                    mx = max_xor32(mx) * scale_log2;
+                    const bool up = mx > m_run[qb] + kTau;
+                    any_rescale |= up;
+                    const float m_new = up ? mx : m_run[qb];
+                    alpha[qb] = up ? __builtin_amdgcn_exp2f(m_run[qb] - m_new) : 1.f;
+                    m_run[qb] = m_new;
+                }
+                if (__any(any_rescale)) {
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        l_run[qb] *= alpha[qb];
+#pragma unroll
+                        for (int db = 0; db < 4; ++db)
+                            o_acc[qb][db] *= alpha[qb];
                     }
-                l_run[qb] += sum_xor32(rs);
+                }
+                exps(false);
             }
+            // each lane keeps its own partial row sum; the two halves of a
+            // row are added in the epilogue
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                l_run[qb] += rs[qb];
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -473,13 +507,14 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
     const float kLn2 = 0.6931471805599453f;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+        // lanes l and l ^ 32 hold partial sums of the same row
+        const float l = sum_xor32(l_run[qb]);
         const int64_t my_row = tile_row0 + row_off[qb];
         if (my_row >= qs.len)
             continue;
         const int64_t orow = qs.out_row0 + my_row;
         float *out = a.out + (orow * a.Hq + h) * HD;
         float *lse_p = a.lse + (int64_t)h * a.lse_ld + orow;
-        const float l = l_run[qb];
         const float lse_blk = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
         const float inv_l = l > 0.f ? 1.f / l : 0.f;
         if (!qs.merge) {

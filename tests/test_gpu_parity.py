@@ -257,6 +257,52 @@ def test_bf16_block_small(Sq, Sk, Hq, Hkv, qo, ko, causal):
     compare(out.t, lse.t, ro, rl, BF16_OUT_TOL, BF16_LSE_TOL, "bf16 block")
 
 
+def score_dynamics_inputs(kind, Sq, Sk, H, seed):
+    """bf16 q, k, v whose scores stress the running max of the streaming
+    softmax: "growing" -- key norms rise along the sequence, so a row's max
+    climbs many times past the lazy-rescale threshold within one launch;
+    "negative" -- every score near -100 nats (exponentials against a zero
+    reference would underflow to 0); "sink" -- key 0 dominates every row by
+    about 60 nats, the rest of the row is negligible beside it.  v is
+    drawn at half scale: in a row dominated by one key the bf16 rounding of
+    the probabilities alone moves the output by up to 2^-9 max|v|, which for
+    unit-scale v (max about 5) is the whole 1e-2 tolerance; the stress is
+    on the scores."""
+    q, _, _ = make_qkv(S=Sq, H=H, D=128, seed=seed, dtype=torch.float32)
+    _, k, v = make_qkv(S=Sk, H=H, D=128, seed=seed + 1, dtype=torch.float32)
+    u = make_qkv(S=1, H=H, D=128, seed=seed + 2, dtype=torch.float32)[0]  # [1, H, D]
+    if kind == "growing":
+        q = 2.0 * q
+        k = k * (1.0 + 8.0 * torch.arange(Sk, dtype=torch.float32) / Sk)[:, None, None]
+    elif kind == "negative":
+        q = 3.0 * u + 0.5 * q
+        k = -3.0 * u + 0.5 * k
+    elif kind == "sink":
+        k = 0.3 * k
+        k[0] = 6.0 * u[0]
+        q = 0.3 * q + u
+    v = 0.5 * v
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("kind", ["growing", "negative", "sink"])
+@pytest.mark.parametrize("qo,ko,causal", [(0, 0, True), (1500, 0, True), (0, 0, False),
+                                          (0, 700, True)])
+def test_bf16_block_score_dynamics(kind, qo, ko, causal):
+    """Rows whose running max rises mid-launch (raise + rescale), rows far
+    below zero, a dominant first key, and rows with no visible key for the
+    first tiles (qo < ko) next to rows that have one."""
+    Sq, Sk, H = 1000, 2000, 2
+    announce(f"bf16 block fwd score dynamics {kind} qo={qo} ko={ko} causal={causal}")
+    q, k, v = score_dynamics_inputs(kind, Sq, Sk, H, seed=31)
+    out, lse = Guarded(Sq, H, 128), Guarded(H, Sq)
+    cp.cp_attn_block_fwd(*dev(q, k, v), out.t, lse.t, q_offset=qo, k_offset=ko, causal=causal)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    ro, rl = oracle_rows(q, k, v, None, causal=causal, q_offset=qo, k_offset=ko)
+    compare(out.t, lse.t, ro, rl, BF16_OUT_TOL, BF16_LSE_TOL, f"bf16 {kind}")
+
+
 def test_bf16_block_empty_kv():
     announce("bf16 block fwd Sk=0")
     q, k, v = make_qkv(S=130, H=2, D=128, dtype=torch.bfloat16)
