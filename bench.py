@@ -23,10 +23,13 @@ The CPU oracle is timed on a bounded sample of the ring share's rows.
 instead (striped: q, k, v permuted to striped order once, before timing);
 ``--part ring|ulysses|bwd|usp|usp_bwd`` times one share, the backward pass,
 or one rank of the USP hybrid (8-way Ulysses x 2-way ring), forward or
-backward.
+backward; ``--part merge|repack`` times the bandwidth-bound kernels alone
+(the log-sum-exp merges of a ring rank run as separate kernels, the Ulysses
+repacks of a rank) in GB/s against the HBM peak.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--part both|ring|ulysses|bwd|usp|usp_bwd]
+                    [--part both|ring|ulysses|bwd|usp|usp_bwd|merge|repack]
+                    [--merge-in-place]
                     [--layout zigzag|striped|contiguous]
                     [--rank r]
 """
@@ -444,16 +447,126 @@ def usp(args, cp, torch, dq, dku, dvu, stream):
     print(json.dumps(result))
 
 
+def merge_repack(args, cp, torch, dq, dku, dvu, stream):
+    """The bandwidth-bound kernels alone (one JSON line each run).
+
+    merge: the log-sum-exp merges of one ring rank at 128K (P = 8, zigzag)
+    when they run as separate kernels: 15 per step (17 computed chunk
+    pairs, the first result of each of the 2 query chunks is stored), each
+    folding an [8192, 32, 128] float32 block result and its [32, 8192] lse
+    into the running ones, out of place (or in place with --merge-in-place).
+    Algorithmic bytes: 12 per output element + 12 per (row, head).
+
+    repack: the Ulysses repacks of one rank at 128K (seq->head of q
+    [131072, 32, 128] and of k, v [131072, 8, 128] bf16, head->seq of the
+    float32 output), each reading and writing its rank's share once."""
+    from seeded_inputs import make_qkv
+    dev = "cuda:0"
+    if args.part == "merge":
+        rows, n_merge = S // (2 * P), 15
+        o1, o2, _ = make_qkv(S=rows, H=HQ, D=D, seed=11)
+        l1, l2, _ = make_qkv(S=HQ, H=rows, D=1, seed=12)
+        l1, l2 = 3.0 * l1[..., 0], 3.0 * l2[..., 0]
+        l1[:, ::97] = float("-inf")          # rows with no visible key on one side
+        l2[:, ::89] = float("-inf")
+        o1, o2, l1, l2 = (x.to(dev).contiguous() for x in (o1, o2, l1, l2))
+        if args.merge_in_place:
+            o, lse = o1, l1
+        else:
+            o, lse = torch.empty_like(o1), torch.empty_like(l1)
+
+        def step():
+            for _ in range(n_merge):
+                cp.cp_lse_merge(o1, l1, o2, l2, o, lse, stream=stream)
+
+        kind = cp.CP_KERNEL_MERGE
+        bytes_step = n_merge * (rows * HQ * D * 12 + rows * HQ * 12)
+        kernel = "lse_merge_kernel"
+        workload = (f"log-sum-exp merges of one zigzag ring rank at S=131072, P=8: {n_merge} "
+                    f"per step, each [{rows}, {HQ}, {D}] float32 + lse [{HQ}, {rows}], "
+                    + ("in place" if args.merge_in_place else "out of place"))
+        metric = "lse merge HBM GB/s + % of HBM peak, 8192x32x128 fp32 chunk"
+    else:
+        hp, hkp = HQ // P, HKV_ULY // P
+        ql = torch.empty(S, hp, D, device=dev, dtype=torch.bfloat16)
+        kl = torch.empty(S, hkp, D, device=dev, dtype=torch.bfloat16)
+        vl = torch.empty(S, hkp, D, device=dev, dtype=torch.bfloat16)
+        ol = torch.randn(S, hp, D, device=dev, dtype=torch.float32,
+                         generator=torch.Generator(device=dev).manual_seed(13))
+        out = torch.zeros(S, HQ, D, device=dev, dtype=torch.float32)   # head slice 0 written
+
+        def step():
+            cp.cp_seq_to_head(dq, P, ULY_RANK, y=ql, stream=stream)
+            cp.cp_seq_to_head(dku, P, ULY_RANK, y=kl, stream=stream)
+            cp.cp_seq_to_head(dvu, P, ULY_RANK, y=vl, stream=stream)
+            cp.cp_head_to_seq(ol, out, P, ULY_RANK, stream=stream)
+
+        kind = cp.CP_KERNEL_PERMUTE
+        bytes_step = 2 * (S * hp * D * 2 + 2 * S * hkp * D * 2 + S * hp * D * 4)
+        kernel = "unit_copy_kernel"
+        workload = ("Ulysses repacks of one rank at S=131072, P=8: seq->head of q "
+                    "[131072, 32, 128] and k, v [131072, 8, 128] bf16, head->seq of the "
+                    "float32 output [131072, 4, 128] into its head slice of [131072, 32, 128]")
+        metric = "Ulysses repack HBM GB/s + % of HBM peak, S=128K H=32/8 D=128"
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    cp.cp_timing_enable(True)
+    cp.cp_timing_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    k_ms, k_n = cp.cp_timing_read(kind)
+    cp.cp_timing_enable(False)
+    gbs = bytes_step * args.steps / (k_ms * 1e-3) / 1e9 if k_ms > 0 else None
+    result = {
+        "metric": metric,
+        "value": round(bytes_step * args.steps / elapsed / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if args.part == "merge" else "bf16+f32",
+        "data": "synthetic",
+        "config": {"workload": workload, "parts": args.part, "bytes_per_step": bytes_step},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel,
+            "achieved": round(gbs, 1) if gbs else None,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4) if gbs else None,
+            "traffic": None,
+            "launches": k_n,
+            "avg_launch_ms": round(k_ms / max(k_n, 1), 4),
+            "bytes_per_launch": bytes_step * args.steps / max(k_n, 1),
+        },
+    }
+    print(json.dumps(result))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--part", choices=["both", "ring", "ulysses", "bwd", "usp", "usp_bwd"],
+    ap.add_argument("--part", choices=["both", "ring", "ulysses", "bwd", "usp", "usp_bwd",
+                                       "merge", "repack"],
                     default="both",
                     help="bwd: time the backward pass of both shares instead; usp: one rank "
-                         "of the 8-way Ulysses x 2-way ring hybrid")
+                         "of the 8-way Ulysses x 2-way ring hybrid; merge / repack: the "
+                         "bandwidth-bound kernels alone (GB/s against the HBM peak)")
+    ap.add_argument("--merge-in-place", action="store_true",
+                    help="--part merge: fold into the running output in place")
     ap.add_argument("--layout", choices=["zigzag", "striped", "contiguous"], default="zigzag",
                     help="split of the ring share (striped: inputs permuted to striped order "
                          "once, before timing)")
@@ -535,6 +648,9 @@ def main():
 
     if args.part == "usp":
         usp(args, cp, torch, dq, dku, dvu, stream)
+        return
+    if args.part in ("merge", "repack"):
+        merge_repack(args, cp, torch, dq, dku, dvu, stream)
         return
     if args.part == "usp_bwd":
         usp_bwd(args, cp, torch, dq, dku, dvu, stream)
