@@ -316,19 +316,23 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
 #pragma unroll
     for (int sd = 0; sd < 8; ++sd)
         k_off[sd] = tile_off(l32, 2 * sd + hi);
-    // scores of sub-tile u, whose tile sits in stage ST
-    auto scores = [&](int u, f32x16 (&sc)[QB], auto st) {
-        const char LDS_AS *kt = stage_base<decltype(st)::value>() + (u & 1) * 32 * 256;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-            sc[qb] = f32x16{};
-        // all eight K fragments are requested before the first MFMA, so the
-        // LDS latency is paid once per half tile rather than once per MFMA
-        bf16x8 kf[8];
+    // K fragments of the next half tile to be scored.  They are requested
+    // one half tile ahead, right after the V fragments, so they land while
+    // the softmax runs instead of stalling the score MFMAs: for the first
+    // half of a tile from the same tile, for the second half from the next
+    // tile, whose loads every wavefront waited for before this tile's
+    // barrier (its stage is overwritten only after the next tile's one).
+    bf16x8 kf[8];
+    auto load_k = [&](const char LDS_AS *kt) {
 #pragma unroll
         for (int sd = 0; sd < 8; ++sd)
             kf[sd] = lds_b128(kt, k_off[sd]);
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    // S^T of the half tile whose K fragments are in kf
+    auto scores = [&](f32x16 (&sc)[QB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+            sc[qb] = f32x16{};
 #pragma unroll
         for (int sd = 0; sd < 8; ++sd) {
 #pragma unroll
@@ -380,9 +384,9 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             f32x16 cur[QB];
-            scores(2 * t + half, cur, st);
-            // V fragments of this half tile, requested now: they land while
-            // the softmax runs
+            scores(cur);
+            // V fragments of this half tile and K fragments of the next one,
+            // requested now: they land while the softmax runs
             const char LDS_AS *vt = stage_base<ST>() + kTileBytes;
             bf16x8 vfr[2][4];
 #pragma unroll
@@ -390,6 +394,10 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
                     vfr[kh][db] = v_frag(vt, 2 * half + kh, db);
+            if (half == 0)
+                load_k(stage_base<ST>() + 32 * 256);
+            else if (t + 1 < n_tiles)
+                load_k(stage_base<(ST + 1) % 3>());
             __builtin_amdgcn_sched_barrier(0);
             const int64_t key0 = r.key0 + half * 32;      // first key of the half tile
             const bool need_mask = (key0 + 32 > kv_len) ||
@@ -493,6 +501,13 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
     using I2 = std::integral_constant<int, 2>;
     issue(0, I0{});
     issue(1, I1{});
+    // the first half tile's K fragments (the loop's barriers then keep one
+    // half tile ahead)
+    if (n_tiles > 0) {
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        load_k(stage_base<0>());
+    }
     for (int t = 0; t < n_tiles; t += 3) {
         tile_step(t, I0{});
         if (t + 1 >= n_tiles)
