@@ -426,7 +426,7 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
             // the wavefront takes the exact path: half-tile max, lazy raise,
             // rescale, exponentials again.
             bf16x8 pf[QB][2];
-            float rs[QB];
+            float rs[QB], rs2[QB][2];
             auto exps = [&](bool first) {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
@@ -441,9 +441,14 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
                         for (int j = 0; j < 8; ++j) {
                             const float p = __builtin_amdgcn_exp2f(
                                 __builtin_fmaf(cur[qb][8 * kh + j], scale_log2, -m_use));
-                            rs[qb] = (kh == 0 && j == 0) ? p : rs[qb] + p;
+                            // two interleaved partial sums (keys of even / odd j)
+                            if (kh == 0 && j < 2)
+                                rs2[qb][j] = p;
+                            else
+                                rs2[qb][j & 1] += p;
                             pf[qb][kh][j] = (__bf16)p;
                         }
+                    rs[qb] = rs2[qb][0] + rs2[qb][1];
                 }
             };
             exps(true);
