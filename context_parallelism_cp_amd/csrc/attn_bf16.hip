@@ -39,7 +39,9 @@
 //     half tiles crossing it (or a ragged end) compare absolute positions.
 //   * Workgroups are mapped XCD-aware: the heads of a launch are spread over
 //     the 8 XCDs, a head's tiles stay on its XCD(s), and every XCD walks its
-//     tiles heaviest-first (most visible keys first).
+//     tiles heaviest-first (most visible keys first).  With a multiple of 8
+//     heads an XCD takes its heads one after another, so its CUs stream the
+//     same head's K/V tiles through its L2 at the same time.
 //   * The epilogue either writes (out, lse) or folds the block result into
 //     the (out, lse) already stored (log-sum-exp merge, handbook section
 //     "Ring Attention：KV 沿环传一圈").
@@ -207,9 +209,8 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
         const int bid = blockIdx.x;
         if (tm.xcd_mode == 1) {
             const int x = bid % kXcds, s = bid / kXcds;
-            const int hpx = a.Hq / kXcds;
-            h = x + kXcds * (s % hpx);
-            tp = s / hpx;
+            h = x + kXcds * (s / tm.total);
+            tp = s % tm.total;
         } else if (tm.xcd_mode == 2) {
             const int x = bid % kXcds, s = bid / kXcds;
             const int xph = kXcds / a.Hq;
