@@ -29,12 +29,15 @@
 //     identically for P and V, and the V^T fragment is two transpose reads of
 //     the row-major V tile.  Each lane keeps one query, so the rescale by
 //     exp2(m_old - m_new) is a per-lane scalar.
-//   * Per 32-key half tile, all K fragments and then all V fragments are
-//     requested from LDS before their first use, so the LDS latency is paid
-//     once per phase rather than once per MFMA.
+//   * Per 32-key half tile, all V fragments are requested from LDS before
+//     their first use, and the K fragments one half tile ahead, so the LDS
+//     latency lands during the softmax rather than in front of the MFMAs.
 //   * The running max is only raised when a half tile's max exceeds it by
 //     more than 2^8 (in base 2), so the 64-register rescale of O is rare; the
-//     exponentials stay <= 2^8 and the final O / l is unchanged.
+//     exponentials stay <= 2^8 and the final O / l is unchanged.  The
+//     exponentials are taken against the running max first; the half tile's
+//     max is computed only when some lane's partial sum reaches 2^8 (or the
+//     row has no finite max yet), so the common path has no max at all.
 //   * Half tiles strictly below the causal diagonal run without the mask;
 //     half tiles crossing it (or a ragged end) compare absolute positions.
 //   * Workgroups are mapped XCD-aware: the heads of a launch are spread over
