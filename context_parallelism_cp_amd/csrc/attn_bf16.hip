@@ -10,8 +10,12 @@
 //
 // Work decomposition
 //   * A workgroup of 8 wavefronts (two per SIMD) owns BM = 256 query rows of
-//     one head; each wavefront owns 32 rows.  The two wavefronts of a SIMD
-//     overlap one's matrix work with the other's softmax.
+//     one head; each wavefront owns 32 rows.  With grouped-query attention,
+//     when the query heads per KV head (pack) divide 8, the workgroup owns
+//     256 / pack rows of all pack heads of one KV head instead (8 / pack
+//     wavefronts per head), so one K/V stream through LDS serves them all.
+//     The two wavefronts of a SIMD overlap one's matrix work with the
+//     other's softmax.
 //   * Keys stream through LDS BN = 64 at a time in a 3-stage ring filled by
 //     direct buffer->LDS 16-byte loads (no staging registers); the buffer
 //     resource of a tile ends at the segment's last row, so rows past it read
@@ -90,6 +94,7 @@ struct TileMap {
     int32_t use_order;                  // order[] valid (total <= kMaxOrder)
     int32_t xcd_mode;                   // 0 linear, 1 Hq % 8 == 0, 2 8 % Hq == 0
     int32_t slots;                      // tile positions walked per XCD lane
+    int32_t pack;                       // query heads per workgroup (they share one KV head)
     uint16_t order[kMaxOrder];          // tile positions, heaviest first
 };
 
@@ -206,26 +211,33 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    // ---- which (head, row tile) this workgroup owns
-    int h, tp;
+    // ---- which (head group, row tile) this workgroup owns.  A head group is
+    // `pack` consecutive query heads sharing one KV head; each head gets
+    // kWaves / pack wavefronts, i.e. bm = 32 * kWaves / pack rows.
+    const int pack = tm.pack;
+    const int wph = kWaves / pack;                 // wavefronts per query head
+    const int bm = 32 * wph;                       // rows per workgroup
+    const int n_hg = a.Hq / pack;
+    int hg, tp;
     {
         const int bid = blockIdx.x;
         if (tm.xcd_mode == 1) {
             const int x = bid % kXcds, s = bid / kXcds;
-            h = x + kXcds * (s / tm.total);
+            hg = x + kXcds * (s / tm.total);
             tp = s % tm.total;
         } else if (tm.xcd_mode == 2) {
             const int x = bid % kXcds, s = bid / kXcds;
-            const int xph = kXcds / a.Hq;
-            h = x % a.Hq;
-            tp = s * xph + x / a.Hq;
+            const int xph = kXcds / n_hg;
+            hg = x % n_hg;
+            tp = s * xph + x / n_hg;
         } else {
-            h = bid / tm.total;
+            hg = bid / tm.total;
             tp = bid % tm.total;
         }
-        if (h >= a.Hq || tp >= tm.total)
+        if (hg >= n_hg || tp >= tm.total)
             return;
     }
+    const int h = hg * pack + wave / wph;          // this wavefront's query head
     int tile_lin;
     if (tm.use_order) {
         tile_lin = tm.order[tp];
@@ -239,8 +251,8 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
     int tile = tile_lin - tm.start[s];
     if (!tm.use_order && a.causal)   // without the table: later rows (more keys) first
         tile = (tm.start[s + 1] - tm.start[s]) - 1 - tile;
-    const int64_t tile_row0 = (int64_t)tile * BM;
-    const int g = h / (a.Hq / a.Hkv);
+    const int64_t tile_row0 = (int64_t)tile * bm;
+    const int g = h / (a.Hq / a.Hkv);              // the same for every wavefront
 
     const __bf16 *qg = (const __bf16 *)a.q;
     const int64_t q_stride = (int64_t)a.Hq * HD;
@@ -253,7 +265,7 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
     int row_off[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
-        row_off[qb] = wave * 32 * QB + qb * 32 + l32;
+        row_off[qb] = (wave % wph) * 32 * QB + qb * 32 + l32;
 
     // Q^T fragments: B operand of step sd holds dims 16*sd + 8*hi + [0, 8).
     bf16x8 qf[QB][8];
@@ -273,7 +285,7 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
 
     // ---- the tile stream: every KV segment's tiles up to the causal bound
     const int64_t first_pos = qs.pos0 + tile_row0;
-    const int64_t last_pos = qs.pos0 + min(tile_row0 + BM, qs.len) - 1;
+    const int64_t last_pos = qs.pos0 + min(tile_row0 + bm, qs.len) - 1;
     int seg_tiles[2] = {0, 0};
     for (int kv_i = 0; kv_i < qs.n_kv; ++kv_i) {
         const KvSeg &kv = qs.kv[kv_i];
@@ -581,11 +593,11 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
     }
 }
 
-// Visible keys of the last row of row tile `tile` of segment `s`.
-int64_t tile_work(const AttnLaunch &a, int s, int tile)
+// Visible keys of the last row of row tile `tile` (bm rows) of segment `s`.
+int64_t tile_work(const AttnLaunch &a, int s, int tile, int bm)
 {
     const QSeg &q = a.qs[s];
-    const int64_t last = q.pos0 + std::min<int64_t>((int64_t)(tile + 1) * BM, q.len) - 1;
+    const int64_t last = q.pos0 + std::min<int64_t>((int64_t)(tile + 1) * bm, q.len) - 1;
     int64_t w = 0;
     for (int k = 0; k < q.n_kv; ++k) {
         const KvSeg &kv = q.kv[k];
@@ -599,13 +611,20 @@ int64_t tile_work(const AttnLaunch &a, int s, int tile)
 hipError_t launch_attn_bf16(const AttnLaunch &a, hipStream_t stream)
 {
     TileMap tm{};
+    // Query heads that share a KV head go into one workgroup when their
+    // number divides the wavefront count: the K/V tiles in LDS then serve
+    // all of them (one L2 stream instead of one per query head).
+    const int group = a.Hkv > 0 ? a.Hq / a.Hkv : 1;
+    tm.pack = (group >= 1 && group <= kWaves && kWaves % group == 0) ? group : 1;
+    const int bm = BM / tm.pack;
+    const int n_hg = a.Hq / tm.pack;
     int64_t total = 0;
     for (int s = 0; s < a.n_q; ++s) {
         tm.start[s] = (int32_t)total;
-        total += (a.qs[s].len + BM - 1) / BM;
+        total += (a.qs[s].len + bm - 1) / bm;
     }
     tm.start[a.n_q] = (int32_t)total;
-    if (total == 0 || a.Hq == 0)
+    if (total == 0 || n_hg == 0)
         return hipSuccess;
     tm.total = (int32_t)total;
     tm.use_order = total <= kMaxOrder ? 1 : 0;
@@ -615,23 +634,23 @@ hipError_t launch_attn_bf16(const AttnLaunch &a, hipStream_t stream)
         w.reserve(total);
         for (int s = 0; s < a.n_q; ++s)
             for (int t = tm.start[s]; t < tm.start[s + 1]; ++t)
-                w.push_back({-tile_work(a, s, t - tm.start[s]), -t});
+                w.push_back({-tile_work(a, s, t - tm.start[s], bm), -t});
         std::sort(w.begin(), w.end());
         for (int64_t i = 0; i < total; ++i)
             tm.order[i] = (uint16_t)(-w[i].second);
     }
     int64_t grid;
-    if (a.Hq % kXcds == 0) {
+    if (n_hg % kXcds == 0) {
         tm.xcd_mode = 1;
-        grid = total * a.Hq;
-    } else if (kXcds % a.Hq == 0) {
+        grid = total * n_hg;
+    } else if (kXcds % n_hg == 0) {
         tm.xcd_mode = 2;
-        const int xph = kXcds / a.Hq;
+        const int xph = kXcds / n_hg;
         const int64_t slots = (total + xph - 1) / xph;
         grid = slots * kXcds;
     } else {
         tm.xcd_mode = 0;
-        grid = total * a.Hq;
+        grid = total * n_hg;
     }
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
     hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a, tm,
