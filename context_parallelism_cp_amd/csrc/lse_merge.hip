@@ -75,8 +75,10 @@ hipError_t launch_lse_merge(const float *o1, const float *lse1, const float *o2,
         return hipSuccess;
     const int64_t groups_per_block = (int64_t)G * (kThreads / 64);
     int64_t blocks = (n_groups + groups_per_block - 1) / groups_per_block;
-    if (blocks > 4096)
-        blocks = 4096;  // grid-stride beyond this: 16 blocks per CU
+    // one loop trip per wavefront up to 2^20 workgroups (grid-stride
+    // beyond): measured faster than 16 or 4 workgroups per CU looping
+    if (blocks > (1 << 20))
+        blocks = 1 << 20;
     hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                        (const f32x4 *)o1, lse1, (const f32x4 *)o2, lse2, (f32x4 *)o, lse, Sq,
                        H, L, G, n_groups);
