@@ -244,6 +244,12 @@ def oracle_rows(q, k, v, rows, **kw):
     (257, 300, 2, 1, 0, 200, True),    # rows 0..198 see no key
     (64, 1000, 8, 2, 999, 0, True),
     (1, 1, 1, 1, 5, 5, True),
+    # query heads per KV head 8 (one wavefront per head in a workgroup), 2,
+    # and 16 (more than a workgroup's wavefronts: one head per workgroup)
+    (300, 517, 8, 1, 400, 100, True),
+    (130, 700, 16, 2, 50, 0, True),
+    (97, 333, 6, 3, 0, 0, False),
+    (257, 300, 16, 1, 0, 200, True),
 ])
 def test_bf16_block_small(Sq, Sk, Hq, Hkv, qo, ko, causal):
     announce(f"bf16 block fwd Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} qo={qo} ko={ko} causal={causal}")
