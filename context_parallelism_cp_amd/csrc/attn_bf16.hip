@@ -608,6 +608,10 @@ int64_t tile_work(const AttnLaunch &a, int s, int tile, int bm)
 
 }  // namespace
 
+// The launch arguments travel in the kernel-argument segment (4 KiB).
+static_assert(sizeof(AttnLaunch) + sizeof(TileMap) + sizeof(float) <= 4096,
+              "attention kernel arguments exceed the kernel-argument segment");
+
 hipError_t launch_attn_bf16(const AttnLaunch &a, hipStream_t stream)
 {
     TileMap tm{};
