@@ -1,0 +1,65 @@
+"""Host-side logic of bench.py, on the CPU: the FLOP convention of the
+handbook's zigzag work model (section "之字形切分": a diagonal chunk pair
+counts half), its agreement with the library's ring plan, the one-GPU
+guard, and the traffic figure's tie to the kernel source it was taken for.
+"""
+import hashlib
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_headline_flop_counts():
+    # one zigzag rank of 8 at 128K, 32 heads, D = 128: 16 chunk units of
+    # 8192^2 pairs (2 per ring step) = 2^44; the Ulysses share (4 heads over
+    # the whole causal sequence) is the same 2^44
+    assert bench.ring_share_flop(131072, 32, 128, 8, "zigzag", 0) == 2.0 ** 44
+    assert bench.ulysses_share_flop(131072, 4, 128) == 2.0 ** 44
+    # the whole layer is P times a balanced share
+    assert 8 * bench.ring_share_flop(131072, 32, 128, 8, "striped") == 2.0 ** 47
+    # contiguous ranks do r + 1/2 units: the 64K P = 4 case, rank 3 vs rank 0
+    heavy = bench.ring_share_flop(65536, 32, 128, 4, "contiguous", 3)
+    light = bench.ring_share_flop(65536, 32, 128, 4, "contiguous", 0)
+    assert heavy / light == 7.0
+    assert heavy / bench.ring_share_flop(65536, 32, 128, 4, "zigzag", 3) == 1.75
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "striped", "contiguous"])
+@pytest.mark.parametrize("rank", [0, 3, 7])
+def test_plan_flop_matches_closed_form(layout, rank):
+    import context_parallelism_cp_amd as cp
+    assert bench.plan_flop(cp, 131072, 32, 128, 8, layout, rank) == \
+        bench.ring_share_flop(131072, 32, 128, 8, layout, rank)
+
+
+def test_plan_flop_padded_length_counts_real_rows_only():
+    import context_parallelism_cp_amd as cp
+    full = bench.plan_flop(cp, 131072, 32, 128, 8, "zigzag", 0)
+    short = bench.plan_flop(cp, 131071, 32, 128, 8, "zigzag", 0)
+    assert 0.999 * full < short < full
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_recorded_traffic_follows_the_kernel_source(tmp_path):
+    src = tmp_path / "kernel.hip"
+    src.write_text("// some kernel\n")
+    digest = hashlib.sha256(src.read_bytes()).hexdigest()
+    prof = tmp_path / "traffic.md"
+    prof.write_text(f"# summary\n\ntraffic_bytes_per_launch: 1234\nkernel_source_sha256: {digest}\n")
+    assert bench.recorded_traffic(str(prof), str(src)) == 1234.0
+    src.write_text("// the kernel changed\n")
+    assert bench.recorded_traffic(str(prof), str(src)) is None
+    assert bench.recorded_traffic(str(tmp_path / "missing.md"), str(src)) is None
