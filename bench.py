@@ -76,6 +76,24 @@ def plan_flop(cp, S, H, D, P, layout, rank):
     return 4.0 * D * H * units
 
 
+def plan_flop_exact(cp, S, H, D, P, layout, rank):
+    """4*D*H per visible (q, k) pair counted exactly: a diagonal pair of
+    lq query and lk key rows starting at the same position has
+    sum_i min(i + 1, lk) visible pairs (C(C+1)/2 for C x C) instead of
+    half.  None for the striped split, whose diagonal pairs sit at local
+    offsets."""
+    if layout == "striped":
+        return None
+    units = 0.0
+    for (_r, _t, _qc, _kc, _qo, _ko, lq, lk, kind) in cp.cp_ring_plan(S, P, layout, rank, True):
+        if kind == cp.CP_PAIR_FULL:
+            units += lq * lk
+        elif kind == cp.CP_PAIR_DIAG:
+            m = min(lq, lk)
+            units += m * (m + 1) / 2.0 + (lq - m) * lk
+    return 4.0 * D * H * units
+
+
 def ulysses_share_flop(S, H_local, D):
     """Full-sequence causal attention of H_local heads, diagonal counted half."""
     return 4.0 * D * H_local * S * S / 2.0
@@ -627,10 +645,16 @@ def main():
     uly_out = torch.zeros(S, HQ, D, device=dev, dtype=torch.float32)
     stream = torch.cuda.current_stream()
 
+    ring_done = []          # per timed step: an event after the ring share
+
     def step():
         if args.part in ("both", "ring"):
             cp.cp_ring_fwd(rq, rk, rv, P, args.layout, args.rank, out=ring_out, lse=ring_lse,
                            stream=stream, seq_len=seq)
+            if ring_done is not None and len(ring_done) < args.steps and timing[0]:
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record(stream)
+                ring_done.append(ev)
         if args.part in ("both", "ulysses"):
             cp.cp_seq_to_head(dq, P, ULY_RANK, y=ql, stream=stream)
             cp.cp_seq_to_head(dku, P, ULY_RANK, y=kl, stream=stream)
@@ -660,18 +684,28 @@ def main():
                  ring_out, ring_lse, stream, dq)
         return
 
+    timing = [False]
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
+    # events on the launch stream around every step (no host synchronisation
+    # inside the timed region) give the per-step median
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    timing[0] = True
     cp.cp_timing_enable(True)
     cp.cp_timing_reset()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    step_ev[0].record(stream)
+    for i in range(args.steps):
         step()
+        step_ev[i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(args.steps))
+    ring_ms = (sorted(step_ev[i].elapsed_time(ring_done[i]) for i in range(args.steps))
+               if len(ring_done) == args.steps else None)
     attn_ms, attn_n = cp.cp_timing_read(cp.CP_KERNEL_ATTN_BF16)
     perm_ms, perm_n = cp.cp_timing_read(cp.CP_KERNEL_PERMUTE)
     cp.cp_timing_enable(False)
@@ -680,6 +714,10 @@ def main():
                  if args.part in ("both", "ring") else 0.0)
     flop_uly = ulysses_share_flop(S, hp, D) if args.part in ("both", "ulysses") else 0.0
     flop_step = flop_ring + flop_uly
+    ring_exact = (plan_flop_exact(cp, seq, HQ, D, P, args.layout, args.rank)
+                  if args.part in ("both", "ring") else 0.0)
+    flop_exact = (None if ring_exact is None else ring_exact + (
+        4.0 * D * hp * S * (S + 1) / 2.0 if args.part in ("both", "ulysses") else 0.0))
     ms_step = elapsed * 1e3 / args.steps
     value = flop_step * args.steps / elapsed / 1e12
     attn_tflops = flop_step * args.steps / (attn_ms * 1e-3) / 1e12 if attn_ms > 0 else None
@@ -716,7 +754,17 @@ def main():
             "S": S, "Hq": HQ, "Hkv_ring": HQ, "Hkv_ulysses": HKV_ULY, "D": D, "P": P,
             "flop_per_step": flop_step,
             "flop_convention": "4*D*Hq per visible (q,k) pair, diagonal chunk counted half",
+            "flop_per_step_exact": flop_exact,
             "inputs_sha256": sha256_of(q[:4096], k[:4096], v[:4096]),
+        },
+        "timing": {
+            "ms_per_step_median": round(step_ms[len(step_ms) // 2], 3),
+            "ms_per_step_min": round(step_ms[0], 3),
+            "ring_ms_median": round(ring_ms[len(ring_ms) // 2], 3) if ring_ms else None,
+            "value_exact_count": (round(flop_exact * args.steps / elapsed / 1e12, 2)
+                                  if flop_exact else None),
+            "source": "HIP events on the launch stream around each timed step (the ring "
+                      "share: cp_ring_fwd with its fused merges)",
         },
         "roofline": {
             "bound": "mfma",

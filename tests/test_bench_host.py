@@ -63,3 +63,16 @@ def test_recorded_traffic_follows_the_kernel_source(tmp_path):
     src.write_text("// the kernel changed\n")
     assert bench.recorded_traffic(str(prof), str(src)) is None
     assert bench.recorded_traffic(str(tmp_path / "missing.md"), str(src)) is None
+
+
+def test_exact_count_closed_forms():
+    import context_parallelism_cp_amd as cp
+    # contiguous P = 4 on 32 tokens, rank 3: three full 8 x 8 blocks and one
+    # causal 8 x 8 diagonal block with 8 * 9 / 2 visible pairs
+    assert bench.plan_flop_exact(cp, 32, 1, 1, 4, "contiguous", 3) == 4.0 * (3 * 64 + 36)
+    # zigzag rank of 8 at 128K: 15 full 8192^2 chunk pairs and 2 diagonal
+    # ones, exceeding the half-diagonal convention by 2 * 8192 / 2 pairs
+    exact = bench.plan_flop_exact(cp, 131072, 32, 128, 8, "zigzag", 0)
+    half = bench.plan_flop(cp, 131072, 32, 128, 8, "zigzag", 0)
+    assert exact - half == 4.0 * 128 * 32 * 8192
+    assert bench.plan_flop_exact(cp, 131072, 32, 128, 8, "striped", 0) is None
