@@ -149,10 +149,20 @@ def cpu_baseline(q, k, v, budget_s=12.0, max_rows=512):
         done_rows.extend(int(p) for p in rows)
         if t_total >= budget_s:
             break
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": flop / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": (f"{len(done_rows)} seeded query rows of ring rank {RING_RANK}'s share "
                    f"(S={S}, P={P} zigzag) x all {HQ} heads against every visible key, "
