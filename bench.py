@@ -661,7 +661,7 @@ def main():
         if args.part in ("both", "ring"):
             cp.cp_ring_fwd(rq, rk, rv, P, args.layout, args.rank, out=ring_out, lse=ring_lse,
                            stream=stream, seq_len=seq)
-            if ring_done is not None and len(ring_done) < args.steps and timing[0]:
+            if timing[0] and len(ring_done) < args.steps:
                 ev = torch.cuda.Event(enable_timing=True)
                 ev.record(stream)
                 ring_done.append(ev)
