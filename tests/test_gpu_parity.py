@@ -232,6 +232,35 @@ def test_merge_against_oracle(Sq, H, D):
     compare(d1, dl1, ro, rl, F32_TOL, F32_TOL, "merge in place")
 
 
+@pytest.mark.parametrize("Sq,H", [(8192, 32), (131072, 66)])
+def test_merge_full_size_sampled(Sq, H):
+    """The merge at the size a ring rank folds per step (8192 rows x 32
+    heads, one loop trip per wavefront) and past the grid's cap (131072 x 66
+    (row, head) groups, so wavefronts loop), out of place and in place;
+    seeded sampled rows against the oracle's merge of the same rows (the
+    merge is row-independent)."""
+    D = 128
+    announce(f"lse merge full size Sq={Sq} H={H} D={D} (sampled rows)")
+    g = torch.Generator(device=DEV).manual_seed(Sq + H)
+    o1 = torch.randn(Sq, H, D, device=DEV, generator=g)
+    o2 = torch.randn(Sq, H, D, device=DEV, generator=g)
+    l1 = torch.randn(H, Sq, device=DEV, generator=g) * 4
+    l2 = torch.randn(H, Sq, device=DEV, generator=g) * 4
+    l1[:, ::97] = -float("inf")
+    l2[:, ::89] = -float("inf")
+    rows = sample_rows(Sq, 48, seed=Sq).to(DEV)
+    ref_in = [t.cpu() for t in (o1[rows], l1[:, rows], o2[rows], l2[:, rows])]
+    ro, rl = OA.lse_merge(*ref_in)
+    out, lse = torch.empty_like(o1), torch.empty_like(l1)
+    cp.cp_lse_merge(o1, l1, o2, l2, out, lse)
+    torch.cuda.synchronize()
+    compare(out[rows], lse[:, rows], ro, rl, F32_TOL, F32_TOL, "merge full size")
+    del out, lse
+    cp.cp_lse_merge(o1, l1, o2, l2, o1, l1)     # in place
+    torch.cuda.synchronize()
+    compare(o1[rows], l1[:, rows], ro, rl, F32_TOL, F32_TOL, "merge full size in place")
+
+
 # ------------------------------------------------------------------ bf16
 def oracle_rows(q, k, v, rows, **kw):
     return native.attention_rows(q, k, v, rows=rows, **kw)
