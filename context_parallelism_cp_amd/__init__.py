@@ -115,24 +115,70 @@ def _dtype_code(t) -> int:
     raise CpError(CP_ERR_UNSUPPORTED, f"dtype {t.dtype} is not supported")
 
 
-def _dense(*ts):
-    for t in ts:
+def _need(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise CpError(CP_ERR_SHAPE, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _checked(ref, *specs):
+    """Check every tensor argument before the library is called.
+
+    ``ref`` is the tensor whose dtype and device the others follow (q, or
+    dout for cp_attn_bwd_dvec, or x for the repacks).  Each spec is
+    ``(tensor, shape, kind, name)``: ``shape`` the exact shape (None: any),
+    ``kind`` "in" (ref's dtype, which must be bfloat16 or float32), "f32"
+    (float32), "same" (ref's dtype, any element size) or "u8" (a byte
+    workspace).  Every tensor must be dense and live on ref's GPU.  The C
+    side receives only pointers and sizes, so a wrong buffer would otherwise
+    be read or written out of bounds by the kernels."""
+    import torch
+    for t, shape, kind, name in specs:
+        if not torch.is_tensor(t):
+            raise CpError(CP_ERR_NULL, f"{name} must be a torch tensor")
+        if shape is not None:
+            _need(t, shape, name)
+    want = {"in": ref.dtype, "same": ref.dtype, "f32": torch.float32, "u8": torch.uint8}
+    for t, shape, kind, name in specs:
+        if kind == "in" and t.dtype not in (torch.bfloat16, torch.float32):
+            raise CpError(CP_ERR_UNSUPPORTED, f"{name}: dtype {t.dtype} is not supported")
+        if t.dtype != want[kind]:
+            raise CpError(CP_ERR_UNSUPPORTED,
+                          f"{name} must have dtype {want[kind]}, got {t.dtype}")
         if not t.is_contiguous():
-            raise CpError(CP_ERR_ALIGN, "tensors must be contiguous")
+            raise CpError(CP_ERR_ALIGN, f"{name} must be contiguous")
+    if ref.device.type != "cuda":
+        raise CpError(CP_ERR_UNSUPPORTED, f"tensors must live on a GPU, got {ref.device}")
+    for t, shape, kind, name in specs:
+        if t.device != ref.device:
+            raise CpError(CP_ERR_UNSUPPORTED,
+                          f"{name} must be on {ref.device} like the inputs, got {t.device}")
 
 
 # ------------------------------------------------------------------ entry points
+def _dims(t, n, name):
+    """The sizes of a tensor that must have n dimensions."""
+    import torch
+    if not torch.is_tensor(t):
+        raise CpError(CP_ERR_NULL, f"{name} must be a torch tensor")
+    if t.dim() != n:
+        raise CpError(CP_ERR_SHAPE, f"{name} must have {n} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _f32(shape, ref):
+    import torch
+    return torch.empty(*shape, device=ref.device, dtype=torch.float32)
+
+
 def cp_attn_block_fwd(q, k, v, out=None, lse=None, q_offset: int = 0, k_offset: int = 0,
                       causal: bool = True, stream=None):
     """out [Sq,Hq,D] f32 and lse [Hq,Sq] f32 of q [Sq,Hq,D] against k, v [Sk,Hkv,D]."""
-    import torch
-    Sq, Hq, D = q.shape
-    Sk, Hkv, _ = k.shape
-    if out is None:
-        out = torch.empty(Sq, Hq, D, device=q.device, dtype=torch.float32)
-    if lse is None:
-        lse = torch.empty(Hq, Sq, device=q.device, dtype=torch.float32)
-    _dense(q, k, v, out, lse)
+    Sq, Hq, D = _dims(q, 3, "q")
+    Sk, Hkv, _ = _dims(k, 3, "k")
+    out = _f32((Sq, Hq, D), q) if out is None else out
+    lse = _f32((Hq, Sq), q) if lse is None else lse
+    _checked(q, (q, None, "in", "q"), (k, (Sk, Hkv, D), "in", "k"), (v, (Sk, Hkv, D), "in", "v"),
+             (out, (Sq, Hq, D), "f32", "out"), (lse, (Hq, Sq), "f32", "lse"))
     _check(lib.cp_attn_block_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                  lse.data_ptr(), Sq, Sk, Hq, Hkv, D, q_offset, k_offset,
                                  int(bool(causal)), _dtype_code(q), _stream(q, stream)))
@@ -142,12 +188,12 @@ def cp_attn_block_fwd(q, k, v, out=None, lse=None, q_offset: int = 0, k_offset: 
 def cp_lse_merge(o1, lse1, o2, lse2, o=None, lse=None, stream=None):
     """Log-sum-exp merge; o may be o1 and lse may be lse1 (in place)."""
     import torch
-    Sq, H, D = o1.shape
-    if o is None:
-        o = torch.empty_like(o1)
-    if lse is None:
-        lse = torch.empty_like(lse1)
-    _dense(o1, lse1, o2, lse2, o, lse)
+    Sq, H, D = _dims(o1, 3, "o1")
+    o = torch.empty_like(o1) if o is None else o
+    lse = _f32((H, Sq), o1) if lse is None else lse
+    _checked(o1, (o1, None, "f32", "o1"), (lse1, (H, Sq), "f32", "lse1"),
+             (o2, (Sq, H, D), "f32", "o2"), (lse2, (H, Sq), "f32", "lse2"),
+             (o, (Sq, H, D), "f32", "o"), (lse, (H, Sq), "f32", "lse"))
     _check(lib.cp_lse_merge(o1.data_ptr(), lse1.data_ptr(), o2.data_ptr(), lse2.data_ptr(),
                             o.data_ptr(), lse.data_ptr(), Sq, H, D, _stream(o1, stream)))
     return o, lse
@@ -167,11 +213,6 @@ def _ring_rows(S: int, P: int, lay: int, rank: int):
     return rows_in, (rows_in if rank < 0 else Sp // max(P, 1))
 
 
-def _need(t, shape, name):
-    if tuple(t.shape) != tuple(shape):
-        raise CpError(CP_ERR_SHAPE, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
-
-
 def cp_ring_fwd(q, k, v, P: int, layout="zigzag", rank: int = -1, causal: bool = True,
                 out=None, lse=None, stream=None, seq_len=None):
     """Ring attention over P virtual ranks (rank=-1: all, in the inputs'
@@ -179,22 +220,16 @@ def cp_ring_fwd(q, k, v, P: int, layout="zigzag", rank: int = -1, causal: bool =
     rank's share in its local order).  seq_len: the real length when the
     split does not divide it (striped tensors then hold the padded length;
     padding rows of the output come back as (0, -inf))."""
-    import torch
-    _, Hq, D = q.shape
-    _, Hkv, _ = k.shape
+    _, Hq, D = _dims(q, 3, "q")
+    _, Hkv, _ = _dims(k, 3, "k")
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
     S = q.shape[0] if seq_len is None else int(seq_len)
     rows_in, rows = _ring_rows(S, P, lay, rank)
-    _need(q, (rows_in, Hq, D), "q")
-    _need(k, (rows_in, Hkv, D), "k")
-    _need(v, (rows_in, Hkv, D), "v")
-    if out is None:
-        out = torch.empty(rows, Hq, D, device=q.device, dtype=torch.float32)
-    if lse is None:
-        lse = torch.empty(Hq, rows, device=q.device, dtype=torch.float32)
-    _need(out, (rows, Hq, D), "out")
-    _need(lse, (Hq, rows), "lse")
-    _dense(q, k, v, out, lse)
+    out = _f32((rows, Hq, D), q) if out is None else out
+    lse = _f32((Hq, rows), q) if lse is None else lse
+    _checked(q, (q, (rows_in, Hq, D), "in", "q"), (k, (rows_in, Hkv, D), "in", "k"),
+             (v, (rows_in, Hkv, D), "in", "v"), (out, (rows, Hq, D), "f32", "out"),
+             (lse, (Hq, rows), "f32", "lse"))
     _check(lib.cp_ring_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            lse.data_ptr(), S, Hq, Hkv, D, P, lay, rank, int(bool(causal)),
                            _dtype_code(q), _stream(q, stream)))
@@ -203,11 +238,10 @@ def cp_ring_fwd(q, k, v, P: int, layout="zigzag", rank: int = -1, causal: bool =
 
 def cp_attn_bwd_dvec(out, dout, dvec=None, stream=None):
     """dvec[h][i] = sum_d dout[i][h][d] * out[i][h][d] (float32 [Hq][Sq])."""
-    import torch
-    Sq, Hq, D = out.shape
-    if dvec is None:
-        dvec = torch.empty(Hq, Sq, device=out.device, dtype=torch.float32)
-    _dense(out, dout, dvec)
+    Sq, Hq, D = _dims(out, 3, "out")
+    dvec = _f32((Hq, Sq), dout) if dvec is None else dvec
+    _checked(dout, (dout, (Sq, Hq, D), "in", "dout"), (out, (Sq, Hq, D), "f32", "out"),
+             (dvec, (Hq, Sq), "f32", "dvec"))
     _check(lib.cp_attn_bwd_dvec(out.data_ptr(), dout.data_ptr(), dvec.data_ptr(), Sq, Hq, D,
                                 _dtype_code(dout), _stream(out, stream)))
     return dvec
@@ -218,16 +252,15 @@ def cp_attn_block_bwd(q, k, v, dout, lse, dvec, dq=None, dk=None, dv=None, q_off
                       stream=None):
     """Gradients of one query chunk against one KV block (float32 dq, dk,
     dv), from the rows' final lse and dvec; accumulate adds into dq/dk/dv."""
-    import torch
-    Sq, Hq, D = q.shape
-    Sk, Hkv, _ = k.shape
-    if dq is None:
-        dq = torch.empty(Sq, Hq, D, device=q.device, dtype=torch.float32)
-    if dk is None:
-        dk = torch.empty(Sk, Hkv, D, device=q.device, dtype=torch.float32)
-    if dv is None:
-        dv = torch.empty(Sk, Hkv, D, device=q.device, dtype=torch.float32)
-    _dense(q, k, v, dout, lse, dvec, dq, dk, dv)
+    Sq, Hq, D = _dims(q, 3, "q")
+    Sk, Hkv, _ = _dims(k, 3, "k")
+    dq = _f32((Sq, Hq, D), q) if dq is None else dq
+    dk = _f32((Sk, Hkv, D), q) if dk is None else dk
+    dv = _f32((Sk, Hkv, D), q) if dv is None else dv
+    _checked(q, (q, None, "in", "q"), (k, (Sk, Hkv, D), "in", "k"), (v, (Sk, Hkv, D), "in", "v"),
+             (dout, (Sq, Hq, D), "in", "dout"), (lse, (Hq, Sq), "f32", "lse"),
+             (dvec, (Hq, Sq), "f32", "dvec"), (dq, (Sq, Hq, D), "f32", "dq"),
+             (dk, (Sk, Hkv, D), "f32", "dk"), (dv, (Sk, Hkv, D), "f32", "dv"))
     _check(lib.cp_attn_block_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
                                  lse.data_ptr(), dvec.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                  dv.data_ptr(), Sq, Sk, Hq, Hkv, D, q_offset, k_offset,
@@ -236,34 +269,34 @@ def cp_attn_block_bwd(q, k, v, dout, lse, dvec, dq=None, dk=None, dv=None, q_off
     return dq, dk, dv
 
 
+def _ring_bwd_args(q, k, v, out, lse, dout, P, layout, rank, seq_len, dq, dk, dv):
+    """Shapes of a ring backward call, its gradient buffers and their checks."""
+    _, Hq, D = _dims(q, 3, "q")
+    _, Hkv, _ = _dims(k, 3, "k")
+    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
+    S = q.shape[0] if seq_len is None else int(seq_len)
+    rows_in, rows = _ring_rows(S, P, lay, rank)
+    dq = _f32((rows, Hq, D), q) if dq is None else dq
+    dk = _f32((rows_in, Hkv, D), q) if dk is None else dk
+    dv = _f32((rows_in, Hkv, D), q) if dv is None else dv
+    specs = [(q, (rows_in, Hq, D), "in", "q"), (k, (rows_in, Hkv, D), "in", "k"),
+             (v, (rows_in, Hkv, D), "in", "v"), (out, (rows, Hq, D), "f32", "out"),
+             (lse, (Hq, rows), "f32", "lse"), (dout, (rows, Hq, D), "in", "dout"),
+             (dq, (rows, Hq, D), "f32", "dq"), (dk, (rows_in, Hkv, D), "f32", "dk"),
+             (dv, (rows_in, Hkv, D), "f32", "dv")]
+    return S, Hq, Hkv, D, lay, rows, dq, dk, dv, specs
+
+
 def cp_ring_bwd(q, k, v, out, lse, dout, P: int, layout="zigzag", rank: int = -1,
                 causal: bool = True, dq=None, dk=None, dv=None, dvec=None, stream=None,
                 seq_len=None):
     """Backward of cp_ring_fwd: dq in the forward's output layout, dk and dv
     [rows of k][Hkv][D] float32 in the inputs' order -- natural, or striped
     for the striped layout (contributions of the rank(s) computed)."""
-    import torch
-    _, Hq, D = q.shape
-    _, Hkv, _ = k.shape
-    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
-    S = q.shape[0] if seq_len is None else int(seq_len)
-    rows_in, rows = _ring_rows(S, P, lay, rank)
-    for t, shape, name in ((q, (rows_in, Hq, D), "q"), (k, (rows_in, Hkv, D), "k"),
-                           (v, (rows_in, Hkv, D), "v"), (out, (rows, Hq, D), "out"),
-                           (lse, (Hq, rows), "lse"), (dout, (rows, Hq, D), "dout")):
-        _need(t, shape, name)
-    if dq is None:
-        dq = torch.empty(rows, Hq, D, device=q.device, dtype=torch.float32)
-    if dk is None:
-        dk = torch.empty(rows_in, Hkv, D, device=q.device, dtype=torch.float32)
-    if dv is None:
-        dv = torch.empty(rows_in, Hkv, D, device=q.device, dtype=torch.float32)
-    if dvec is None:
-        dvec = torch.empty(Hq, rows, device=q.device, dtype=torch.float32)
-    for t, shape, name in ((dq, (rows, Hq, D), "dq"), (dk, (rows_in, Hkv, D), "dk"),
-                           (dv, (rows_in, Hkv, D), "dv"), (dvec, (Hq, rows), "dvec")):
-        _need(t, shape, name)
-    _dense(q, k, v, out, lse, dout, dq, dk, dv, dvec)
+    S, Hq, Hkv, D, lay, rows, dq, dk, dv, specs = _ring_bwd_args(
+        q, k, v, out, lse, dout, P, layout, rank, seq_len, dq, dk, dv)
+    dvec = _f32((Hq, rows), q) if dvec is None else dvec
+    _checked(q, *specs, (dvec, (Hq, rows), "f32", "dvec"))
     _check(lib.cp_ring_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                            lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                            dv.data_ptr(), dvec.data_ptr(), S, Hq, Hkv, D, P, lay, rank,
@@ -271,15 +304,27 @@ def cp_ring_bwd(q, k, v, out, lse, dout, P: int, layout="zigzag", rank: int = -1
     return dq, dk, dv
 
 
+def _dtype_arg(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    return CP_BF16 if str(dtype) == "torch.bfloat16" else CP_F32
+
+
 def cp_usp_fwd_workspace(S: int, Hq: int, Hkv: int, D: int, P_u: int, P_r: int, layout,
                          rank: int, dtype) -> int:
     """Workspace bytes of cp_usp_fwd (dtype: CP_F32 / CP_BF16 or a torch dtype)."""
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
-    code = dtype if isinstance(dtype, int) else (CP_BF16 if str(dtype) == "torch.bfloat16"
-                                                 else CP_F32)
     n = ctypes.c_size_t(0)
-    _check(lib.cp_usp_fwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, code, ctypes.byref(n)))
+    _check(lib.cp_usp_fwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, _dtype_arg(dtype),
+                                    ctypes.byref(n)))
     return n.value
+
+
+def _workspace(workspace, need, ref):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=ref.device, dtype=torch.uint8)
+    return workspace
 
 
 def cp_usp_fwd(q, k, v, P_u: int, P_r: int, layout="zigzag", rank: int = -1,
@@ -289,25 +334,18 @@ def cp_usp_fwd(q, k, v, P_u: int, P_r: int, layout="zigzag", rank: int = -1,
     out, lse over the inputs' rows in their order; rank: ring group r's
     rows in its local order, head share u written.  seq_len: the real length
     when the ring split does not divide it (padded as cp_ring_fwd)."""
-    import torch
-    _, Hq, D = q.shape
-    _, Hkv, _ = k.shape
+    _, Hq, D = _dims(q, 3, "q")
+    _, Hkv, _ = _dims(k, 3, "k")
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
     S = q.shape[0] if seq_len is None else int(seq_len)
     rows_in, rows = _ring_rows(S, P_r, lay, -1 if rank < 0 else rank // max(P_u, 1))
     need = cp_usp_fwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, _dtype_code(q))
-    _need(q, (rows_in, Hq, D), "q")
-    _need(k, (rows_in, Hkv, D), "k")
-    _need(v, (rows_in, Hkv, D), "v")
-    if out is None:
-        out = torch.empty(rows, Hq, D, device=q.device, dtype=torch.float32)
-    if lse is None:
-        lse = torch.empty(Hq, rows, device=q.device, dtype=torch.float32)
-    _need(out, (rows, Hq, D), "out")
-    _need(lse, (Hq, rows), "lse")
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
-    _dense(q, k, v, out, lse, workspace)
+    out = _f32((rows, Hq, D), q) if out is None else out
+    lse = _f32((Hq, rows), q) if lse is None else lse
+    workspace = _workspace(workspace, need, q)
+    _checked(q, (q, (rows_in, Hq, D), "in", "q"), (k, (rows_in, Hkv, D), "in", "k"),
+             (v, (rows_in, Hkv, D), "in", "v"), (out, (rows, Hq, D), "f32", "out"),
+             (lse, (Hq, rows), "f32", "lse"), (workspace, None, "u8", "workspace"))
     _check(lib.cp_usp_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           lse.data_ptr(), S, Hq, Hkv, D, P_u, P_r, lay, rank, int(bool(causal)),
                           _dtype_code(q), workspace.data_ptr(), workspace.numel(),
@@ -319,10 +357,9 @@ def cp_usp_bwd_workspace(S: int, Hq: int, Hkv: int, D: int, P_u: int, P_r: int, 
                          rank: int, dtype) -> int:
     """Workspace bytes of cp_usp_bwd (dtype: CP_F32 / CP_BF16 or a torch dtype)."""
     lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
-    code = dtype if isinstance(dtype, int) else (CP_BF16 if str(dtype) == "torch.bfloat16"
-                                                 else CP_F32)
     n = ctypes.c_size_t(0)
-    _check(lib.cp_usp_bwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, code, ctypes.byref(n)))
+    _check(lib.cp_usp_bwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, _dtype_arg(dtype),
+                                    ctypes.byref(n)))
     return n.value
 
 
@@ -331,29 +368,12 @@ def cp_usp_bwd(q, k, v, out, lse, dout, P_u: int, P_r: int, layout="zigzag", ran
                seq_len=None):
     """Backward of cp_usp_fwd: dq in its output layout, dk and dv over the
     inputs' rows (a rank writes only its head share)."""
-    import torch
-    _, Hq, D = q.shape
-    _, Hkv, _ = k.shape
-    lay = LAYOUTS[layout] if isinstance(layout, str) else int(layout)
-    S = q.shape[0] if seq_len is None else int(seq_len)
-    rows_in, rows = _ring_rows(S, P_r, lay, -1 if rank < 0 else rank // max(P_u, 1))
+    ring_rank = -1 if rank < 0 else rank // max(P_u, 1)
+    S, Hq, Hkv, D, lay, rows, dq, dk, dv, specs = _ring_bwd_args(
+        q, k, v, out, lse, dout, P_r, layout, ring_rank, seq_len, dq, dk, dv)
     need = cp_usp_bwd_workspace(S, Hq, Hkv, D, P_u, P_r, lay, rank, _dtype_code(q))
-    f32 = dict(device=q.device, dtype=torch.float32)
-    if dq is None:
-        dq = torch.empty(rows, Hq, D, **f32)
-    if dk is None:
-        dk = torch.empty(rows_in, Hkv, D, **f32)
-    if dv is None:
-        dv = torch.empty(rows_in, Hkv, D, **f32)
-    for t, shape, name in ((q, (rows_in, Hq, D), "q"), (k, (rows_in, Hkv, D), "k"),
-                           (v, (rows_in, Hkv, D), "v"),
-                           (out, (rows, Hq, D), "out"), (lse, (Hq, rows), "lse"),
-                           (dout, (rows, Hq, D), "dout"), (dq, (rows, Hq, D), "dq"),
-                           (dk, (rows_in, Hkv, D), "dk"), (dv, (rows_in, Hkv, D), "dv")):
-        _need(t, shape, name)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
-    _dense(q, k, v, out, lse, dout, dq, dk, dv, workspace)
+    workspace = _workspace(workspace, need, q)
+    _checked(q, *specs, (workspace, None, "u8", "workspace"))
     _check(lib.cp_usp_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                           dv.data_ptr(), S, Hq, Hkv, D, P_u, P_r, lay, rank, int(bool(causal)),
@@ -365,12 +385,12 @@ def cp_usp_bwd(q, k, v, out, lse, dout, P_u: int, P_r: int, layout="zigzag", ran
 def cp_seq_to_head(x, P: int, rank: int = -1, y=None, stream=None):
     """x natural [S,H,D] -> [P,S,H/P,D] (rank=-1) or [S,H/P,D] (rank=p)."""
     import torch
-    S, H, D = x.shape
+    S, H, D = _dims(x, 3, "x")
     Hp = H // max(P, 1)
+    shape = (P, S, Hp, D) if rank < 0 else (S, Hp, D)
     if y is None:
-        shape = (P, S, Hp, D) if rank < 0 else (S, Hp, D)
         y = torch.empty(shape, device=x.device, dtype=x.dtype)
-    _dense(x, y)
+    _checked(x, (x, None, "same", "x"), (y, shape, "same", "y"))
     _check(lib.cp_seq_to_head(x.data_ptr(), y.data_ptr(), S, H, D, P, rank, x.element_size(),
                               _stream(x, stream)))
     return y
@@ -380,13 +400,12 @@ def cp_kv_seq_to_head(x, P: int, rank: int = -1, y=None, stream=None):
     """K or V natural [S,H,D] -> [P,S,Hp,D] (rank=-1) or [S,Hp,D] (rank=p);
     with P > H every head is replicated P/H times (Hp = 1)."""
     import torch
-    S, H, D = x.shape
+    S, H, D = _dims(x, 3, "x")
     Hp = H // P if P <= H else 1
+    shape = (P, S, Hp, D) if rank < 0 else (S, Hp, D)
     if y is None:
-        shape = (P, S, Hp, D) if rank < 0 else (S, Hp, D)
         y = torch.empty(shape, device=x.device, dtype=x.dtype)
-    _need(y, (P, S, Hp, D) if rank < 0 else (S, Hp, D), "y")
-    _dense(x, y)
+    _checked(x, (x, None, "same", "x"), (y, shape, "same", "y"))
     _check(lib.cp_kv_seq_to_head(x.data_ptr(), y.data_ptr(), S, H, D, P, rank,
                                  x.element_size(), _stream(x, stream)))
     return y
@@ -395,8 +414,10 @@ def cp_kv_seq_to_head(x, P: int, rank: int = -1, y=None, stream=None):
 def cp_head_to_seq(x, y, P: int, rank: int = -1, stream=None):
     """Inverse of cp_seq_to_head into the natural [S,H,D] tensor y; rank=p
     writes head slice p of y only."""
-    S, H, D = y.shape
-    _dense(x, y)
+    S, H, D = _dims(y, 3, "y")
+    Hp = H // max(P, 1)
+    _checked(y, (x, (P, S, Hp, D) if rank < 0 else (S, Hp, D), "same", "x"),
+             (y, None, "same", "y"))
     _check(lib.cp_head_to_seq(x.data_ptr(), y.data_ptr(), S, H, D, P, rank, x.element_size(),
                               _stream(y, stream)))
     return y

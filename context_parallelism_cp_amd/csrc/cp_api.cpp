@@ -677,10 +677,15 @@ int cp_attn_block_bwd(const void *q, const void *k, const void *v, const void *d
     return rc ? rc : ok();
 }
 
-int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out, const float *lse,
-                const void *dout, float *dq, float *dk, float *dv, float *dvec, int64_t S, int Hq,
-                int Hkv, int D, int P, cp_layout layout, int rank, int causal, cp_dtype dtype,
-                void *stream)
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the ring backward (every one before any HIP call).
+int ring_bwd_check(const void *q, const void *k, const void *v, const float *out,
+                   const float *lse, const void *dout, float *dq, float *dk, float *dv,
+                   const float *dvec, int64_t S, int Hq, int Hkv, int D, int P, cp_layout layout,
+                   int rank, cp_dtype dtype)
 {
     int rc = check_ring_shape(S, P, layout, rank);
     if (rc)
@@ -693,22 +698,29 @@ int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out, c
     rc = check_bwd(q, k, v, dout, lse, dvec, dq, dk, dv, rows_out, rows_in, Hq, Hkv, D, dtype);
     if (rc)
         return rc;
-    {
-        const size_t eb = dtype == CP_BF16 ? 2 : 4;
-        const size_t qb = (size_t)rows_in * Hq * D * eb, ob = (size_t)rows_out * Hq * D * 4;
-        const size_t gk = (size_t)rows_in * Hkv * D * 4;
-        if (overlaps(q, qb, dq, ob) || overlaps(q, qb, dk, gk) || overlaps(q, qb, dv, gk) ||
-            overlaps(out, ob, dq, ob) || overlaps(out, ob, dk, gk) || overlaps(out, ob, dv, gk) ||
-            overlaps(dvec, (size_t)rows_out * Hq * 4, out, ob) ||
-            overlaps(dvec, (size_t)rows_out * Hq * 4, dq, ob))
-            return fail(CP_ERR_ALIGN, "gradient buffers must not overlap the inputs");
-        if (!aligned(out, 4))
-            return fail(CP_ERR_ALIGN, "out must be 4-byte aligned");
-    }
-    if (S == 0)
-        return ok();
-    hipStream_t st = (hipStream_t)stream;
-    rc = timed_launch(CP_KERNEL_BWD_DVEC, st, [&] {
+    const size_t eb = dtype == CP_BF16 ? 2 : 4;
+    const size_t qb = (size_t)rows_in * Hq * D * eb, ob = (size_t)rows_out * Hq * D * 4;
+    const size_t gk = (size_t)rows_in * Hkv * D * 4;
+    if (overlaps(q, qb, dq, ob) || overlaps(q, qb, dk, gk) || overlaps(q, qb, dv, gk) ||
+        overlaps(out, ob, dq, ob) || overlaps(out, ob, dk, gk) || overlaps(out, ob, dv, gk) ||
+        overlaps(dvec, (size_t)rows_out * Hq * 4, out, ob) ||
+        overlaps(dvec, (size_t)rows_out * Hq * 4, dq, ob))
+        return fail(CP_ERR_ALIGN, "gradient buffers must not overlap the inputs");
+    if (!aligned(out, 4))
+        return fail(CP_ERR_ALIGN, "out must be 4-byte aligned");
+    return CP_OK;
+}
+
+// The ring backward's launches, after ring_bwd_check: dvec of the output
+// rows, zeroed gradients, then one dq + dk/dv launch pair per computed pair.
+int ring_bwd_run(const void *q, const void *k, const void *v, const float *out,
+                 const float *lse, const void *dout, float *dq, float *dk, float *dv,
+                 float *dvec, int64_t S, int Hq, int Hkv, int D, int P, cp_layout layout,
+                 int rank, int causal, cp_dtype dtype, hipStream_t st)
+{
+    const int64_t rows_in = input_rows(S, P, layout);
+    const int64_t rows_out = ring_rows_out(S, P, layout, rank);
+    int rc = timed_launch(CP_KERNEL_BWD_DVEC, st, [&] {
         return launch_bwd_dvec(out, dout, dtype == CP_BF16 ? 1 : 0, dvec, rows_out, rows_out, Hq,
                                D, st);
     });
@@ -754,7 +766,27 @@ int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out, c
                     return rc;
             }
         }
-    return ok();
+    return CP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out, const float *lse,
+                const void *dout, float *dq, float *dk, float *dv, float *dvec, int64_t S, int Hq,
+                int Hkv, int D, int P, cp_layout layout, int rank, int causal, cp_dtype dtype,
+                void *stream)
+{
+    int rc = ring_bwd_check(q, k, v, out, lse, dout, dq, dk, dv, dvec, S, Hq, Hkv, D, P, layout,
+                            rank, dtype);
+    if (rc)
+        return rc;
+    if (S == 0)
+        return ok();
+    rc = ring_bwd_run(q, k, v, out, lse, dout, dq, dk, dv, dvec, S, Hq, Hkv, D, P, layout, rank,
+                      causal, dtype, (hipStream_t)stream);
+    return rc ? rc : ok();
 }
 
 // One rank's head share, row by row: to_head copies y[t] <- x[t][p*Hp, (p+1)*Hp),

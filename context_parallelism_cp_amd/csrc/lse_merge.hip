@@ -22,10 +22,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
+// No pointer is declared __restrict__: o may be o1 or o2 (and lse may be
+// lse1 or lse2) exactly, and without the qualifier the compiler has to
+// assume they alias, so it keeps every element's loads ahead of its store.
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(
-    const f32x4 *__restrict__ o1, const float *lse1, const f32x4 *__restrict__ o2,
-    const float *lse2, f32x4 *o, float *lse, int64_t Sq, int H, int L, int G,
-    int64_t n_groups)
+    const f32x4 *o1, const float *lse1, const f32x4 *o2, const float *lse2, f32x4 *o,
+    float *lse, int64_t Sq, int H, int L, int G, int64_t n_groups)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;

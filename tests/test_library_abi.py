@@ -353,3 +353,83 @@ def test_kv_seq_to_head_argument_errors():
     assert f(FAKE, FAKE * 2 ** 20, 0, 8, 128, 16, -1, 2, None) == cp.CP_OK
     # P <= H is the plain seq_to_head, with its own checks
     assert f(FAKE, FAKE * 2 ** 20, 64, 8, 128, 3, -1, 2, None) == cp.CP_ERR_SHAPE
+
+
+# ------------------------------------------- binding checks before any launch
+def _bf16(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def _f32t(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.float32)
+
+
+def _raises(code, fn, *a, match=None, **kw):
+    """The binding refuses the call with `code` (the CPU tensors here never
+    reach the library: the checks run before any pointer is handed over)."""
+    with pytest.raises(cp.CpError) as e:
+        fn(*a, **kw)
+    assert e.value.code == code, str(e.value)
+    if match:
+        assert match in str(e.value), str(e.value)
+
+
+def test_binding_refuses_wrong_buffers_before_any_launch():
+    import torch
+    q, k, v = _bf16(64, 4, 128), _bf16(64, 2, 128), _bf16(64, 2, 128)
+    # undersized or wrongly shaped outputs
+    _raises(cp.CP_ERR_SHAPE, cp.cp_attn_block_fwd, q, k, v, out=_f32t(63, 4, 128),
+            match="out must have shape (64, 4, 128)")
+    _raises(cp.CP_ERR_SHAPE, cp.cp_attn_block_fwd, q, k, v, lse=_f32t(64, 4), match="lse")
+    _raises(cp.CP_ERR_SHAPE, cp.cp_attn_block_fwd, q, _bf16(64, 2, 64), v, match="k must")
+    _raises(cp.CP_ERR_SHAPE, cp.cp_attn_block_fwd, q[0], k, v, match="3 dimensions")
+    # a bf16 output, a float32 k next to a bf16 q, an unsupported input dtype
+    _raises(cp.CP_ERR_UNSUPPORTED, cp.cp_attn_block_fwd, q, k, v, out=_bf16(64, 4, 128),
+            match="out must have dtype torch.float32")
+    _raises(cp.CP_ERR_UNSUPPORTED, cp.cp_attn_block_fwd, q, _f32t(64, 2, 128), v,
+            match="k must have dtype torch.bfloat16")
+    _raises(cp.CP_ERR_UNSUPPORTED, cp.cp_attn_block_fwd, q.half(), k.half(), v.half(),
+            match="not supported")
+    # views that are not dense
+    _raises(cp.CP_ERR_ALIGN, cp.cp_attn_block_fwd, q, k, _bf16(64, 128, 2).transpose(1, 2),
+            match="contiguous")
+    # host tensors
+    _raises(cp.CP_ERR_UNSUPPORTED, cp.cp_attn_block_fwd, q, k, v, match="GPU")
+    # merge: o2 of another shape, lse2 in bf16, o for a different head count
+    o, l = _f32t(32, 4, 128), _f32t(4, 32)
+    _raises(cp.CP_ERR_SHAPE, cp.cp_lse_merge, o, l, _f32t(32, 4, 64), l, match="o2")
+    _raises(cp.CP_ERR_UNSUPPORTED, cp.cp_lse_merge, o, l, o, l.bfloat16(), match="lse2")
+    _raises(cp.CP_ERR_SHAPE, cp.cp_lse_merge, o, l, o, l, o=_f32t(32, 2, 128), match="o must")
+    # backward: dq too short, dvec of another dtype, dout of another dtype
+    dout, lse, dvec = _bf16(64, 4, 128), _f32t(4, 64), _f32t(4, 64)
+    _raises(cp.CP_ERR_SHAPE, cp.cp_attn_block_bwd, q, k, v, dout, lse, dvec,
+            dq=_f32t(32, 4, 128), match="dq")
+    _raises(cp.CP_ERR_UNSUPPORTED, cp.cp_attn_block_bwd, q, k, v, dout, lse, dvec.double(),
+            match="dvec")
+    _raises(cp.CP_ERR_UNSUPPORTED, cp.cp_attn_block_bwd, q, k, v, dout.float(), lse, dvec,
+            match="dout")
+    _raises(cp.CP_ERR_SHAPE, cp.cp_attn_bwd_dvec, _f32t(64, 4, 128), dout, _f32t(64, 4),
+            match="dvec")
+    _raises(cp.CP_ERR_UNSUPPORTED, cp.cp_attn_bwd_dvec, _bf16(64, 4, 128), dout,
+            match="out must have dtype")
+    # ring: out for one rank when all ranks are asked, a short dvec
+    _raises(cp.CP_ERR_SHAPE, cp.cp_ring_fwd, q, k, v, 4, "zigzag", -1, out=_f32t(16, 4, 128))
+    out, lse = _f32t(16, 4, 128), _f32t(4, 16)
+    _raises(cp.CP_ERR_SHAPE, cp.cp_ring_bwd, q, k, v, out, lse, _bf16(16, 4, 128), 4, "zigzag",
+            0, dvec=_f32t(4, 8), match="dvec")
+    _raises(cp.CP_ERR_SHAPE, cp.cp_ring_bwd, q, k, v, out, lse, _bf16(16, 4, 128), 4, "zigzag",
+            0, dk=_f32t(16, 2, 128), match="dk")
+    # USP: a workspace of the wrong element type
+    _raises(cp.CP_ERR_UNSUPPORTED, cp.cp_usp_fwd, _bf16(64, 4, 128), _bf16(64, 2, 128),
+            _bf16(64, 2, 128), 2, 2, "zigzag", -1, workspace=torch.zeros(10, dtype=torch.int32),
+            match="workspace")
+    # repacks: y of the wrong shape or element size
+    x = _bf16(64, 8, 128)
+    _raises(cp.CP_ERR_SHAPE, cp.cp_seq_to_head, x, 4, -1, y=_bf16(64, 2, 128), match="y must")
+    _raises(cp.CP_ERR_UNSUPPORTED, cp.cp_seq_to_head, x, 4, 1, y=_f32t(64, 2, 128))
+    _raises(cp.CP_ERR_SHAPE, cp.cp_head_to_seq, _bf16(64, 4, 128), x, 4, 1, match="x must")
+    _raises(cp.CP_ERR_UNSUPPORTED, cp.cp_head_to_seq, _bf16(4, 64, 2, 128), x, 4, -1,
+            match="GPU")
+
