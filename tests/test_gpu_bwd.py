@@ -380,3 +380,164 @@ def test_bf16_ring_bwd_rank_share_128k(layout):
           f"(sum |dk| {scale_dk:.3e})", flush=True)
     assert err_v <= 1e-3 * float(np.abs(want_dv).max())
     assert err_k <= 1e-3 * scale_dk
+
+
+# ------------------------------------ element-wise gradients at full size
+# dq, dk and dv are linear in dout (dvec = dout . out is too), so with dout
+# zero except on a few short runs of query rows every gradient comes from
+# those rows alone.  The float64 oracle then needs the statistics (lse, out)
+# of those rows only, and can give dk and dv of any key row: for each run it
+# is called on the run's query rows at their absolute offset against the
+# whole key sequence, and the runs' key-row contributions are added (the
+# sum over query rows of the definition).  The HIP path runs the whole
+# launch as the benchmark does; rows outside the runs contribute exact zeros
+# there (dP = 0 and dvec = 0 make ds = 0), which is checked on dq too.
+
+def sparse_dout(n_rows, H, local_runs, seed):
+    """bf16 dout [n_rows, H, 128]: zeros except seeded N(0, 1) rows on the
+    runs (local_row0, n); returns it and the runs' rows."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    dout = torch.zeros(n_rows, H, 128, dtype=torch.bfloat16)
+    parts = []
+    for r0, n in local_runs:
+        x = torch.randn(n, H, 128, generator=g).to(torch.bfloat16)
+        dout[r0:r0 + n] = x
+        parts.append(x)
+    return dout, parts
+
+
+def runs_oracle(q, k, v, runs, parts, keys):
+    """Float64 gradients of the dout runs: dq of every run row (one array
+    per run) and dk, dv of the key rows `keys` summed over the runs.
+    q, k, v natural order; runs = (first position, n)."""
+    from oracle import native
+    dqs, dk, dv = [], 0.0, 0.0
+    for (p0, n), dpart in zip(runs, parts):
+        wq, wk, wv = native.attention_bwd_rows(q[p0:p0 + n], k, v, dpart, q_rows=range(n),
+                                               k_rows=keys, q_offset=p0, k_offset=0)
+        dqs.append(wq)
+        dk, dv = dk + wk, dv + wv
+    return dqs, dk, dv
+
+
+def check_sampled(name, got, want, what):
+    got = got.double().cpu().numpy() if torch.is_tensor(got) else got
+    assert not np.isnan(got).any(), f"{what} {name}: NaN"
+    err = float(np.abs(got - want).max())
+    scale = float(np.abs(want).max())
+    print(f"    {what} {name}: max|err| = {err:.3e} (ref max {scale:.3e})", flush=True)
+    assert scale > 0 and err <= BF16_GRAD_REL * scale, f"{what} {name}: error {err}"
+
+
+def sampled_keys(hi, fixed, n_random, seed):
+    rng = np.random.default_rng(seed)
+    ks = set(int(x) for x in fixed if 0 <= x < hi) | set(int(x) for x in rng.integers(0, hi, n_random))
+    return np.array(sorted(ks), dtype=np.int64)
+
+
+def test_bf16_ring_bwd_rank_share_128k_elementwise():
+    """The benchmark's ring backward: zigzag rank 0 of 8 over 131072 tokens,
+    32 heads (chunks 0 and 15).  dout on six runs of the rank's rows (the
+    first rows of chunk 0, its middle and end, the start, middle and end of
+    chunk 15); dk and dv of key rows all over the sequence (tile and chunk
+    boundaries, seeded draws) element by element against the oracle, dq of
+    the run rows too and exact zeros on other rows."""
+    S, H, P, rank = 131072, 32, 8, 0
+    announce(f"bf16 ring bwd S={S} H={H} P={P} zigzag rank {rank}: element-wise dk/dv of "
+             f"sampled keys, sparse dout")
+    q, k, v = make_qkv(S=S, H=H, D=128, seed=0, dtype=torch.bfloat16)
+    pos = OS.layout_index(OS.ZIGZAG, S, P, rank)
+    rows = S // P
+    local_runs = [(0, 8), (3000, 16), (8176, 16), (8192, 8), (12000, 8), (16376, 8)]
+    dout, parts = sparse_dout(rows, H, local_runs, seed=71)
+    qd, kd, vd = dev(q, k, v)
+    out, lse = cp.cp_ring_fwd(qd, kd, vd, P, "zigzag", rank)
+    gq, gk, gv = Guarded(rows, H, 128), Guarded(S, H, 128), Guarded(S, H, 128)
+    cp.cp_ring_bwd(qd, kd, vd, out, lse, dout.to(DEV), P, "zigzag", rank, dq=gq.t, dk=gk.t,
+                   dv=gv.t)
+    torch.cuda.synchronize()
+    for g in (gq, gk, gv):
+        g.check()
+    del qd, kd, vd, out, lse
+    keys = sampled_keys(S, [0, 1, 7, 8, 255, 256, 2999, 3007, 3015, 3016, 8191, 8192, 20000,
+                            65535, 65536, 100000, 122879, 122880, 122881, 126690, 126695,
+                            131063, 131064, 131071], 24, seed=72)
+    runs = [(int(pos[r0]), n) for r0, n in local_runs]
+    wq, wk, wv = runs_oracle(q, k, v, runs, parts, keys)
+    kt = torch.from_numpy(keys).to(DEV)
+    check_sampled("dk", gk.t[kt], wk, "128K ring rank 0")
+    check_sampled("dv", gv.t[kt], wv, "128K ring rank 0")
+    for (r0, n), w in zip(local_runs, wq):
+        check_sampled("dq", gq.t[r0:r0 + n], w, f"128K ring rank 0 rows {r0}+{n}")
+    others = torch.ones(rows, dtype=torch.bool)
+    for r0, n in local_runs:
+        others[r0:r0 + n] = False
+    assert bool((gq.t[others.to(DEV)] == 0).all()), "dq of rows without dout"
+
+
+def test_bf16_block_bwd_gqa_128k_elementwise():
+    """The benchmark's Ulysses backward launch: one block of 131072 query rows
+    on 4 query heads and 1 KV head, causal, offsets 0.  dout on runs spread
+    over the sequence; dk, dv of sampled key rows and dq of the run rows
+    element by element against the oracle."""
+    S, Hq, Hkv = 131072, 4, 1
+    announce(f"bf16 block bwd S={S} Hq={Hq} Hkv={Hkv}: element-wise dk/dv of sampled keys, "
+             f"sparse dout")
+    q, _, _ = make_qkv(S=S, H=Hq, D=128, seed=81, dtype=torch.bfloat16)
+    _, k, v = make_qkv(S=S, H=Hkv, D=128, seed=82, dtype=torch.bfloat16)
+    runs = [(0, 8), (4090, 16), (65530, 16), (100000, 16), (131056, 16)]
+    dout, parts = sparse_dout(S, Hq, runs, seed=83)
+    dq, dk, dv = run_block_bwd(q, k, v, dout, 0, 0, True)
+    keys = sampled_keys(S, [0, 1, 7, 8, 127, 128, 4089, 4090, 4105, 4106, 65535, 65536, 99999,
+                            100015, 100016, 131055, 131056, 131071], 24, seed=84)
+    wq, wk, wv = runs_oracle(q, k, v, runs, parts, keys)
+    kt = torch.from_numpy(keys).to(DEV)
+    check_sampled("dk", dk[kt], wk, "128K GQA block")
+    check_sampled("dv", dv[kt], wv, "128K GQA block")
+    for (r0, n), w in zip(runs, wq):
+        check_sampled("dq", dq[r0:r0 + n], w, f"128K GQA block rows {r0}+{n}")
+
+
+def test_bf16_usp_bwd_rank_share_128k_elementwise():
+    """The benchmark's USP backward share: rank 13 (Ulysses rank 5 of ring
+    group 1) of 8 x 2 over 131072 tokens, 32 query heads on 8 KV heads,
+    zigzag (group 1 holds positions 32768 .. 98303).  dout on runs of the
+    group's rows; the share's head slice (query heads 20..23, KV head 5) of
+    dk, dv at sampled keys and of dq on the run rows against the oracle on
+    that head group; keys after the group's last position get exact zeros."""
+    from test_gpu_usp import run_group
+    S, Hq, Hkv, P_u, P_r, rank = 131072, 32, 8, 8, 2, 13
+    u, r = rank % P_u, rank // P_u
+    hs = slice(u * Hq // P_u, (u + 1) * Hq // P_u)
+    announce(f"bf16 USP bwd S={S} {P_u}x{P_r} zigzag rank {rank}: element-wise dk/dv of "
+             f"sampled keys, sparse dout")
+    q, k, v = make_qkv(S=S, H=Hq, D=128, seed=91, dtype=torch.bfloat16, Hkv=Hkv)
+    rows = S // P_r
+    pos = OS.layout_index(OS.ZIGZAG, S, P_r, r)
+    local_runs = [(0, 8), (16000, 16), (32760, 16), (65520, 16)]
+    dout, parts = sparse_dout(rows, Hq, local_runs, seed=92)
+    qd, kd, vd = dev(q, k, v)
+    out, lse = run_group(qd, kd, vd, P_u, P_r, "zigzag", r)
+    gq = torch.full((rows, Hq, 128), 7.0, device=DEV)
+    gk = torch.full((S, Hkv, 128), 7.0, device=DEV)
+    gv = torch.full((S, Hkv, 128), 7.0, device=DEV)
+    cp.cp_usp_bwd(qd, kd, vd, out, lse, dout.to(DEV), P_u, P_r, "zigzag", rank, dq=gq, dk=gk,
+                  dv=gv)
+    torch.cuda.synchronize()
+    del qd, kd, vd, out, lse
+    runs = [(int(pos[r0]), n) for r0, n in local_runs]
+    assert all(int(pos[r0 + n - 1]) == p0 + n - 1 for (r0, n), (p0, _) in zip(local_runs, runs))
+    keys = sampled_keys(S, [0, 1, 32767, 32768, 32775, 32776, 48768, 48783, 65527, 65528, 65535,
+                            65536, 65543, 98287, 98303, 98304, 110000, 131071], 24, seed=93)
+    qh, kh, vh = (x[:, sl].contiguous() for x, sl in ((q, hs), (k, slice(u, u + 1)),
+                                                       (v, slice(u, u + 1))))
+    wq, wk, wv = runs_oracle(qh, kh, vh, runs, [p[:, hs].contiguous() for p in parts], keys)
+    kt = torch.from_numpy(keys).to(DEV)
+    check_sampled("dk", gk[kt, u:u + 1], wk, f"128K USP rank {rank}")
+    check_sampled("dv", gv[kt, u:u + 1], wv, f"128K USP rank {rank}")
+    late = torch.from_numpy(keys[keys > 98303]).to(DEV)
+    assert bool((gk[late, u] == 0).all()) and bool((gv[late, u] == 0).all())
+    for (r0, n), w in zip(local_runs, wq):
+        check_sampled("dq", gq[r0:r0 + n, hs], w, f"128K USP rank {rank} rows {r0}+{n}")
+    assert bool((gq[:, :hs.start] == 7.0).all()) and bool((gq[:, hs.stop:] == 7.0).all())
