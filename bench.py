@@ -105,10 +105,11 @@ BWD_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bwd_128k_rank_share_h
 BWD_KERNEL_SOURCE = os.path.join(ROOT, "context_parallelism_cp_amd", "csrc", "bwd_bf16.hip")
 
 
-def recorded_traffic(profile=TRAFFIC_PROFILE, source=KERNEL_SOURCE):
+def recorded_traffic(profile=TRAFFIC_PROFILE, source=KERNEL_SOURCE, workload=None):
     """HBM bytes per launch (or launch pair) from a committed FETCH_SIZE /
     WRITE_SIZE summary, or None when the kernel source changed since it was
-    taken."""
+    taken or the summary is of another workload (its ``workload_key`` line
+    must equal ``workload``)."""
     import hashlib
     try:
         fields = {}
@@ -121,9 +122,16 @@ def recorded_traffic(profile=TRAFFIC_PROFILE, source=KERNEL_SOURCE):
             current = hashlib.sha256(f.read()).hexdigest()
         if fields.get("kernel_source_sha256") != current:
             return None
+        if workload is None or fields.get("workload_key") != workload:
+            return None
         return float(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def workload_key(part, layout, rank, seq, ring_p):
+    """The bench workload a traffic summary belongs to."""
+    return f"part={part} layout={layout} rank={rank} seq={seq} P={ring_p}"
 
 
 def cpu_baseline(q, k, v, budget_s=12.0, max_rows=512):
@@ -158,10 +166,12 @@ def cpu_baseline(q, k, v, budget_s=12.0, max_rows=512):
                     break
     except OSError:
         pass
+    full = ring_share_flop(S, HQ, D, P, "zigzag", RING_RANK)
     return {
         "value": flop / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "full_ring_share_s_extrapolated": round(full / (flop / t_total), 1),
         "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": (f"{len(done_rows)} seeded query rows of ring rank {RING_RANK}'s share "
@@ -270,8 +280,8 @@ def backward(args, cp, torch, q_host, dq, dk, dv, dku, dvu, ql, kl, vl, uly_out_
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(kern_tflops / PEAK_BF16_TFLOPS, 4) if kern_tflops else None,
-            "traffic": (recorded_traffic(BWD_TRAFFIC_PROFILE, BWD_KERNEL_SOURCE)
-                        if (args.layout, args.rank) == ("zigzag", RING_RANK) else None),
+            "traffic": recorded_traffic(BWD_TRAFFIC_PROFILE, BWD_KERNEL_SOURCE,
+                                        workload_key("bwd", args.layout, args.rank, S, P)),
             "traffic_unit": "bytes per dq + dk/dv launch pair (HBM read + write, calibrated)",
             "launches": bwd_n,
             "avg_launch_ms": round(bwd_ms / max(bwd_n, 1), 4),
@@ -475,6 +485,91 @@ def usp(args, cp, torch, dq, dku, dvu, stream):
     print(json.dumps(result))
 
 
+def rank_sweep(args, cp, torch, dq, dk, dv, stream, seq, RP):
+    """Every rank's share of one ring, timed rank by rank (one JSON line):
+    q, k, v bf16 [seq, 32, 128] (the first seq rows of the inputs; default
+    65536 over P = 4 ranks), the contiguous and the zigzag split.  Per rank:
+    its work in the handbook's units ("之字形切分": C x C chunk pairs of the
+    2P-way split, C = seq / 2P, a diagonal pair counted half -- contiguous
+    [2, 6, 10, 14] and zigzag [8, 8, 8, 8] at P = 4), its FLOP, the median
+    ms of its cp_ring_fwd and the attention kernel's rate.  On a synchronous
+    ring every step waits for the slowest rank, so a split's ring time is its
+    largest rank time.  value: the zigzag split's FLOP over all ranks per
+    second of rank time."""
+    dev = "cuda:0"
+    C = seq // (2 * RP)
+    q, k, v = dq[:seq], dk[:seq], dv[:seq]
+    rows = seq // RP
+    out = torch.empty(rows, HQ, D, device=dev, dtype=torch.float32)
+    lse = torch.empty(HQ, rows, device=dev, dtype=torch.float32)
+    table = {}
+    for layout in ("contiguous", "zigzag"):
+        per = []
+        for rank in range(RP):
+            def step():
+                cp.cp_ring_fwd(q, k, v, RP, layout, rank, out=out, lse=lse, stream=stream)
+            for _ in range(args.warmup):
+                step()
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            cp.cp_timing_enable(True)
+            cp.cp_timing_reset()
+            ev[0].record(stream)
+            for i in range(args.steps):
+                step()
+                ev[i + 1].record(stream)
+            torch.cuda.synchronize()
+            ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+            attn_ms, attn_n = cp.cp_timing_read(cp.CP_KERNEL_ATTN_BF16)
+            cp.cp_timing_enable(False)
+            flop = plan_flop(cp, seq, HQ, D, RP, layout, rank)
+            kern = flop * args.steps / (attn_ms * 1e-3) / 1e12
+            per.append({"rank": rank, "units": flop / (4.0 * D * HQ * C * C), "flop": flop,
+                        "launches": attn_n // args.steps,
+                        "ms_median": round(ms[len(ms) // 2], 3),
+                        "kernel_tflops": round(kern, 2),
+                        "kernel_frac": round(kern / PEAK_BF16_TFLOPS, 4)})
+        table[layout] = {"ranks": per,
+                         "ring_time_ms": max(r["ms_median"] for r in per),
+                         "flop_all_ranks": sum(r["flop"] for r in per)}
+    zz = table["zigzag"]
+    value = zz["flop_all_ranks"] / (sum(r["ms_median"] for r in zz["ranks"]) * 1e-3) / 1e12
+    kern_ms = sum(r["flop"] / (r["kernel_tflops"] * 1e12) for r in zz["ranks"])
+    print(json.dumps({
+        "metric": f"causal ring per-rank shares TFLOP/s, S={seq} P={RP} H=32 D=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sum(r["ms_median"] for r in zz["ranks"]), 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"every rank of a {RP}-rank ring over {seq} tokens (Hq=Hkv=32, D=128, "
+                         "bf16 inputs, fp32 out + lse), timed rank by rank; contiguous and "
+                         "zigzag splits"),
+            "parts": "ranks", "seq": seq, "P": RP, "chunk": C,
+            "flop_convention": "4*D*Hq per visible (q,k) pair, diagonal chunk counted half",
+            "per_rank": table,
+            "ring_time_ratio_contiguous_over_zigzag": round(
+                table["contiguous"]["ring_time_ms"] / zz["ring_time_ms"], 3),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_bf16_kernel",
+            "achieved": round(zz["flop_all_ranks"] / kern_ms / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(zz["flop_all_ranks"] / kern_ms / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+    }))
+
+
 def merge_repack(args, cp, torch, dq, dku, dvu, stream):
     """The bandwidth-bound kernels alone (one JSON line each run).
 
@@ -588,7 +683,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--part", choices=["both", "ring", "ulysses", "bwd", "usp", "usp_bwd",
-                                       "merge", "repack"],
+                                       "merge", "repack", "ranks"],
                     default="both",
                     help="bwd: time the backward pass of both shares instead; usp: one rank "
                          "of the 8-way Ulysses x 2-way ring hybrid; merge / repack: the "
@@ -598,21 +693,38 @@ def main():
     ap.add_argument("--layout", choices=["zigzag", "striped", "contiguous"], default="zigzag",
                     help="split of the ring share (striped: inputs permuted to striped order "
                          "once, before timing)")
-    ap.add_argument("--seq", type=int, default=S,
+    ap.add_argument("--seq", type=int, default=None,
                     help="sequence length of the ring share (--part ring only; lengths the "
                          "split does not divide are padded)")
-    ap.add_argument("--rank", type=int, default=RING_RANK, choices=range(2 * P),
-                    help="the virtual rank whose share is timed (ring: 0..7, usp: 0..15)")
+    ap.add_argument("--rank", type=int, default=RING_RANK, choices=range(-1, 2 * P),
+                    help="the virtual rank whose share is timed (ring: 0..P-1 or -1 for "
+                         "every rank at once, usp: 0..15)")
+    ap.add_argument("--ring-p", type=int, default=None,
+                    help="ranks of the ring (--part ring and --part ranks only)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="before warm-up, copy 1 GiB device to device once (a plain copy "
                          "kernel of known size that scales HBM byte counters)")
     args = ap.parse_args()
-    if args.part not in ("usp", "usp_bwd") and args.rank >= P:
-        ap.error(f"--rank must be below {P} for the ring share")
-    if args.seq != S and args.part != "ring":
-        ap.error("--seq applies to --part ring only")
+    if args.part == "ranks":       # the 64K per-rank comparison: 4 ranks over 65536 tokens
+        args.seq = 65536 if args.seq is None else args.seq
+        args.ring_p = 4 if args.ring_p is None else args.ring_p
+    args.seq = S if args.seq is None else args.seq
+    args.ring_p = P if args.ring_p is None else args.ring_p
+    RP = args.ring_p
+    if RP != P and args.part not in ("ring", "ranks"):
+        ap.error("--ring-p applies to --part ring and --part ranks only")
+    if not 1 <= RP <= 64:
+        ap.error("--ring-p must be in [1, 64]")
+    if args.part not in ("usp", "usp_bwd") and args.rank >= RP:
+        ap.error(f"--rank must be below {RP} for the ring share")
+    if args.rank < 0 and args.part != "ring":
+        ap.error("--rank -1 (every rank) applies to --part ring only")
+    if args.seq != S and args.part not in ("ring", "ranks"):
+        ap.error("--seq applies to --part ring and --part ranks only")
     if not 1 <= args.seq <= S:
         ap.error(f"--seq must be in [1, {S}]")
+    if args.part == "ranks" and args.seq % (2 * RP) != 0:
+        ap.error("--part ranks needs a length that 2 * --ring-p divides")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the ring and Ulysses ranks are virtual and "
               "played on a single MI355X; run it with --gpus 1.", file=sys.stderr)
@@ -636,14 +748,14 @@ def main():
     if args.layout == "striped":
         # a striped rank holds its shard in striped order: permute once (the
         # padding rows, if any, repeat the last row; they are never read)
-        order = torch.cat([torch.from_numpy(cp.cp_layout_index("striped", seq, P, r).astype("int64"))
-                           for r in range(P)]).clamp_(max=seq - 1).to(dev)
+        order = torch.cat([torch.from_numpy(cp.cp_layout_index("striped", seq, RP, r).astype("int64"))
+                           for r in range(RP)]).clamp_(max=seq - 1).to(dev)
         rq, rk, rv = dq[order].contiguous(), dk[order].contiguous(), dv[order].contiguous()
         del order
     else:
         rq, rk, rv = dq[:seq], dk[:seq], dv[:seq]
 
-    rows = cp.padded_length(seq, P, args.layout) // P
+    rows = cp._ring_rows(seq, RP, cp.LAYOUTS[args.layout], args.rank)[1]
     ring_out = torch.empty(rows, HQ, D, device=dev, dtype=torch.float32)
     ring_lse = torch.empty(HQ, rows, device=dev, dtype=torch.float32)
     hp, hkp = HQ // P, HKV_ULY // P
@@ -659,7 +771,7 @@ def main():
 
     def step():
         if args.part in ("both", "ring"):
-            cp.cp_ring_fwd(rq, rk, rv, P, args.layout, args.rank, out=ring_out, lse=ring_lse,
+            cp.cp_ring_fwd(rq, rk, rv, RP, args.layout, args.rank, out=ring_out, lse=ring_lse,
                            stream=stream, seq_len=seq)
             if timing[0] and len(ring_done) < args.steps:
                 ev = torch.cuda.Event(enable_timing=True)
@@ -682,6 +794,9 @@ def main():
 
     if args.part == "usp":
         usp(args, cp, torch, dq, dku, dvu, stream)
+        return
+    if args.part == "ranks":
+        rank_sweep(args, cp, torch, dq, dk, dv, stream, args.seq, RP)
         return
     if args.part in ("merge", "repack"):
         merge_repack(args, cp, torch, dq, dku, dvu, stream)
@@ -720,11 +835,11 @@ def main():
     perm_ms, perm_n = cp.cp_timing_read(cp.CP_KERNEL_PERMUTE)
     cp.cp_timing_enable(False)
 
-    flop_ring = (plan_flop(cp, seq, HQ, D, P, args.layout, args.rank)
+    flop_ring = (plan_flop(cp, seq, HQ, D, RP, args.layout, args.rank)
                  if args.part in ("both", "ring") else 0.0)
     flop_uly = ulysses_share_flop(S, hp, D) if args.part in ("both", "ulysses") else 0.0
     flop_step = flop_ring + flop_uly
-    ring_exact = (plan_flop_exact(cp, seq, HQ, D, P, args.layout, args.rank)
+    ring_exact = (plan_flop_exact(cp, seq, HQ, D, RP, args.layout, args.rank)
                   if args.part in ("both", "ring") else 0.0)
     flop_exact = (None if ring_exact is None else ring_exact + (
         4.0 * D * hp * S * (S + 1) / 2.0 if args.part in ("both", "ulysses") else 0.0))
@@ -754,14 +869,18 @@ def main():
                          "rank (S=131072, Hq=Hkv=32, D=128, P=8, 16 chunks of 8192) plus "
                          "Ulysses GQA rank (Hq=32, Hkv=8, P=8 -> 4 q heads on 1 KV head over "
                          "all 131072 tokens); bf16 inputs, fp32 out + lse"
-                         if (args.layout, args.rank, seq) == ("zigzag", RING_RANK, S) else
-                         f"as the default workload with ring rank {args.rank} of the "
-                         f"{args.layout} split over {seq} tokens"),
+                         if (args.layout, args.rank, seq, RP) == ("zigzag", RING_RANK, S, P)
+                         and args.part == "both" else
+                         f"{args.part}: ring " + ("every rank" if args.rank < 0 else
+                                                  f"rank {args.rank}")
+                         + f" of the {RP}-rank {args.layout} split over {seq} tokens "
+                         "(Hq=Hkv=32, D=128)"
+                         + (" plus the Ulysses GQA rank" if args.part == "both" else "")),
             "parts": args.part,
             "ring_layout": args.layout,
             "ring_rank": args.rank,
             "ring_seq": seq,
-            "S": S, "Hq": HQ, "Hkv_ring": HQ, "Hkv_ulysses": HKV_ULY, "D": D, "P": P,
+            "S": S, "Hq": HQ, "Hkv_ring": HQ, "Hkv_ulysses": HKV_ULY, "D": D, "P": RP,
             "flop_per_step": flop_step,
             "flop_convention": "4*D*Hq per visible (q,k) pair, diagonal chunk counted half",
             "flop_per_step_exact": flop_exact,
@@ -783,7 +902,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4) if attn_tflops else None,
-            "traffic": recorded_traffic(),
+            "traffic": recorded_traffic(workload=workload_key(args.part, args.layout, args.rank,
+                                                              seq, RP)),
             "traffic_unit": "bytes per launch (HBM read + write, calibrated)",
             "launches": attn_n,
             "avg_launch_ms": round(attn_ms / max(attn_n, 1), 4),

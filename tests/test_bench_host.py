@@ -53,16 +53,49 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
-def test_recorded_traffic_follows_the_kernel_source(tmp_path):
+def test_recorded_traffic_follows_the_kernel_source_and_workload(tmp_path):
     src = tmp_path / "kernel.hip"
     src.write_text("// some kernel\n")
     digest = hashlib.sha256(src.read_bytes()).hexdigest()
+    key = bench.workload_key("both", "zigzag", 0, 131072, 8)
     prof = tmp_path / "traffic.md"
-    prof.write_text(f"# summary\n\ntraffic_bytes_per_launch: 1234\nkernel_source_sha256: {digest}\n")
-    assert bench.recorded_traffic(str(prof), str(src)) == 1234.0
+    prof.write_text(f"# summary\n\ntraffic_bytes_per_launch: 1234\nworkload_key: {key}\n"
+                    f"kernel_source_sha256: {digest}\n")
+    assert bench.recorded_traffic(str(prof), str(src), key) == 1234.0
+    # another workload of the same kernel: no figure
+    for other in (bench.workload_key("ring", "zigzag", 0, 131072, 8),
+                  bench.workload_key("both", "striped", 0, 131072, 8),
+                  bench.workload_key("both", "zigzag", 3, 131072, 8),
+                  bench.workload_key("both", "zigzag", 0, 131071, 8),
+                  bench.workload_key("ring", "zigzag", -1, 32768, 8), None):
+        assert bench.recorded_traffic(str(prof), str(src), other) is None
     src.write_text("// the kernel changed\n")
-    assert bench.recorded_traffic(str(prof), str(src)) is None
-    assert bench.recorded_traffic(str(tmp_path / "missing.md"), str(src)) is None
+    assert bench.recorded_traffic(str(prof), str(src), key) is None
+    assert bench.recorded_traffic(str(tmp_path / "missing.md"), str(src), key) is None
+
+
+def test_work_model_units_of_the_64k_comparison():
+    """The per-rank sweep reports work in the handbook's units (C x C chunk
+    pairs of the 2P-way split, diagonal half): contiguous [2, 6, 10, 14] and
+    zigzag [8, 8, 8, 8] at P = 4, as the page's work snippet prints."""
+    import context_parallelism_cp_amd as cp
+    import pins
+    g = pins.load_golden("work_p4.txt")
+    S, P = 65536, 4
+    C = S // (2 * P)
+    unit = 4.0 * 128 * 32 * C * C
+    for layout in ("contiguous", "zigzag"):
+        got = [bench.plan_flop(cp, S, 32, 128, P, layout, r) / unit for r in range(P)]
+        assert got == [float(x) for x in g[layout]]
+
+
+def test_bench_argument_guards():
+    for extra, msg in ((["--part", "ulysses", "--ring-p", "4"], "--ring-p"),
+                       (["--part", "ranks", "--seq", "65535"], "divides"),
+                       (["--part", "bwd", "--rank", "-1"], "every rank")):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *extra],
+                           capture_output=True, text=True, timeout=120)
+        assert r.returncode == 2 and msg in r.stderr, r.stderr
 
 
 def test_exact_count_closed_forms():
