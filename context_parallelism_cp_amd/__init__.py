@@ -57,6 +57,8 @@ SIGNATURES = {
                           _I64, _I, _I, _I, _P],
     "cp_ring_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I, _I,
                     _I, _P],
+    "cp_ring_bwd_noalloc": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _I,
+                            _I, _I, _P],
     "cp_seq_to_head": [_P, _P, _I64, _I, _I, _I, _I, _SZ, _P],
     "cp_head_to_seq": [_P, _P, _I64, _I, _I, _I, _I, _SZ, _P],
     "cp_usp_fwd_workspace": [_I64, _I, _I, _I, _I, _I, _I, _I, _I,
@@ -301,6 +303,21 @@ def cp_ring_bwd(q, k, v, out, lse, dout, P: int, layout="zigzag", rank: int = -1
                            lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                            dv.data_ptr(), dvec.data_ptr(), S, Hq, Hkv, D, P, lay, rank,
                            int(bool(causal)), _dtype_code(q), _stream(q, stream)))
+    return dq, dk, dv
+
+
+def cp_ring_bwd_noalloc(q, k, v, out, lse, dout, dq, dk, dv, P: int, layout="zigzag",
+                        rank: int = -1, causal: bool = True, stream=None, seq_len=None):
+    """cp_ring_bwd with its dvec scratch in the library's own device array:
+    the library allocates nothing (dq, dk, dv are the caller's buffers).
+    Calls that overlap on one GPU race (one array per GPU)."""
+    S, Hq, Hkv, D, lay, rows, dq, dk, dv, specs = _ring_bwd_args(
+        q, k, v, out, lse, dout, P, layout, rank, seq_len, dq, dk, dv)
+    _checked(q, *specs)
+    _check(lib.cp_ring_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), S, Hq, Hkv, D, P, lay, rank, int(bool(causal)),
+                                   _dtype_code(q), _stream(q, stream)))
     return dq, dk, dv
 
 

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libcpattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["cp_api.cpp", "attn_bf16.hip", "attn_f32.hip", "lse_merge.hip", "repack.hip",
-           "bwd_f32.hip", "bwd_bf16.hip"]
+           "bwd_f32.hip", "bwd_bf16.hip", "scratch.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

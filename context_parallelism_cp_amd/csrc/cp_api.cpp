@@ -789,6 +789,34 @@ int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out, c
     return rc ? rc : ok();
 }
 
+int cp_ring_bwd_noalloc(const void *q, const void *k, const void *v, const float *out,
+                        const float *lse, const void *dout, float *dq, float *dk, float *dv,
+                        int64_t S, int Hq, int Hkv, int D, int P, cp_layout layout, int rank,
+                        int causal, cp_dtype dtype, void *stream)
+{
+    // dvec comes from the library's scratch array, which no caller buffer can
+    // overlap: the checks run with lse (same shape, read only) in its place
+    int rc = ring_bwd_check(q, k, v, out, lse, dout, dq, dk, dv, lse, S, Hq, Hkv, D, P, layout,
+                            rank, dtype);
+    if (rc)
+        return rc;
+    const int64_t need = (int64_t)Hq * ring_rows_out(S, P, layout, rank);
+    if (need > kScratchFloats)
+        return fail(CP_ERR_WORKSPACE,
+                    "cp_ring_bwd_noalloc keeps Hq x output rows = %lld floats of dvec in its "
+                    "scratch array, which holds %lld; use cp_ring_bwd with a caller buffer",
+                    (long long)need, (long long)kScratchFloats);
+    if (S == 0)
+        return ok();
+    float *dvec = nullptr;
+    const hipError_t e = scratch_floats(&dvec);
+    if (e != hipSuccess)
+        return fail(CP_ERR_HIP, "scratch array lookup failed: %s", hipGetErrorString(e));
+    rc = ring_bwd_run(q, k, v, out, lse, dout, dq, dk, dv, dvec, S, Hq, Hkv, D, P, layout, rank,
+                      causal, dtype, (hipStream_t)stream);
+    return rc ? rc : ok();
+}
+
 // One rank's head share, row by row: to_head copies y[t] <- x[t][p*Hp, (p+1)*Hp),
 // otherwise y[t][p*Hp, (p+1)*Hp) <- x[t], for rows t in [0, rows).
 static int head_share_copy(bool to_head, const void *x, void *y, int64_t rows, int H, int D,

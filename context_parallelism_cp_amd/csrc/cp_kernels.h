@@ -105,4 +105,10 @@ hipError_t launch_fill_2d(float *p, int64_t ld, int64_t n_rows, int64_t n_cols, 
                           hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdLaunch &b, hipStream_t stream);
 
+// The library's device scratch array (16 MiB of floats per GPU, held from
+// the code object's load until the process ends): *ptr receives its address
+// on the current device.  Calls on one device share the array.
+constexpr int64_t kScratchFloats = (int64_t)1 << 22;
+hipError_t scratch_floats(float **ptr);
+
 }  // namespace cpattn

@@ -231,6 +231,26 @@ int cp_ring_bwd(const void *q, const void *k, const void *v, const float *out,
                 int rank, int causal, cp_dtype dtype, void *stream);
 
 /*
+ * cp_ring_bwd_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): cp_ring_bwd with the same arguments except dvec, and the
+ * same results, its dvec scratch kept in a device array of the library's
+ * own.  It allocates nothing and calls no allocating routine.
+ * Limit: Hq * (rows of out) <= 4194304 floats (16 MiB, e.g. 32 heads over
+ * 131072 rows); a larger call returns CP_ERR_WORKSPACE before any HIP call.
+ * Each GPU holds one such array (looked up on the current device at the
+ * first call there, held until the process ends) and every call on that
+ * GPU uses it: calls that overlap in time on one GPU (different streams or
+ * host threads) race and must be ordered, e.g. on one stream.  Each call
+ * rewrites every entry it reads, so nothing carries over between calls.
+ * Errors: as cp_ring_bwd, plus CP_ERR_WORKSPACE.
+ */
+int cp_ring_bwd_noalloc(const void *q, const void *k, const void *v, const float *out,
+                        const float *lse, const void *dout, float *dq, float *dk, float *dv,
+                        int64_t S, int Hq, int Hkv, int D, int P, cp_layout layout, int rank,
+                        int causal, cp_dtype dtype, void *stream);
+
+/*
  * cp_seq_to_head / cp_head_to_seq -- the Ulysses layout changes of [HB],
  * section "Ulysses：在序列和头之间转置", done as local repacks: the all-to-all
  * between P ranks becomes a strided copy on one GPU.  Elements are opaque

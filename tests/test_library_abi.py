@@ -433,3 +433,18 @@ def test_binding_refuses_wrong_buffers_before_any_launch():
     _raises(cp.CP_ERR_UNSUPPORTED, cp.cp_head_to_seq, _bf16(4, 64, 2, 128), x, 4, -1,
             match="GPU")
 
+
+def test_ring_bwd_noalloc_limit_before_any_hip_call():
+    """The allocation-free ring backward keeps dvec (Hq x output rows floats)
+    in a 2^22-float array of the library's: a larger call is refused with
+    CP_ERR_WORKSPACE before any HIP call, and argument errors come first."""
+    f = cp.lib.cp_ring_bwd_noalloc
+    a = [(1 << 40) + i * (1 << 36) for i in range(9)]   # q k v out lse dout dq dk dv
+    Z, B = cp.CP_LAYOUT_ZIGZAG, cp.CP_BF16
+    assert f(*a, 131072, 40, 8, 128, 8, Z, -1, 1, B, None) == cp.CP_ERR_WORKSPACE
+    assert "4194304" in cp.cp_last_error() and "cp_ring_bwd" in cp.cp_last_error()
+    assert f(*a, 1 << 20, 40, 8, 128, 8, Z, 3, 1, B, None) == cp.CP_ERR_WORKSPACE
+    assert f(None, *a[1:], 4096, 32, 8, 128, 8, Z, -1, 1, B, None) == cp.CP_ERR_NULL
+    assert f(*a, 4096, 32, 8, 100, 8, Z, -1, 1, B, None) == cp.CP_ERR_UNSUPPORTED
+    assert f(*a, 4096, 32, 8, 128, 8, Z, 8, 1, B, None) == cp.CP_ERR_SHAPE
+    assert f(*a, 0, 32, 8, 128, 8, Z, -1, 1, B, None) == cp.CP_OK
