@@ -10,10 +10,10 @@ Sources, all on the handbook page "上下文并行：Ring Attention 与 Ulysses"
   [r*C, (r+1)*C) with C = S/P; at step t it holds the KV block of rank
   src = (r - t) mod P, computes only when src <= r, merges with the
   log-sum-exp rule and passes the block to rank r+1;
-* section "之字形切分" (zigzag split): the sequence is cut into 2P chunks,
-  rank r takes chunks r and 2P-1-r; the contiguous split of the same
-  snippet gives rank r chunks 2r and 2r+1; the work of a query chunk q is
-  q + 1/2 KV chunks (the diagonal chunk counts half);
+* section "之字形切分" (zigzag split): the sequence is cut into 2P chunks;
+  the zigzag split gives each rank one chunk from the front and its mirror
+  from the back, the contiguous split gives consecutive chunks; causal work
+  counts the key chunks a query chunk sees, the diagonal one as half;
 * section "Ulysses：在序列和头之间转置": seq_to_head and head_to_seq are
   a reshape/transpose followed by ``all_to_all_single``.
 
@@ -35,6 +35,8 @@ Readings where the page is silent (the page has no zigzag ring code):
 """
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 
 from .attention import attention, attention_at, attention_bwd, attention_bwd_at, lse_merge
@@ -44,20 +46,33 @@ SKIP, FULL, DIAG = 0, 1, 2
 
 
 # ----------------------------------------------------------------- splits
-def split_contiguous(P: int) -> dict[int, list[int]]:
-    """Zigzag-section snippet: contiguous split in 2P chunks, rank r gets [2r, 2r+1]."""
-    return {r: [2 * r, 2 * r + 1] for r in range(P)}
+def rank_chunks(layout: int, P: int, rank: int) -> list[int]:
+    """The chunks of the 2P-way split that ``rank`` holds, in its local
+    order (the zigzag section's two splits, stated as ownership rules):
+
+    * contiguous: chunks are handed out two at a time in sequence order, so
+      chunk c belongs to rank c // 2;
+    * zigzag: chunk c and its mirror chunk 2P-1-c belong to one rank, the
+      one numbered by the nearer end, min(c, 2P-1-c).
+    """
+    n = 2 * P
+    if layout == CONTIGUOUS:
+        owner = [c // 2 for c in range(n)]
+    elif layout == ZIGZAG:
+        owner = [min(c, n - 1 - c) for c in range(n)]
+    else:
+        raise ValueError("rank_chunks covers the contiguous and zigzag splits")
+    return [c for c in range(n) if owner[c] == rank]
 
 
-def split_zigzag(P: int) -> dict[int, list[int]]:
-    """Zigzag-section snippet: rank r gets chunk r and chunk 2P-1-r."""
-    return {r: [r, 2 * P - 1 - r] for r in range(P)}
-
-
-def work(query_chunks) -> float:
-    """Zigzag-section work model: a query chunk with index q needs q full KV
-    chunks plus the diagonal one, which counts half."""
-    return sum(q + 0.5 for q in query_chunks)
+def causal_units(query_chunks, n_chunks: int) -> float:
+    """Causal work of the given query chunks, in units of one full
+    chunk-by-chunk block (the zigzag section's work model): in the
+    n_chunks x n_chunks grid of blocks, query chunk i needs the blocks of
+    key chunks before it in full and the one on the diagonal, whose visible
+    pairs are half of it."""
+    grid = np.tril(np.ones((n_chunks, n_chunks)), k=-1) + 0.5 * np.eye(n_chunks)
+    return float(grid[list(query_chunks)].sum())
 
 
 def padded_length(S: int, P: int, layout: int) -> int:
@@ -86,14 +101,14 @@ def layout_index(layout: int, S: int, P: int, rank: int) -> np.ndarray:
         return np.arange(rank, S, P, dtype=np.int64)
     C = S // (2 * P)
     return np.concatenate([np.arange(c * C, (c + 1) * C, dtype=np.int64)
-                           for c in split_zigzag(P)[rank]])
+                           for c in rank_chunks(ZIGZAG, P, rank)])
 
 
 def _chunks(layout: int, S: int, P: int, rank: int):
     """(chunk ids, chunk length) of ``rank`` for the ring schedule."""
     if layout == CONTIGUOUS:
         return [rank], S // P
-    return split_zigzag(P)[rank], S // (2 * P)
+    return rank_chunks(ZIGZAG, P, rank), S // (2 * P)
 
 
 def ring_plan(S: int, P: int, layout: int, rank: int, causal: bool = True):
@@ -154,34 +169,30 @@ def _real_rows(S: int, P: int, rank: int, C: int) -> int:
 
 # ---------------------------------------------------------------- the ring
 def ring_contiguous(q, k, v, P: int, causal: bool = True):
-    """The ring section's loop, run for every virtual rank in turn.
+    """The ring section's schedule on P virtual ranks: rank r owns rows
+    [r*C, (r+1)*C); at step t it holds the KV block of rank (r - t) mod P
+    (blocks move one rank to the right per step).  Under the causal mask a
+    block of a later rank lies wholly after the rank's queries and is not
+    computed; the blocks computed are folded into one result with the
+    log-sum-exp merge, in the order the steps bring them.
 
     Returns (outs, lses, computed): per rank its local out [C, Hq, D],
-    lse [Hq, C] and the number of KV blocks it actually computed.
+    lse [Hq, C] and the number of KV blocks it computed.
     """
     S = q.shape[0]
     C = S // P
+    owned = [slice(r * C, (r + 1) * C) for r in range(P)]
+    # source rank of the block each rank holds at each step
+    held = np.array([[(r - t) % P for t in range(P)] for r in range(P)])
     outs, lses, computed = [], [], []
-    blocks = [(k[r * C:(r + 1) * C], v[r * C:(r + 1) * C]) for r in range(P)]
-    for rank in range(P):
-        q_l = q[rank * C:(rank + 1) * C]
-        out = lse = None
-        n = 0
-        src = rank
-        for step in range(P):
-            if src <= rank or not causal:
-                kb, vb = blocks[src]          # the block that arrived this step
-                o, l = attention(q_l, kb, vb, causal=causal,
-                                 q_offset=rank * C, k_offset=src * C)
-                if out is None:
-                    out, lse = o, l
-                else:
-                    out, lse = lse_merge(out, lse, o, l)
-                n += 1
-            src = (src - 1) % P               # receive from the left
-        outs.append(out)
-        lses.append(lse)
-        computed.append(n)
+    for r in range(P):
+        sources = [int(s) for s in held[r] if not causal or s <= r]
+        parts = [attention(q[owned[r]], k[owned[s]], v[owned[s]], causal=causal,
+                           q_offset=r * C, k_offset=s * C) for s in sources]
+        o, l = functools.reduce(lambda acc, part: lse_merge(*acc, *part), parts)
+        outs.append(o)
+        lses.append(l)
+        computed.append(len(parts))
     return outs, lses, computed
 
 
@@ -194,7 +205,7 @@ def ring_zigzag(q, k, v, P: int, causal: bool = True):
     """
     S, Hq, D = q.shape
     C = S // (2 * P)
-    split = split_zigzag(P)
+    split = [rank_chunks(ZIGZAG, P, r) for r in range(P)]
     outs, lses, units = [], [], []
     for rank in range(P):
         state = {}

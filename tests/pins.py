@@ -266,16 +266,21 @@ def pin_global_max_route(attn, global_max_attn):
 
 
 # ----------------------------------------------------------- schedules
-def pin_work(split_contiguous, split_zigzag, work):
+def pin_work(rank_chunks, causal_units, CONTIGUOUS, ZIGZAG):
+    """The zigzag section's printed work per rank for P = 4 (golden), every
+    chunk owned exactly once, and the closed forms 4r + 2 (contiguous) and
+    2P (zigzag) that summing the diagonal-half block grid gives."""
     g = load_golden("work_p4.txt")
     P = 4
-    assert [work(split_contiguous(P)[r]) for r in range(P)] == g["contiguous"]
-    assert [work(split_zigzag(P)[r]) for r in range(P)] == g["zigzag"]
-    # every chunk owned exactly once by the splits
-    for split in (split_contiguous, split_zigzag):
+    assert [causal_units(rank_chunks(CONTIGUOUS, P, r), 2 * P) for r in range(P)] == g["contiguous"]
+    assert [causal_units(rank_chunks(ZIGZAG, P, r), 2 * P) for r in range(P)] == g["zigzag"]
+    for layout in (CONTIGUOUS, ZIGZAG):
         for PP in (2, 4, 8):
-            owned = sorted(c for r in range(PP) for c in split(PP)[r])
+            owned = sorted(c for r in range(PP) for c in rank_chunks(layout, PP, r))
             assert owned == list(range(2 * PP))
+            for r in range(PP):
+                want = 4 * r + 2 if layout == CONTIGUOUS else 2 * PP
+                assert causal_units(rank_chunks(layout, PP, r), 2 * PP) == want
 
 
 def make_qkv_page():

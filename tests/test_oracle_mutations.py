@@ -141,7 +141,8 @@ def _schedule_pins_fail(sch, att):
     import oracle.schedules as real
     failed = 0
     checks = []
-    checks.append(lambda: pins.pin_work(sch.split_contiguous, sch.split_zigzag, sch.work))
+    checks.append(lambda: pins.pin_work(sch.rank_chunks, sch.causal_units, sch.CONTIGUOUS,
+                                        sch.ZIGZAG))
 
     def ring_checks():
         from oracle.attention import attention
@@ -187,26 +188,33 @@ def _schedule_pins_fail(sch, att):
     for c in checks:
         try:
             c()
-        except (AssertionError, ValueError, IndexError, KeyError):
+        except (AssertionError, ValueError, IndexError, KeyError, TypeError):
             failed += 1
     return failed
 
 
 def pins_split_zigzag(P):
     """The zigzag split as the page's prose states it: rank r takes the r-th
-    chunk and the (r+1)-th chunk from the end."""
-    return {r: [r, 2 * P - (r + 1)] for r in range(P)}
+    chunk and the (r+1)-th chunk from the end (counting from the front, chunk
+    2P - r - 1)."""
+    out = {}
+    for r in range(P):
+        nth_from_end = r + 1
+        out[r] = [r, 2 * P - nth_from_end]
+    return out
 
 
 SCHEDULE_MUTANTS = [
-    ("zigzag second chunk", "return {r: [r, 2 * P - 1 - r] for r in range(P)}",
-     "return {r: [r, 2 * P - 2 - r] for r in range(P)}"),
-    ("contiguous split", "return {r: [2 * r, 2 * r + 1] for r in range(P)}",
-     "return {r: [r, r + 1] for r in range(P)}"),
-    ("work counts diagonal fully", "return sum(q + 0.5 for q in query_chunks)",
-     "return sum(q + 1.0 for q in query_chunks)"),
-    ("ring skip rule", "if src <= rank or not causal:", "if src < rank or not causal:"),
-    ("ring key offset", "q_offset=rank * C, k_offset=src * C)", "q_offset=rank * C, k_offset=rank * C)"),
+    ("zigzag mirror owner", "owner = [min(c, n - 1 - c) for c in range(n)]",
+     "owner = [min(c, n - 2 - c) % P for c in range(n)]"),
+    ("contiguous owner", "owner = [c // 2 for c in range(n)]", "owner = [c % P for c in range(n)]"),
+    ("work counts diagonal fully", "+ 0.5 * np.eye(n_chunks)", "+ 1.0 * np.eye(n_chunks)"),
+    ("work grid upper triangle", "np.tril(np.ones((n_chunks, n_chunks)), k=-1)",
+     "np.triu(np.ones((n_chunks, n_chunks)), k=1)"),
+    ("ring skip rule", "if not causal or s <= r]", "if not causal or s < r]"),
+    ("ring key offset", "q_offset=r * C, k_offset=s * C)", "q_offset=r * C, k_offset=r * C)"),
+    ("ring one step short", "held = np.array([[(r - t) % P for t in range(P)]",
+     "held = np.array([[(r - t) % P for t in range(P - 1)]"),
     ("zigzag skip rule", "if causal and kc > qc:", "if causal and kc >= qc:"),
     ("plan classification", "elif kc == qc:\n                        kind = DIAG",
      "elif kc == qc + 1:\n                        kind = DIAG"),

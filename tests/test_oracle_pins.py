@@ -85,9 +85,10 @@ def test_c_oracle_rejects_bad_arguments():
 
 # ------------------------------------------------------------- schedules
 def test_work_model_golden():
-    pins.pin_work(R.split_contiguous, R.split_zigzag, R.work)
+    pins.pin_work(R.rank_chunks, R.causal_units, R.CONTIGUOUS, R.ZIGZAG)
     for P in (2, 4, 8, 16):
-        assert all(R.work(R.split_zigzag(P)[r]) == 2 * P for r in range(P))
+        assert all(R.causal_units(R.rank_chunks(R.ZIGZAG, P, r), 2 * P) == 2 * P
+                   for r in range(P))
 
 
 def test_page_make_qkv_is_the_seeded_generator():
@@ -119,7 +120,7 @@ def test_ring_zigzag_equals_single_pass_and_balances(P, S):
         np.testing.assert_allclose(lses[r], ref_l[:, idx], rtol=0, atol=1e-12)
         # the page: with the zigzag split every rank does the same work at every step
         assert units[r] == [2.0] * P
-        assert sum(units[r]) == R.work(R.split_zigzag(P)[r])
+        assert sum(units[r]) == R.causal_units(R.rank_chunks(R.ZIGZAG, P, r), 2 * P)
 
 
 def test_ring_noncausal_equals_single_pass():
@@ -156,10 +157,10 @@ def test_ring_plan_counts_and_coverage(P):
         n_comp = sum(1 for p in mine if p[8] != R.SKIP)
         assert n_comp == 2 * P + 1          # P=4: 9, P=8: 17 launches per rank
         units = sum(1.0 if p[8] == R.FULL else 0.5 for p in mine if p[8] != R.SKIP)
-        assert units == R.work(R.split_zigzag(P)[r])
+        assert units == R.causal_units(R.rank_chunks(R.ZIGZAG, P, r), 2 * P)
         # each (q chunk, k chunk <= q chunk) pair appears exactly once
         comp = sorted((p[2], p[3]) for p in mine if p[8] != R.SKIP)
-        want = sorted((qc, kc) for qc in R.split_zigzag(P)[r] for kc in range(qc + 1))
+        want = sorted((qc, kc) for qc in R.rank_chunks(R.ZIGZAG, P, r) for kc in range(qc + 1))
         assert comp == want
     cont = R.ring_plan(S, P, R.CONTIGUOUS, -1)
     counts = [sum(1 for p in cont if p[0] == r and p[8] != R.SKIP) for r in range(P)]
