@@ -92,7 +92,8 @@ struct TileMap {
     int32_t start[kMaxQSegs + 1];       // prefix sum of row tiles over the segments
     int32_t total;                      // row tiles in the launch
     int32_t use_order;                  // order[] valid (total <= kMaxOrder)
-    int32_t xcd_mode;                   // 0 linear, 1 Hq % 8 == 0, 2 8 % Hq == 0
+    int32_t xcd_mode;                   // 0 linear, 1 Hq % 8 == 0, 2 8 % Hq == 0, 3 bands
+    int32_t band;                       // row tiles per band (xcd_mode 3)
     int32_t slots;                      // tile positions walked per XCD lane
     int32_t pack;                       // query heads per workgroup (they share one KV head)
     uint16_t order[kMaxOrder];          // tile positions, heaviest first
@@ -230,6 +231,24 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
             const int xph = kXcds / n_hg;
             hg = x % n_hg;
             tp = s * xph + x / n_hg;
+        } else if (tm.xcd_mode == 3) {
+            // one causal segment: its row tiles cut into 2 * xph bands whose
+            // sizes differ by one at most; XCD lane j of the head group takes
+            // band 2*xph-1-j, then band j, each from its last row tile down
+            // (equal work per XCD; the workgroups an XCD holds at a time are
+            // neighbouring row tiles that stream the same keys at about the
+            // same time)
+            const int x = bid % kXcds, s = bid / kXcds;
+            const int xph = kXcds / n_hg;
+            const int nb = 2 * xph;                    // band k: [k*T/nb, (k+1)*T/nb)
+            const int j = x / n_hg;
+            hg = x % n_hg;
+            const int kh = nb - 1 - j;
+            const int h0 = (int)((int64_t)kh * tm.total / nb);
+            const int sh = (int)((int64_t)(kh + 1) * tm.total / nb) - h0;
+            const int l0 = (int)((int64_t)j * tm.total / nb);
+            const int sl = (int)((int64_t)(j + 1) * tm.total / nb) - l0;
+            tp = s < sh ? h0 + (sh - 1 - s) : (s - sh < sl ? l0 + (sl - 1 - (s - sh)) : tm.total);
         } else {
             hg = bid / tm.total;
             tp = bid % tm.total;
@@ -249,7 +268,7 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
         ++s;
     const QSeg &qs = a.qs[s];
     int tile = tile_lin - tm.start[s];
-    if (!tm.use_order && a.causal)   // without the table: later rows (more keys) first
+    if (!tm.use_order && a.causal && tm.xcd_mode != 3)   // without the table: later rows first
         tile = (tm.start[s + 1] - tm.start[s]) - 1 - tile;
     const int64_t tile_row0 = (int64_t)tile * bm;
     const int g = h / (a.Hq / a.Hkv);              // the same for every wavefront
@@ -647,6 +666,11 @@ hipError_t launch_attn_bf16(const AttnLaunch &a, hipStream_t stream)
     if (n_hg % kXcds == 0) {
         tm.xcd_mode = 1;
         grid = total * n_hg;
+    } else if (kXcds % n_hg == 0 && !tm.use_order && a.causal && a.n_q == 1) {
+        tm.xcd_mode = 3;
+        const int bands = 2 * (kXcds / n_hg);
+        tm.band = (int32_t)((total + bands - 1) / bands);   // largest band
+        grid = (int64_t)kXcds * 2 * tm.band;
     } else if (kXcds % n_hg == 0) {
         tm.xcd_mode = 2;
         const int xph = kXcds / n_hg;

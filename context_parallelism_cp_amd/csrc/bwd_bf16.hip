@@ -199,15 +199,52 @@ constexpr int kDqStage = 2 * kTileBytes;               // K then V
 __shared__ __attribute__((aligned(1024))) char g_dq[3 * kDqStage];
 constexpr int kDqLoads = 2 * (kTileRows / 4) / kDqWaves;   // tile loads per wavefront
 
+// Order of the dq launch's (head, row tile) units over the XCDs (workgroup
+// b runs on XCD b % 8, as its slot b / 8):
+//   mode 0: the units head-major, later row tiles (more keys under the
+//     causal mask) first within a head, cut into 8 contiguous runs of
+//     per_xcd: the workgroups an XCD holds at a time stream one head's K/V;
+//   mode 1 (causal, KV heads not a multiple of 8): per head, the row tiles
+//     cut into 16 bands (sizes differing by one at most, `band` the
+//     largest); XCD x takes band 15 - x, then band x, each from its last
+//     tile down (equal work per XCD; an XCD's
+//     workgroups are neighbouring row tiles that stream the same keys at
+//     about the same time).
+struct DqWork {
+    int mode;
+    int n_row_tiles;
+    int per_xcd;      // mode 0
+    int band;         // mode 1
+};
+
 __global__ __launch_bounds__(kDqThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dq_kernel(BwdLaunch b, int n_row_tiles)
+void bwd_dq_kernel(BwdLaunch b, DqWork w)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l32 = lane & 31, hi = lane >> 5;
-    // later row tiles (more visible keys under the causal mask) first
-    const int h = blockIdx.x % b.Hq;
-    const int tile = n_row_tiles - 1 - (int)(blockIdx.x / b.Hq);
+    const int n_row_tiles = w.n_row_tiles;
+    int h, tile;
+    {
+        const int x = blockIdx.x % 8, slot = blockIdx.x / 8;
+        if (w.mode == 0) {
+            const int64_t lin = (int64_t)x * w.per_xcd + slot;
+            if (slot >= w.per_xcd || lin >= (int64_t)n_row_tiles * b.Hq)
+                return;
+            h = (int)(lin / n_row_tiles);
+            tile = n_row_tiles - 1 - (int)(lin % n_row_tiles);
+        } else {
+            // band k holds row tiles [k*M/16, (k+1)*M/16)
+            const int M = n_row_tiles;
+            h = slot / (2 * w.band);
+            const int s = slot % (2 * w.band);
+            const int h0 = (15 - x) * M / 16, sh = (16 - x) * M / 16 - h0;
+            const int l0 = x * M / 16, sl = (x + 1) * M / 16 - l0;
+            tile = s < sh ? h0 + (sh - 1 - s) : (s - sh < sl ? l0 + (sl - 1 - (s - sh)) : M);
+            if (h >= b.Hq || tile >= n_row_tiles)
+                return;
+        }
+    }
     const int64_t tile_row0 = (int64_t)tile * kDqRows;
     const int g = h / (b.Hq / b.Hkv);
     const int64_t q_stride = (int64_t)b.Hq * HD, kv_stride = (int64_t)b.Hkv * HD;
@@ -369,265 +406,297 @@ void bwd_dq_kernel(BwdLaunch b, int n_row_tiles)
 }
 
 // ============================================================ dk/dv kernel
-constexpr int kKvWaves = 4;
-constexpr int kKvRows = kKvWaves * 32;                 // 128 keys
+// A workgroup of 8 wavefronts owns 128 keys of one KV head: 4 pairs of 32
+// keys, the two wavefronts of a pair on one SIMD (wavefronts w and w + 4).
+// The pair splits the work of its keys by role:
+//   role 0 keeps K^T in registers: S = Q K^T, P = exp(S - lse) (masked),
+//          dV += P^T dO; it passes P (float32) to role 1 through LDS;
+//   role 1 keeps V^T in registers: dP = dO V^T, dS = P (dP - dvec),
+//          dK += dS^T Q, one query tile behind role 0 (it reads the P that
+//          role 0 wrote before the previous barrier).
+// Each wavefront then holds one key-side operand and one accumulator pair
+// (about half of what one wavefront doing all four products needs), so two
+// fit on a SIMD and the SIMD interleaves one's matrix work with the other's
+// exponentials and waits.  Every product is the one the single-wavefront
+// form computes, in the same order.
+constexpr int kKvWaves = 8;
+constexpr int kKvPairs = 4;
+constexpr int kKvRows = kKvPairs * 32;                 // 128 keys
 constexpr int kKvThreads = kKvWaves * 64;
 constexpr int kStatBytes = 64 * 4;                     // one float per lane of the loading wave
 constexpr int kKvStage = 2 * kTileBytes + 2 * kStatBytes;   // q, dout, lse, dvec
+constexpr int kKvStages = 5;
+constexpr int kKvAhead = 3;        // tile it + 3 is requested at step it (stages - 2)
+constexpr int kPBytes = 64 * 16 * 4;                   // a pair's P: 16 floats per lane
 
-// the ring's three stages: q tile, dout tile, lse, dvec in each
-__shared__ __attribute__((aligned(1024))) char g_kv[4 * kKvStage];
+// the ring: q tile, dout tile, lse, dvec in each stage; then P, double-buffered
+__shared__ __attribute__((aligned(1024))) char g_kv[kKvStages * kKvStage];
+__shared__ __attribute__((aligned(1024))) char g_p[2 * kKvPairs * kPBytes];
 constexpr int kKvLoads = 2 * (kTileRows / 4) / kKvWaves;   // tile loads per wavefront
 constexpr int kKvLoads0 = kKvLoads + 2;                     // wavefront 0 also loads lse, dvec
 
-__global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(BwdLaunch b)
+// Work of the dk/dv launch: `units` per KV head, each one key tile or (under
+// the causal mask) the pair of key tiles t and n_key_tiles - 1 - t, whose
+// visible query rows add up to about the same count for every t.  The
+// units of all KV heads, head-major, are cut into 8 contiguous runs of
+// `per_xcd`, one per XCD (workgroup b runs on XCD b % 8), so the workgroups
+// an XCD holds at a time belong to one KV head and read the same query
+// tiles.
+struct KvWork {
+    int units;        // units per KV head
+    int per_xcd;      // units per XCD
+    int paired;       // 1: a unit is a pair of key tiles
+    int n_key_tiles;
+};
+
+__global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = wave % kKvPairs;
+    const int role = wave / kKvPairs;
     const int l32 = lane & 31, hi = lane >> 5;
-    // earlier key tiles (seen by more query rows under the causal mask) first
-    const int g = blockIdx.x % b.Hkv;
-    const int tile = (int)(blockIdx.x / b.Hkv);
-    const int64_t key_row0 = (int64_t)tile * kKvRows;
+    int g, tiles[2], n_phase;
+    {
+        const int x = blockIdx.x % 8, slot = blockIdx.x / 8;
+        const int64_t lin = (int64_t)x * w.per_xcd + slot;
+        if (slot >= w.per_xcd || lin >= (int64_t)w.units * b.Hkv)
+            return;
+        g = (int)(lin / w.units);
+        const int u = (int)(lin % w.units);
+        tiles[0] = u;
+        tiles[1] = w.n_key_tiles - 1 - u;
+        n_phase = (w.paired && tiles[1] != u) ? 2 : 1;
+    }
     const int group = b.Hq / b.Hkv;
     const int64_t q_stride = (int64_t)b.Hq * HD, kv_stride = (int64_t)b.Hkv * HD;
-    const int64_t my_key = key_row0 + wave * 32 + l32;
-    const bool key_ok = my_key < b.Sk;
-
-    // K^T and V^T fragments (B operands): key my_key, dims 16*sd + 8*hi + [0, 8)
-    bf16x8 kf[8], vf[8];
-    {
-        const int64_t r = key_ok ? my_key : 0;
-        const u32x4 *ks = (const u32x4 *)((const __bf16 *)b.k + r * kv_stride + g * HD + 8 * hi);
-        const u32x4 *vs = (const u32x4 *)((const __bf16 *)b.v + r * kv_stride + g * HD + 8 * hi);
-#pragma unroll
-        for (int sd = 0; sd < 8; ++sd) {
-            u32x4 x = ks[2 * sd], y = vs[2 * sd];
-            if (!key_ok) {
-                x = u32x4{0, 0, 0, 0};
-                y = u32x4{0, 0, 0, 0};
-            }
-            kf[sd] = __builtin_bit_cast(bf16x8, x);
-            vf[sd] = __builtin_bit_cast(bf16x8, y);
-        }
-    }
     const float scale = 1.f / sqrtf((float)HD);
     const float c = kLog2e * scale;
-
-    // query tiles that see any of the workgroup's keys
-    const int64_t first_key_pos = b.k_offset + key_row0;
-    int64_t q_begin = 0;
-    if (b.causal)
-        q_begin = min(max(first_key_pos - b.q_offset, (int64_t)0), b.Sq);
-    const int qt_begin = (int)(q_begin / kTileRows);
-    const int n_qt = (int)((b.Sq + kTileRows - 1) / kTileRows) - qt_begin;
-    const int n_iter = n_qt > 0 ? n_qt * group : 0;        // (head, query tile) pairs
-
+    const int n_qt_all = (int)((b.Sq + kTileRows - 1) / kTileRows);
     const uint32_t ring = (uint32_t)(uintptr_t)(char LDS_AS *)g_kv;
-    auto issue = [&](int it) {
-        if (it < n_iter) {
-            const int h = g * group + it / n_qt;
-            const int64_t q0 = (int64_t)(qt_begin + it % n_qt) * kTileRows;
-            const uint32_t st = ring + (uint32_t)(it % 4) * kKvStage;
-            load_two_tiles<kKvWaves>(st, st + kTileBytes, (const __bf16 *)b.q + h * HD,
-                                     (const __bf16 *)b.dout + h * HD, q_stride, q0, b.Sq, wave,
-                                     lane);
-            if (wave == 0) {
-                // lse and dvec of the tile's rows (rows past Sq read as zeros)
-                const int64_t rows = min(b.Sq - q0, (int64_t)kTileRows);
-                const int bytes = (int)rows * 4;
-                dma4(st + 2 * kTileBytes, lane * 4, rsrc(b.lse + h * b.stat_ld + q0, bytes));
-                dma4(st + 2 * kTileBytes + kStatBytes, lane * 4,
-                     rsrc(b.dvec + h * b.stat_ld + q0, bytes));
-            }
-        }
-    };
-
     const FragOffsets fo = frag_offsets(lane);
-    f32x16 dka[4], dva[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        dka[i] = f32x16{};
-        dva[i] = f32x16{};
-    }
 
-    // S = Q K^T and dP = dO V^T of query tile it (its stage in the ring)
-    // K^T and V^T fragments stay in AGPRs and the MFMAs read them there
-    // directly (about 1.6% faster than letting the compiler copy them to
-    // VGPRs each tile).  The compiler does not see inline-assembly MFMAs as
-    // MFMAs, so the hazards it would cover are covered by the code's shape:
-    // the first result is early-clobber (it must not alias Q or dO), each
-    // chain accumulates into exactly its own destination, and S and dP are
-    // first read by the VALU in the next pipeline step, after the 16 dV/dK
-    // MFMAs behind the scheduling barrier have passed through the same
-    // in-order matrix pipe.
-    auto scores = [&](int it, f32x16 &s, f32x16 &dp) {
-        const char LDS_AS *qt = (const char LDS_AS *)g_kv + (it % 4) * kKvStage;
-        const char LDS_AS *dt = qt + kTileBytes;
-        bf16x8 qa[8];
-#pragma unroll
-        for (int sd = 0; sd < 8; ++sd)
-            qa[sd] = lds_b128(qt, fo.rowf[sd]);
-        __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                         : "=&v"(s) : "v"(qa[0]), "a"(kf[0]));
-#pragma unroll
-        for (int sd = 1; sd < 8; ++sd)
-            __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                             : "+v"(s) : "v"(qa[sd]), "a"(kf[sd]));
-        bf16x8 da[8];
-#pragma unroll
-        for (int sd = 0; sd < 8; ++sd)
-            da[sd] = lds_b128(dt, fo.rowf[sd]);
-        __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-                         : "=&v"(dp) : "v"(da[0]), "a"(vf[0]));
-#pragma unroll
-        for (int sd = 1; sd < 8; ++sd)
-            __asm__ volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                             : "+v"(dp) : "v"(da[sd]), "a"(vf[sd]));
-    };
-    // waits until tile `it` is complete in every wavefront, `ahead` later
-    // tiles may still be in flight
-    auto wait_tile = [&](int ahead) {
-        if (ahead >= 2) {
-            if (wave == 0)
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads0));
-            else
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads));
-        } else if (ahead == 1) {
-            if (wave == 0)
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads0));
-            else
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads));
-        } else {
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        }
-        lds_barrier();
-    };
+    // Phase 0 walks its query tiles from the last one down, phase 1 from its
+    // first visible one up: with paired units every workgroup is then at
+    // query tile (last - s) or (s - const) after s tiles, so the workgroups
+    // of an XCD stream the same tiles at the same time.  The heads of the
+    // KV head's group are the inner loop.
+    for (int ph = 0; ph < n_phase; ++ph) {
+        const int64_t key_row0 = (int64_t)tiles[ph] * kKvRows;
+        const int lane_key = pair * 32 + l32;               // key row within the tile
+        const int keys_here = (int)min(b.Sk - key_row0, (int64_t)kKvRows);
+        const bool key_ok = lane_key < keys_here;
+        const bool down = ph == 0;
 
-    // Software pipeline over query tiles: step it runs S and dP of tile it+1
-    // on the matrix cores while the VALU turns tile it's S and dP into P and
-    // dS, then dV += P^T dO and dK += dS^T Q for tile it.  Four ring stages:
-    // tiles it and it+1 are read, it+2 is in flight, it+3 is issued into the
-    // stage of it-1.
-    f32x16 s_cur, dp_cur;
-    issue(0);
-    issue(1);
-    issue(2);
-    if (n_iter > 0) {
-        wait_tile(min(n_iter - 1, 2));
-        scores(0, s_cur, dp_cur);
-    }
-    // one pipeline step: consumes tile it's S and dP (s_c, dp_c), produces
-    // tile it+1's (s_n, dp_n; recomputed from tile it on the last step, and
-    // unused) -- unconditional, so the scheduler sees the MFMAs and the VALU
-    // work in one block
-    auto step = [&](int it, f32x16 &s_c, f32x16 &dp_c, f32x16 &s_n, f32x16 &dp_n) {
-        if (it + 1 < n_iter) {
-            // outstanding: tiles it+1 and (if any) it+2
-            wait_tile(min(n_iter - 2 - it, 1));
-            issue(it + 3);
-        }
-        const char LDS_AS *qt = (const char LDS_AS *)g_kv + (it % 4) * kKvStage;
-        const char LDS_AS *dt = qt + kTileBytes;
-        const float LDS_AS *lt = (const float LDS_AS *)(qt + 2 * kTileBytes);
-        const float LDS_AS *vt = lt + kStatBytes / 4;
-        f32x4 l4s[4], d4s[4];
+        // the key-side operand of this wavefront's role: K^T (role 0) or V^T
+        // (role 1), key row lane_key of the tile, dims 16*sd + 8*hi + [0, 8)
+        bf16x8 kv[8];
+        {
+            const __bf16 *src = (const __bf16 *)(role == 0 ? b.k : b.v) +
+                                (key_row0 * kv_stride + g * HD + 8 * hi);
+            const u32x4 *p4 = (const u32x4 *)(src + (key_ok ? lane_key : 0) * kv_stride);
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            l4s[i4] = *(const f32x4 LDS_AS *)(lt + 8 * i4 + 4 * hi);
-            d4s[i4] = *(const f32x4 LDS_AS *)(vt + 8 * i4 + 4 * hi);
-        }
-        scores(it + 1 < n_iter ? it + 1 : it, s_n, dp_n);
-        const int64_t q0 = (int64_t)(qt_begin + it % n_qt) * kTileRows;
-        const int64_t qpos0 = b.q_offset + q0;
-        const bool need_mask = b.causal && first_key_pos + kKvRows - 1 > qpos0;
-        int lim = -1;
-        if (need_mask)
-            lim = (int)min(max(b.k_offset + my_key - qpos0, (int64_t)-1), (int64_t)64);
-        bf16x8 pf[2], sf[2];
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            const f32x4 l4 = l4s[i4];
-            const f32x4 d4 = d4s[i4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * i4 + e;
-                float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s_c[i], c, -l4[e] * kLog2e));
-                const int qi = 8 * i4 + 4 * hi + e;
-                p = qi >= lim ? p : 0.f;
-                pf[i >> 3][i & 7] = (__bf16)p;
-                sf[i >> 3][i & 7] = (__bf16)(p * (dp_c[i] - d4[e]));
+            for (int sd = 0; sd < 8; ++sd) {
+                u32x4 x = p4[2 * sd];
+                if (!key_ok)
+                    x = u32x4{0, 0, 0, 0};
+                kv[sd] = __builtin_bit_cast(bf16x8, x);
             }
         }
-        // interleave: the 16 MFMAs of the next tile's S and dP, each followed
-        // by a share of this tile's VALU work
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        {
-            bf16x8 dc[2][4];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    dc[kh][db] = col_frag(dt, fo, kh, db);
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[kh], dc[kh][db], dva[db],
-                                                                     0, 0, 0);
-        }
-        {
-            bf16x8 qc[2][4];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    qc[kh][db] = col_frag(qt, fo, kh, db);
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf[kh], qc[kh][db], dka[db],
-                                                                     0, 0, 0);
-        }
-    };
-    f32x16 s_alt, dp_alt;
-    for (int it = 0; it < n_iter; it += 2) {
-        step(it, s_cur, dp_cur, s_alt, dp_alt);
-        if (it + 1 >= n_iter)
-            break;
-        step(it + 1, s_alt, dp_alt, s_cur, dp_cur);
-    }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no tile load outlives the loop
 
-    // epilogue: lane holds dK[key = 8*(i/4) + 4*hi + i%4][d = 32*db + l32]
-    // (and dV likewise) for the wavefront's 32 keys
+        // query tiles that see any of the workgroup's keys
+        const int64_t first_key_pos = b.k_offset + key_row0;
+        int64_t q_begin = 0;
+        if (b.causal)
+            q_begin = min(max(first_key_pos - b.q_offset, (int64_t)0), b.Sq);
+        const int qt_begin = (int)(q_begin / kTileRows);
+        const int n_qt = n_qt_all - qt_begin;
+        const int n_iter = n_qt > 0 ? n_qt * group : 0;     // (query tile, head) pairs
+        // first row of the query tile of iteration it, and its head
+        auto q_row0 = [&](int it) {
+            const int k = it / group;
+            return (int64_t)(down ? n_qt_all - 1 - k : qt_begin + k) * kTileRows;
+        };
+        auto head_of = [&](int it) { return g * group + it % group; };
+
+        auto issue = [&](int it) {
+            if (it < n_iter) {
+                const int h = head_of(it);
+                const int64_t q0 = q_row0(it);
+                const uint32_t st = ring + (uint32_t)(it % kKvStages) * kKvStage;
+                load_two_tiles<kKvWaves>(st, st + kTileBytes, (const __bf16 *)b.q + h * HD,
+                                         (const __bf16 *)b.dout + h * HD, q_stride, q0, b.Sq,
+                                         wave, lane);
+                if (wave == 0) {
+                    // lse and dvec of the tile's rows (rows past Sq read as zeros)
+                    const int64_t rows = min(b.Sq - q0, (int64_t)kTileRows);
+                    const int bytes = (int)rows * 4;
+                    dma4(st + 2 * kTileBytes, lane * 4, rsrc(b.lse + h * b.stat_ld + q0, bytes));
+                    dma4(st + 2 * kTileBytes + kStatBytes, lane * 4,
+                         rsrc(b.dvec + h * b.stat_ld + q0, bytes));
+                }
+            }
+        };
+
+        f32x16 acc[4];          // dV (role 0) or dK (role 1)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int64_t key = key_row0 + wave * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        if (key >= b.Sk)
-            continue;
-        float *pk = b.dk + (key * b.Hkv + g) * HD + l32;
-        float *pv = b.dv + (key * b.Hkv + g) * HD + l32;
+        for (int i = 0; i < 4; ++i)
+            acc[i] = f32x16{};
+
+        // step it: every wavefront's loads of tile it have landed (later
+        // tiles may still be in flight), every wavefront has finished step
+        // it - 1, then tile it + kKvAhead is requested into the stage of
+        // tile it + kKvAhead - kKvStages = it - 2, whose last reader (role 1)
+        // was in step it - 1.
+        if (ph > 0)
+            lds_barrier();      // the previous phase's stages are no longer read
+        for (int t = 0; t < kKvAhead; ++t)
+            issue(t);
+        // the step loop, compiled once per role (separate register lifetimes)
+        auto steps = [&](auto role_c) {
+        constexpr int kRole = decltype(role_c)::value;
+        for (int it = 0; n_iter > 0 && it <= n_iter; ++it) {
+            const int ahead = max(0, min(kKvAhead - 1, n_iter - 1 - it));
+            if (ahead == 2) {
+                if (wave == 0)
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads0));
+                else
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads));
+            } else if (ahead == 1) {
+                if (wave == 0)
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads0));
+                else
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads));
+            } else {
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            }
+            lds_barrier();
+            issue(it + kKvAhead);
+            float LDS_AS *pbuf = (float LDS_AS *)(g_p + ((it & 1) * kKvPairs + pair) * kPBytes);
+            if constexpr (kRole == 0) {
+                if (it == n_iter)
+                    continue;
+                const char LDS_AS *qt = (const char LDS_AS *)g_kv + (it % kKvStages) * kKvStage;
+                const char LDS_AS *dt = qt + kTileBytes;
+                const float LDS_AS *lt = (const float LDS_AS *)(qt + 2 * kTileBytes);
+                // S = Q K^T: lane holds key l32 and query rows 8*(i/4) + 4*hi + i%4
+                f32x16 sc = f32x16{};
+                {
+                    bf16x8 qa[8];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const float k_val = dka[db][i] * scale + (b.accumulate ? pk[db * 32] : 0.f);
-            const float v_val = dva[db][i] + (b.accumulate ? pv[db * 32] : 0.f);
-            pk[db * 32] = k_val;
-            pv[db * 32] = v_val;
+                    for (int sd = 0; sd < 8; ++sd)
+                        qa[sd] = lds_b128(qt, fo.rowf[sd]);
+#pragma unroll
+                    for (int sd = 0; sd < 8; ++sd)
+                        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[sd], kv[sd], sc, 0, 0, 0);
+                }
+                const int64_t qpos0 = b.q_offset + q_row0(it);
+                const bool need_mask = b.causal && first_key_pos + kKvRows - 1 > qpos0;
+                int lim = -1;
+                if (need_mask) {
+                    // lane's key position minus the tile's first query position
+                    const int base = (int)min(max(first_key_pos - qpos0, (int64_t)-1024),
+                                              (int64_t)1024);
+                    lim = min(max(base + lane_key, -1), 64);
+                }
+                // P, then to the pair's role-1 wavefront (lane to lane)
+                bf16x8 pf[2];
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x4 l4 = *(const f32x4 LDS_AS *)(lt + 8 * i4 + 4 * hi);
+                    f32x4 p4;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * i4 + e;
+                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c, -l4[e] * kLog2e));
+                        const int qi = 8 * i4 + 4 * hi + e;
+                        p = qi >= lim ? p : 0.f;
+                        p4[e] = p;
+                        pf[i >> 3][i & 7] = (__bf16)p;
+                    }
+                    *(f32x4 LDS_AS *)(pbuf + i4 * 256 + lane * 4) = p4;
+                }
+                // dV += P^T dO
+                bf16x8 dc[2][4];
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int db = 0; db < 4; ++db)
+                        dc[kh][db] = col_frag(dt, fo, kh, db);
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int db = 0; db < 4; ++db)
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[kh], dc[kh][db],
+                                                                         acc[db], 0, 0, 0);
+            } else {
+                if (it == 0)
+                    continue;
+                const int t = it - 1;
+                const float LDS_AS *pprev =
+                    (const float LDS_AS *)(g_p + (((t & 1) * kKvPairs) + pair) * kPBytes);
+                const char LDS_AS *qt = (const char LDS_AS *)g_kv + (t % kKvStages) * kKvStage;
+                const char LDS_AS *dt = qt + kTileBytes;
+                const float LDS_AS *vt = (const float LDS_AS *)(qt + 2 * kTileBytes) +
+                                         kStatBytes / 4;
+                // dP = dO V^T, same layout as S
+                f32x16 dp = f32x16{};
+                {
+                    bf16x8 da[8];
+#pragma unroll
+                    for (int sd = 0; sd < 8; ++sd)
+                        da[sd] = lds_b128(dt, fo.rowf[sd]);
+#pragma unroll
+                    for (int sd = 0; sd < 8; ++sd)
+                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[sd], kv[sd], dp, 0, 0, 0);
+                }
+                bf16x8 sf[2];
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    const f32x4 p4 = *(const f32x4 LDS_AS *)(pprev + i4 * 256 + lane * 4);
+                    const f32x4 d4 = *(const f32x4 LDS_AS *)(vt + 8 * i4 + 4 * hi);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 4 * i4 + e;
+                        sf[i >> 3][i & 7] = (__bf16)(p4[e] * (dp[i] - d4[e]));
+                    }
+                }
+                // dK += dS^T Q
+                bf16x8 qc[2][4];
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int db = 0; db < 4; ++db)
+                        qc[kh][db] = col_frag(qt, fo, kh, db);
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int db = 0; db < 4; ++db)
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf[kh], qc[kh][db],
+                                                                         acc[db], 0, 0, 0);
+            }
+        }
+        };
+        if (role == 0)
+            steps(std::integral_constant<int, 0>{});
+        else
+            steps(std::integral_constant<int, 1>{});
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no tile load outlives the phase
+
+        // epilogue: lane holds dV (role 0) or dK (role 1) at
+        // [key = 8*(i/4) + 4*hi + i%4][d = 32*db + l32] of the pair's 32 keys
+        float *dst = (role == 0 ? b.dv : b.dk) + (key_row0 * b.Hkv + g) * HD + l32;
+        const float mul = role == 0 ? 1.f : scale;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int kk = pair * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+            if (kk >= keys_here)
+                continue;
+            float *pk = dst + kk * b.Hkv * HD;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                pk[db * 32] = acc[db][i] * mul + (b.accumulate ? pk[db * 32] : 0.f);
         }
     }
 }
@@ -637,17 +706,32 @@ void bwd_dkdv_kernel(BwdLaunch b)
 hipError_t launch_bwd_bf16(const BwdLaunch &b, hipStream_t stream)
 {
     if (b.Sq > 0) {
-        const int n_row_tiles = (int)((b.Sq + kDqRows - 1) / kDqRows);
-        hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((int64_t)n_row_tiles * b.Hq)),
-                           dim3(kDqThreads), 0, stream, b, n_row_tiles);
+        DqWork w{};
+        w.n_row_tiles = (int)((b.Sq + kDqRows - 1) / kDqRows);
+        w.mode = (b.causal && (b.Hkv % 8 != 0 || b.Hq % 8 != 0)) ? 1 : 0;
+        int64_t grid;
+        if (w.mode == 0) {
+            w.per_xcd = (int)(((int64_t)w.n_row_tiles * b.Hq + 7) / 8);
+            grid = 8 * (int64_t)w.per_xcd;
+        } else {
+            w.band = (w.n_row_tiles + 15) / 16;
+            grid = 8 * (int64_t)b.Hq * 2 * w.band;
+        }
+        hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)grid), dim3(kDqThreads), 0, stream, b,
+                           w);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
     if (b.Sk > 0) {
-        const int64_t n_key_tiles = (b.Sk + kKvRows - 1) / kKvRows;
-        hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(n_key_tiles * b.Hkv)),
-                           dim3(kKvThreads), 0, stream, b);
+        KvWork w{};
+        w.n_key_tiles = (int)((b.Sk + kKvRows - 1) / kKvRows);
+        w.paired = b.causal && w.n_key_tiles > 1 ? 1 : 0;
+        w.units = w.paired ? (w.n_key_tiles + 1) / 2 : w.n_key_tiles;
+        const int64_t total = (int64_t)w.units * b.Hkv;
+        w.per_xcd = (int)((total + 7) / 8);
+        hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(8 * (int64_t)w.per_xcd)),
+                           dim3(kKvThreads), 0, stream, b, w);
     }
     return hipGetLastError();
 }
