@@ -17,22 +17,25 @@
 // Two kernels, each owning its outputs (no atomics):
 //   * bwd_dq_kernel: a workgroup of 8 wavefronts owns 256 query rows of one
 //     head (32 per wavefront) and streams the KV block through LDS 32 keys
-//     at a time (3-stage ring of direct buffer->LDS loads).  Per 32-key
+//     at a time (3-stage ring of direct buffer->LDS loads); the launch's
+//     row tiles are spread over the XCDs so that the workgroups an XCD holds
+//     at a time stream the same K/V tiles.  Per 32-key
 //     tile: S^T = K Q^T and dP^T = V dO^T (A = K or V fragments read from
 //     LDS, B = Q^T or dO^T kept in VGPRs), ds in registers, then
 //     dQ^T += K^T ds^T with K^T from transpose reads of the same K tile.  The
 //     lane holds one query row, so lse and dvec are per-lane scalars.
-//   * bwd_dkdv_kernel: a workgroup of 4 wavefronts (one per SIMD, so each
-//     has 512 registers and dK, dV stay in accumulation registers) owns 128
-//     keys of one KV head (32 per wavefront) and streams the query rows of
-//     every head of its group through LDS 32 at a time (q, dout, lse and
-//     dvec; 4-stage ring).  Per 32-query tile: S = Q K^T and dP = dO V^T
-//     (A = Q or dO fragments from LDS, B = K^T or V^T in VGPRs), then
-//     dV += P^T dO and dK += ds^T Q with P and ds from registers and dO, Q
-//     from transpose reads.  The loop is software-pipelined: the MFMAs of
-//     the next tile's S and dP are interleaved (scheduling groups) with this
-//     tile's exponentials and ds, which a single wavefront per SIMD could
-//     not otherwise overlap.
+//   * bwd_dkdv_kernel: a workgroup of 8 wavefronts (two per SIMD) owns 128
+//     keys of one KV head, 32 per pair of wavefronts on one SIMD, and
+//     streams the query rows of every head of its group through LDS 32 at a
+//     time (q, dout, lse and dvec; 5-stage ring).  The pair splits the work
+//     by role: one wavefront keeps K^T in registers and computes S = Q K^T,
+//     P and dV += P^T dO; the other keeps V^T and computes dP = dO V^T,
+//     dS = P (dP - dvec) and dK += dS^T Q one tile later, P passing between
+//     them through LDS.  Halving each wavefront's registers this way puts two
+//     of them on a SIMD.  Under the causal mask a workgroup takes key tiles
+//     t and n-1-t (equal work), walking the first one's query tiles down and
+//     the second one's up, and the workgroups an XCD holds at a time belong
+//     to one KV head, so they read the same query tiles from L2 together.
 // Tiles use the forward kernel's layout: 256-byte rows with a 16-byte-chunk
 // XOR swizzle that keeps ds_read_b128 row fragments and ds_read_b64_tr_b16
 // column fragments free of bank conflicts.
@@ -419,21 +422,31 @@ void bwd_dq_kernel(BwdLaunch b, DqWork w)
 // fit on a SIMD and the SIMD interleaves one's matrix work with the other's
 // exponentials and waits.  Every product is the one the single-wavefront
 // form computes, in the same order.
+//
+// LDS: the ring's q tiles, then its dout tiles, then its lse/dvec rows, then
+// P (double-buffered).  Each role keeps per-lane base registers into the
+// regions it reads (row fragments, column fragments, its statistics, its
+// pair's P) and the step adds one uniform stage offset: one address add per
+// fragment read.
 constexpr int kKvWaves = 8;
 constexpr int kKvPairs = 4;
 constexpr int kKvRows = kKvPairs * 32;                 // 128 keys
 constexpr int kKvThreads = kKvWaves * 64;
-constexpr int kStatBytes = 64 * 4;                     // one float per lane of the loading wave
-constexpr int kKvStage = 2 * kTileBytes + 2 * kStatBytes;   // q, dout, lse, dvec
 constexpr int kKvStages = 5;
 constexpr int kKvAhead = 3;        // tile it + 3 is requested at step it (stages - 2)
+constexpr int kStatBytes = 64 * 4;                     // one float per lane of the loading wave
 constexpr int kPBytes = 64 * 16 * 4;                   // a pair's P: 16 floats per lane
+constexpr int kQOff = 0;                               // q tile of stage s: kQOff + s * kTileBytes
+constexpr int kDOff = kKvStages * kTileBytes;          // dout tile of stage s
+constexpr int kSOff = 2 * kKvStages * kTileBytes;      // lse of stage s, then dvec (+kStatBytes)
+constexpr int kPOff = kSOff + (kKvStages * 2 * kStatBytes + 1023) / 1024 * 1024;   // P: pair, buffer
+constexpr int kKvLds = kPOff + 2 * kKvPairs * kPBytes;
+static_assert(kDOff + kKvStages * kTileBytes <= kSOff && kPOff % 1024 == 0, "LDS layout");
 
-// the ring: q tile, dout tile, lse, dvec in each stage; then P, double-buffered
-__shared__ __attribute__((aligned(1024))) char g_kv[kKvStages * kKvStage];
-__shared__ __attribute__((aligned(1024))) char g_p[2 * kKvPairs * kPBytes];
+__shared__ __attribute__((aligned(1024))) char g_kv[kKvLds];
 constexpr int kKvLoads = 2 * (kTileRows / 4) / kKvWaves;   // tile loads per wavefront
 constexpr int kKvLoads0 = kKvLoads + 2;                     // wavefront 0 also loads lse, dvec
+static_assert(kKvLoads == 2, "one q and one dout block per wavefront and tile");
 
 // Work of the dk/dv launch: `units` per KV head, each one key tile or (under
 // the causal mask) the pair of key tiles t and n_key_tiles - 1 - t, whose
@@ -448,6 +461,9 @@ struct KvWork {
     int paired;       // 1: a unit is a pair of key tiles
     int n_key_tiles;
 };
+
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
@@ -475,13 +491,12 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
     const float c = kLog2e * scale;
     const int n_qt_all = (int)((b.Sq + kTileRows - 1) / kTileRows);
     const uint32_t ring = (uint32_t)(uintptr_t)(char LDS_AS *)g_kv;
-    const FragOffsets fo = frag_offsets(lane);
+    const int row_bytes = (int)(q_stride * 2);
+    // this wavefront's 16-byte chunk of the tile loads: block `wave` (rows
+    // 4*wave .. 4*wave+3) of every q and dout tile
+    const int dma_row = wave * 4 + (lane >> 4);
+    const int dma_off = dma_row * row_bytes + (((lane & 15) ^ swz(dma_row)) << 4);
 
-    // Phase 0 walks its query tiles from the last one down, phase 1 from its
-    // first visible one up: with paired units every workgroup is then at
-    // query tile (last - s) or (s - const) after s tiles, so the workgroups
-    // of an XCD stream the same tiles at the same time.  The heads of the
-    // KV head's group are the inner loop.
     for (int ph = 0; ph < n_phase; ++ph) {
         const int64_t key_row0 = (int64_t)tiles[ph] * kKvRows;
         const int lane_key = pair * 32 + l32;               // key row within the tile
@@ -513,36 +528,39 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
         const int qt_begin = (int)(q_begin / kTileRows);
         const int n_qt = n_qt_all - qt_begin;
         const int n_iter = n_qt > 0 ? n_qt * group : 0;     // (query tile, head) pairs
-        // first row of the query tile of iteration it, and its head
+        // Phase 0 walks its query tiles from the last one down, phase 1 from
+        // its first visible one up: with paired units every workgroup is then
+        // at query tile (last - s) or (s - const) after s tiles, so the
+        // workgroups of an XCD stream the same tiles at the same time.  The
+        // heads of the KV head's group are the inner loop.
         auto q_row0 = [&](int it) {
             const int k = it / group;
             return (int64_t)(down ? n_qt_all - 1 - k : qt_begin + k) * kTileRows;
         };
-        auto head_of = [&](int it) { return g * group + it % group; };
 
+        // tile it's q and dout rows and its lse, dvec into stage it % kKvStages
         auto issue = [&](int it) {
             if (it < n_iter) {
-                const int h = head_of(it);
+                const int st = it % kKvStages;
+                const int h = g * group + it % group;
                 const int64_t q0 = q_row0(it);
-                const uint32_t st = ring + (uint32_t)(it % kKvStages) * kKvStage;
-                load_two_tiles<kKvWaves>(st, st + kTileBytes, (const __bf16 *)b.q + h * HD,
-                                         (const __bf16 *)b.dout + h * HD, q_stride, q0, b.Sq,
-                                         wave, lane);
+                const int64_t rows = min(b.Sq - q0, (int64_t)kTileRows);   // >= 1
+                const int bytes = (int)(rows - 1) * row_bytes + HD * 2;
+                const int64_t e0 = q0 * q_stride + h * HD;
+                dma16(ring + kQOff + st * kTileBytes + wave * 1024, dma_off,
+                      rsrc((const __bf16 *)b.q + e0, bytes));
+                dma16(ring + kDOff + st * kTileBytes + wave * 1024, dma_off,
+                      rsrc((const __bf16 *)b.dout + e0, bytes));
                 if (wave == 0) {
                     // lse and dvec of the tile's rows (rows past Sq read as zeros)
-                    const int64_t rows = min(b.Sq - q0, (int64_t)kTileRows);
-                    const int bytes = (int)rows * 4;
-                    dma4(st + 2 * kTileBytes, lane * 4, rsrc(b.lse + h * b.stat_ld + q0, bytes));
-                    dma4(st + 2 * kTileBytes + kStatBytes, lane * 4,
-                         rsrc(b.dvec + h * b.stat_ld + q0, bytes));
+                    const int sb = (int)rows * 4;
+                    dma4(ring + kSOff + st * 2 * kStatBytes, lane * 4,
+                         rsrc(b.lse + h * b.stat_ld + q0, sb));
+                    dma4(ring + kSOff + st * 2 * kStatBytes + kStatBytes, lane * 4,
+                         rsrc(b.dvec + h * b.stat_ld + q0, sb));
                 }
             }
         };
-
-        f32x16 acc[4];          // dV (role 0) or dK (role 1)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc[i] = f32x16{};
 
         // step it: every wavefront's loads of tile it have landed (later
         // tiles may still be in flight), every wavefront has finished step
@@ -553,151 +571,185 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
             lds_barrier();      // the previous phase's stages are no longer read
         for (int t = 0; t < kKvAhead; ++t)
             issue(t);
+
         // the step loop, compiled once per role (separate register lifetimes)
         auto steps = [&](auto role_c) {
-        constexpr int kRole = decltype(role_c)::value;
-        for (int it = 0; n_iter > 0 && it <= n_iter; ++it) {
-            const int ahead = max(0, min(kKvAhead - 1, n_iter - 1 - it));
-            if (ahead == 2) {
-                if (wave == 0)
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads0));
-                else
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads));
-            } else if (ahead == 1) {
-                if (wave == 0)
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads0));
-                else
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads));
-            } else {
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-            }
-            lds_barrier();
-            issue(it + kKvAhead);
-            float LDS_AS *pbuf = (float LDS_AS *)(g_p + ((it & 1) * kKvPairs + pair) * kPBytes);
-            if constexpr (kRole == 0) {
-                if (it == n_iter)
-                    continue;
-                const char LDS_AS *qt = (const char LDS_AS *)g_kv + (it % kKvStages) * kKvStage;
-                const char LDS_AS *dt = qt + kTileBytes;
-                const float LDS_AS *lt = (const float LDS_AS *)(qt + 2 * kTileBytes);
-                // S = Q K^T: lane holds key l32 and query rows 8*(i/4) + 4*hi + i%4
-                f32x16 sc = f32x16{};
-                {
-                    bf16x8 qa[8];
+            constexpr int kRole = decltype(role_c)::value;
+            // per-lane LDS bases: row fragments from the role's first operand
+            // tile (q for role 0, dout for role 1), column fragments from the
+            // other, stage offsets as immediates
+            constexpr int kRowOff = kRole == 0 ? kQOff : kDOff;
+            constexpr int kColOff = kRole == 0 ? kDOff : kQOff;
+            const FragOffsets fo = frag_offsets(lane);
+            int rowb[8], colb[2][4];
 #pragma unroll
-                    for (int sd = 0; sd < 8; ++sd)
-                        qa[sd] = lds_b128(qt, fo.rowf[sd]);
+            for (int sd = 0; sd < 8; ++sd)
+                rowb[sd] = fo.rowf[sd] + kRowOff;
 #pragma unroll
-                    for (int sd = 0; sd < 8; ++sd)
-                        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[sd], kv[sd], sc, 0, 0, 0);
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    colb[x][db] = fo.col[x][db] + kColOff;
+            const int statb = kSOff + (kRole == 0 ? 0 : kStatBytes) + hi * 16;
+            const int pl = kPOff + pair * kPBytes + lane * 16;
+            const char LDS_AS *lds = (const char LDS_AS *)g_kv;
+            auto colf = [&](int so, int kh, int db) {
+                const char LDS_AS *t = lds + so + kh * 16 * 256;
+                const i16x4 lo = lds_tr(t, colb[0][db]);
+                const i16x4 up = lds_tr(t, colb[1][db]);
+                return __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                               __builtin_bit_cast(bf16x4, up), 0, 1, 2, 3, 4,
+                                               5, 6, 7);
+            };
+            f32x16 acc[4];          // dV (role 0) or dK (role 1)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i] = f32x16{};
+
+            // byte offsets (uniform) of the stages of tiles it, it - 1 and
+            // it + kKvAhead, advanced around the ring each step
+            int so_cur = 0, so_prev = (kKvStages - 1) * kTileBytes;
+            for (int it = 0; n_iter > 0 && it <= n_iter; ++it) {
+                const int ahead = max(0, min(kKvAhead - 1, n_iter - 1 - it));
+                if (ahead == 2) {
+                    if (wave == 0)
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads0));
+                    else
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads));
+                } else if (ahead == 1) {
+                    if (wave == 0)
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads0));
+                    else
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads));
+                } else {
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
                 }
-                const int64_t qpos0 = b.q_offset + q_row0(it);
-                const bool need_mask = b.causal && first_key_pos + kKvRows - 1 > qpos0;
-                int lim = -1;
-                if (need_mask) {
-                    // lane's key position minus the tile's first query position
-                    const int base = (int)min(max(first_key_pos - qpos0, (int64_t)-1024),
-                                              (int64_t)1024);
-                    lim = min(max(base + lane_key, -1), 64);
-                }
-                // P, then to the pair's role-1 wavefront (lane to lane)
-                bf16x8 pf[2];
+                lds_barrier();
+                issue(it + kKvAhead);
+                const int st_cur = so_cur / kTileBytes, st_prev = so_prev / kTileBytes;
+                if constexpr (kRole == 0) {
+                    if (it < n_iter) {
+                        // S = Q K^T: lane holds key l32 and query rows 8*(i/4) + 4*hi + i%4
+                        f32x16 sc = f32x16{};
+                        {
+                            bf16x8 qa[8];
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const f32x4 l4 = *(const f32x4 LDS_AS *)(lt + 8 * i4 + 4 * hi);
-                    f32x4 p4;
+                            for (int sd = 0; sd < 8; ++sd)
+                                qa[sd] = lds_b128(lds + so_cur, rowb[sd]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 4 * i4 + e;
-                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c, -l4[e] * kLog2e));
-                        const int qi = 8 * i4 + 4 * hi + e;
-                        p = qi >= lim ? p : 0.f;
-                        p4[e] = p;
-                        pf[i >> 3][i & 7] = (__bf16)p;
+                            for (int sd = 0; sd < 8; ++sd)
+                                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[sd], kv[sd], sc,
+                                                                             0, 0, 0);
+                        }
+                        const int64_t qpos0 = b.q_offset + q_row0(it);
+                        const bool need_mask = b.causal && first_key_pos + kKvRows - 1 > qpos0;
+                        int lim = -1;
+                        if (need_mask) {
+                            // lane's key position minus the tile's first query position
+                            const int base = (int)min(max(first_key_pos - qpos0, (int64_t)-1024),
+                                                      (int64_t)1024);
+                            lim = min(max(base + lane_key, -1), 64);
+                        }
+                        // P, then to the pair's role-1 wavefront (lane to lane)
+                        const char LDS_AS *pw = lds + (it & 1) * (kKvPairs * kPBytes);
+                        const char LDS_AS *lt = lds + st_cur * 2 * kStatBytes;
+                        bf16x8 pf[2];
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4) {
+                            const f32x4 l4 = *(const f32x4 LDS_AS *)(lt + i4 * 32 + statb);
+                            f32x4 p4;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int i = 4 * i4 + e;
+                                float p = __builtin_amdgcn_exp2f(
+                                    __builtin_fmaf(sc[i], c, -l4[e] * kLog2e));
+                                const int qi = 8 * i4 + 4 * hi + e;
+                                p = qi >= lim ? p : 0.f;
+                                p4[e] = p;
+                                pf[i >> 3][i & 7] = (__bf16)p;
+                            }
+                            *(f32x4 LDS_AS *)(pw + i4 * 1024 + pl) = p4;
+                        }
+                        // dV += P^T dO
+                        bf16x8 dc[2][4];
+#pragma unroll
+                        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                            for (int db = 0; db < 4; ++db)
+                                dc[kh][db] = colf(so_cur, kh, db);
+#pragma unroll
+                        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                            for (int db = 0; db < 4; ++db)
+                                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    pf[kh], dc[kh][db], acc[db], 0, 0, 0);
                     }
-                    *(f32x4 LDS_AS *)(pbuf + i4 * 256 + lane * 4) = p4;
-                }
-                // dV += P^T dO
-                bf16x8 dc[2][4];
+                } else {
+                    if (it > 0) {
+                        // dP = dO V^T (tile it - 1), same layout as S
+                        f32x16 dp = f32x16{};
+                        {
+                            bf16x8 da[8];
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
+                            for (int sd = 0; sd < 8; ++sd)
+                                da[sd] = lds_b128(lds + so_prev, rowb[sd]);
 #pragma unroll
-                    for (int db = 0; db < 4; ++db)
-                        dc[kh][db] = col_frag(dt, fo, kh, db);
+                            for (int sd = 0; sd < 8; ++sd)
+                                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[sd], kv[sd], dp,
+                                                                             0, 0, 0);
+                        }
+                        const char LDS_AS *pr = lds + ((it - 1) & 1) * (kKvPairs * kPBytes);
+                        const char LDS_AS *vt = lds + st_prev * 2 * kStatBytes;
+                        bf16x8 sf[2];
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
+                        for (int i4 = 0; i4 < 4; ++i4) {
+                            const f32x4 p4 = *(const f32x4 LDS_AS *)(pr + i4 * 1024 + pl);
+                            const f32x4 d4 = *(const f32x4 LDS_AS *)(vt + i4 * 32 + statb);
 #pragma unroll
-                    for (int db = 0; db < 4; ++db)
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[kh], dc[kh][db],
-                                                                         acc[db], 0, 0, 0);
-            } else {
-                if (it == 0)
-                    continue;
-                const int t = it - 1;
-                const float LDS_AS *pprev =
-                    (const float LDS_AS *)(g_p + (((t & 1) * kKvPairs) + pair) * kPBytes);
-                const char LDS_AS *qt = (const char LDS_AS *)g_kv + (t % kKvStages) * kKvStage;
-                const char LDS_AS *dt = qt + kTileBytes;
-                const float LDS_AS *vt = (const float LDS_AS *)(qt + 2 * kTileBytes) +
-                                         kStatBytes / 4;
-                // dP = dO V^T, same layout as S
-                f32x16 dp = f32x16{};
-                {
-                    bf16x8 da[8];
+                            for (int e = 0; e < 4; ++e) {
+                                const int i = 4 * i4 + e;
+                                sf[i >> 3][i & 7] = (__bf16)(p4[e] * (dp[i] - d4[e]));
+                            }
+                        }
+                        // dK += dS^T Q
+                        bf16x8 qc[2][4];
 #pragma unroll
-                    for (int sd = 0; sd < 8; ++sd)
-                        da[sd] = lds_b128(dt, fo.rowf[sd]);
+                        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                    for (int sd = 0; sd < 8; ++sd)
-                        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[sd], kv[sd], dp, 0, 0, 0);
-                }
-                bf16x8 sf[2];
+                            for (int db = 0; db < 4; ++db)
+                                qc[kh][db] = colf(so_prev, kh, db);
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    const f32x4 p4 = *(const f32x4 LDS_AS *)(pprev + i4 * 256 + lane * 4);
-                    const f32x4 d4 = *(const f32x4 LDS_AS *)(vt + 8 * i4 + 4 * hi);
+                        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int i = 4 * i4 + e;
-                        sf[i >> 3][i & 7] = (__bf16)(p4[e] * (dp[i] - d4[e]));
+                            for (int db = 0; db < 4; ++db)
+                                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    sf[kh], qc[kh][db], acc[db], 0, 0, 0);
                     }
                 }
-                // dK += dS^T Q
-                bf16x8 qc[2][4];
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int db = 0; db < 4; ++db)
-                        qc[kh][db] = col_frag(qt, fo, kh, db);
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int db = 0; db < 4; ++db)
-                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf[kh], qc[kh][db],
-                                                                         acc[db], 0, 0, 0);
+                so_prev = so_cur;
+                so_cur = so_cur == (kKvStages - 1) * kTileBytes ? 0 : so_cur + kTileBytes;
             }
-        }
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no tile load outlives the phase
+
+            // epilogue: lane holds dV (role 0) or dK (role 1) at
+            // [key = 8*(i/4) + 4*hi + i%4][d = 32*db + l32] of the pair's 32 keys
+            float *dst = (kRole == 0 ? b.dv : b.dk) + (key_row0 * b.Hkv + g) * HD + l32;
+            const float mul = kRole == 0 ? 1.f : scale;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kk = pair * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+                if (kk >= keys_here)
+                    continue;
+                float *pk = dst + kk * b.Hkv * HD;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    pk[db * 32] = acc[db][i] * mul + (b.accumulate ? pk[db * 32] : 0.f);
+            }
         };
         if (role == 0)
-            steps(std::integral_constant<int, 0>{});
+            steps(IC<0>{});
         else
-            steps(std::integral_constant<int, 1>{});
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // no tile load outlives the phase
-
-        // epilogue: lane holds dV (role 0) or dK (role 1) at
-        // [key = 8*(i/4) + 4*hi + i%4][d = 32*db + l32] of the pair's 32 keys
-        float *dst = (role == 0 ? b.dv : b.dk) + (key_row0 * b.Hkv + g) * HD + l32;
-        const float mul = role == 0 ? 1.f : scale;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int kk = pair * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if (kk >= keys_here)
-                continue;
-            float *pk = dst + kk * b.Hkv * HD;
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-                pk[db * 32] = acc[db][i] * mul + (b.accumulate ? pk[db * 32] : 0.f);
-        }
+            steps(IC<1>{});
     }
 }
 
