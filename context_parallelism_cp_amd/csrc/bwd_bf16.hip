@@ -393,19 +393,28 @@ void bwd_dq_kernel(BwdLaunch b, DqWork w)
     if (!row_ok)
         return;
     float *dst = b.dq + (my_row * b.Hq + h) * HD;
+    // every load before the first store (the loads in flight together, the
+    // stores without waits between them)
+    f32x4 v4[4][4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            f32x4 *p = (f32x4 *)(dst + db * 32 + 8 * i4 + 4 * hi);
-            f32x4 v4;
+        for (int i4 = 0; i4 < 4; ++i4)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                v4[e] = acc[db][4 * i4 + e] * scale;
-            if (b.accumulate)
-                v4 += *p;
-            *p = v4;
-        }
+                v4[db][i4][e] = acc[db][4 * i4 + e] * scale;
+    if (b.accumulate) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                v4[db][i4] += *(const f32x4 *)(dst + db * 32 + 8 * i4 + 4 * hi);
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+            *(f32x4 *)(dst + db * 32 + 8 * i4 + 4 * hi) = v4[db][i4];
 }
 
 // ============================================================ dk/dv kernel
@@ -427,7 +436,13 @@ void bwd_dq_kernel(BwdLaunch b, DqWork w)
 // P (double-buffered).  Each role keeps per-lane base registers into the
 // regions it reads (row fragments, column fragments, its statistics, its
 // pair's P) and the step adds one uniform stage offset: one address add per
-// fragment read.
+// fragment read.  Every batch of LDS reads (row fragments, statistics, P,
+// column fragments) is issued whole before the arithmetic that takes it (a
+// scheduling barrier after the batch): left to itself the scheduler
+// interleaved read, wait and product one fragment at a time, eight LDS round
+// trips in a row.  The epilogue's addresses are computed from an opaque copy
+// of the lane index so that they are not hoisted out of the step loop and
+// kept live across it (34 registers).
 constexpr int kKvWaves = 8;
 constexpr int kKvPairs = 4;
 constexpr int kKvRows = kKvPairs * 32;                 // 128 keys
@@ -636,6 +651,7 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
 #pragma unroll
                             for (int sd = 0; sd < 8; ++sd)
                                 qa[sd] = lds_b128(lds + so_cur, rowb[sd]);
+                            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                             for (int sd = 0; sd < 8; ++sd)
                                 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[sd], kv[sd], sc,
@@ -653,10 +669,15 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
                         // P, then to the pair's role-1 wavefront (lane to lane)
                         const char LDS_AS *pw = lds + (it & 1) * (kKvPairs * kPBytes);
                         const char LDS_AS *lt = lds + st_cur * 2 * kStatBytes;
+                        f32x4 l4s[4];
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4)
+                            l4s[i4] = *(const f32x4 LDS_AS *)(lt + i4 * 32 + statb);
+                        __builtin_amdgcn_sched_barrier(0);
                         bf16x8 pf[2];
 #pragma unroll
                         for (int i4 = 0; i4 < 4; ++i4) {
-                            const f32x4 l4 = *(const f32x4 LDS_AS *)(lt + i4 * 32 + statb);
+                            const f32x4 l4 = l4s[i4];
                             f32x4 p4;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
@@ -677,6 +698,7 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
 #pragma unroll
                             for (int db = 0; db < 4; ++db)
                                 dc[kh][db] = colf(so_cur, kh, db);
+                        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -693,6 +715,7 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
 #pragma unroll
                             for (int sd = 0; sd < 8; ++sd)
                                 da[sd] = lds_b128(lds + so_prev, rowb[sd]);
+                            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                             for (int sd = 0; sd < 8; ++sd)
                                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[sd], kv[sd], dp,
@@ -700,11 +723,18 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
                         }
                         const char LDS_AS *pr = lds + ((it - 1) & 1) * (kKvPairs * kPBytes);
                         const char LDS_AS *vt = lds + st_prev * 2 * kStatBytes;
+                        f32x4 p4s[4], d4s[4];
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4) {
+                            p4s[i4] = *(const f32x4 LDS_AS *)(pr + i4 * 1024 + pl);
+                            d4s[i4] = *(const f32x4 LDS_AS *)(vt + i4 * 32 + statb);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                         bf16x8 sf[2];
 #pragma unroll
                         for (int i4 = 0; i4 < 4; ++i4) {
-                            const f32x4 p4 = *(const f32x4 LDS_AS *)(pr + i4 * 1024 + pl);
-                            const f32x4 d4 = *(const f32x4 LDS_AS *)(vt + i4 * 32 + statb);
+                            const f32x4 p4 = p4s[i4];
+                            const f32x4 d4 = d4s[i4];
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const int i = 4 * i4 + e;
@@ -718,6 +748,7 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
 #pragma unroll
                             for (int db = 0; db < 4; ++db)
                                 qc[kh][db] = colf(so_prev, kh, db);
+                        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -733,17 +764,38 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
 
             // epilogue: lane holds dV (role 0) or dK (role 1) at
             // [key = 8*(i/4) + 4*hi + i%4][d = 32*db + l32] of the pair's 32 keys
-            float *dst = (kRole == 0 ? b.dv : b.dk) + (key_row0 * b.Hkv + g) * HD + l32;
+            // (the lane index is made opaque so that the compiler does not
+            // hoist these addresses out of the step loop and keep them live)
+            int eln = lane;
+            __asm__ volatile("" : "+v"(eln));
+            const int el32 = eln & 31, ehi = eln >> 5;
+            float *dst = (kRole == 0 ? b.dv : b.dk) + (key_row0 * b.Hkv + g) * HD + el32;
             const float mul = kRole == 0 ? 1.f : scale;
+            // every load before the first store, so that the loads are in
+            // flight together and the stores follow without waits
+            if (b.accumulate) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kk = pair * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-                if (kk >= keys_here)
-                    continue;
-                float *pk = dst + kk * b.Hkv * HD;
+                for (int i = 0; i < 16; ++i) {
+                    const int kk = pair * 32 + 8 * (i >> 2) + 4 * ehi + (i & 3);
+                    const float *pk = dst + (int64_t)min(kk, keys_here - 1) * b.Hkv * HD;
+#pragma unroll
+                    for (int db = 0; db < 4; ++db)
+                        acc[db][i] = acc[db][i] * mul + pk[db * 32];
+                }
+            } else {
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
-                    pk[db * 32] = acc[db][i] * mul + (b.accumulate ? pk[db * 32] : 0.f);
+                    acc[db] *= mul;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kk = pair * 32 + 8 * (i >> 2) + 4 * ehi + (i & 3);
+                if (kk >= keys_here)
+                    continue;
+                float *pk = dst + (int64_t)kk * b.Hkv * HD;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    pk[db * 32] = acc[db][i];
             }
         };
         if (role == 0)
