@@ -548,32 +548,38 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
         // at query tile (last - s) or (s - const) after s tiles, so the
         // workgroups of an XCD stream the same tiles at the same time.  The
         // heads of the KV head's group are the inner loop.
-        auto q_row0 = [&](int it) {
-            const int k = it / group;
-            return (int64_t)(down ? n_qt_all - 1 - k : qt_begin + k) * kTileRows;
-        };
 
-        // tile it's q and dout rows and its lse, dvec into stage it % kKvStages
-        auto issue = [&](int it) {
-            if (it < n_iter) {
-                const int st = it % kKvStages;
-                const int h = g * group + it % group;
-                const int64_t q0 = q_row0(it);
+        // Step it's q and dout rows and its lse, dvec go into stage
+        // it % kKvStages.  The loads walk the (query tile, head) pairs in step
+        // order; the next pair to request is a cursor advanced by one per
+        // call, so a request costs no division by the group size.
+        int c_it = 0, c_h = 0, c_k = 0, c_st = 0;
+        auto issue_next = [&]() {
+            if (c_it < n_iter) {
+                const int h = g * group + c_h;
+                const int64_t q0 =
+                    (int64_t)(down ? n_qt_all - 1 - c_k : qt_begin + c_k) * kTileRows;
                 const int64_t rows = min(b.Sq - q0, (int64_t)kTileRows);   // >= 1
                 const int bytes = (int)(rows - 1) * row_bytes + HD * 2;
                 const int64_t e0 = q0 * q_stride + h * HD;
-                dma16(ring + kQOff + st * kTileBytes + wave * 1024, dma_off,
+                dma16(ring + kQOff + c_st * kTileBytes + wave * 1024, dma_off,
                       rsrc((const __bf16 *)b.q + e0, bytes));
-                dma16(ring + kDOff + st * kTileBytes + wave * 1024, dma_off,
+                dma16(ring + kDOff + c_st * kTileBytes + wave * 1024, dma_off,
                       rsrc((const __bf16 *)b.dout + e0, bytes));
                 if (wave == 0) {
                     // lse and dvec of the tile's rows (rows past Sq read as zeros)
                     const int sb = (int)rows * 4;
-                    dma4(ring + kSOff + st * 2 * kStatBytes, lane * 4,
+                    dma4(ring + kSOff + c_st * 2 * kStatBytes, lane * 4,
                          rsrc(b.lse + h * b.stat_ld + q0, sb));
-                    dma4(ring + kSOff + st * 2 * kStatBytes + kStatBytes, lane * 4,
+                    dma4(ring + kSOff + c_st * 2 * kStatBytes + kStatBytes, lane * 4,
                          rsrc(b.dvec + h * b.stat_ld + q0, sb));
                 }
+            }
+            ++c_it;
+            c_st = c_st == kKvStages - 1 ? 0 : c_st + 1;
+            if (++c_h == group) {
+                c_h = 0;
+                ++c_k;
             }
         };
 
@@ -585,7 +591,7 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
         if (ph > 0)
             lds_barrier();      // the previous phase's stages are no longer read
         for (int t = 0; t < kKvAhead; ++t)
-            issue(t);
+            issue_next();
 
         // the step loop, compiled once per role (separate register lifetimes)
         auto steps = [&](auto role_c) {
@@ -624,6 +630,7 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
             // byte offsets (uniform) of the stages of tiles it, it - 1 and
             // it + kKvAhead, advanced around the ring each step
             int so_cur = 0, so_prev = (kKvStages - 1) * kTileBytes;
+            int cur_h = 0, cur_k = 0;       // (head, query tile) of step it
             for (int it = 0; n_iter > 0 && it <= n_iter; ++it) {
                 const int ahead = max(0, min(kKvAhead - 1, n_iter - 1 - it));
                 if (ahead == 2) {
@@ -640,58 +647,31 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
                 }
                 lds_barrier();
-                issue(it + kKvAhead);
                 const int st_cur = so_cur / kTileBytes, st_prev = so_prev / kTileBytes;
+                // The next tile's loads are requested after this step's first
+                // LDS reads, so that their scalar address work runs while
+                // those reads are in flight.
                 if constexpr (kRole == 0) {
                     if (it < n_iter) {
-                        // S = Q K^T: lane holds key l32 and query rows 8*(i/4) + 4*hi + i%4
-                        f32x16 sc = f32x16{};
-                        {
-                            bf16x8 qa[8];
-#pragma unroll
-                            for (int sd = 0; sd < 8; ++sd)
-                                qa[sd] = lds_b128(lds + so_cur, rowb[sd]);
-                            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                            for (int sd = 0; sd < 8; ++sd)
-                                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[sd], kv[sd], sc,
-                                                                             0, 0, 0);
-                        }
-                        const int64_t qpos0 = b.q_offset + q_row0(it);
-                        const bool need_mask = b.causal && first_key_pos + kKvRows - 1 > qpos0;
-                        int lim = -1;
-                        if (need_mask) {
-                            // lane's key position minus the tile's first query position
-                            const int base = (int)min(max(first_key_pos - qpos0, (int64_t)-1024),
-                                                      (int64_t)1024);
-                            lim = min(max(base + lane_key, -1), 64);
-                        }
-                        // P, then to the pair's role-1 wavefront (lane to lane)
-                        const char LDS_AS *pw = lds + (it & 1) * (kKvPairs * kPBytes);
+                        // S = Q K^T: lane holds key l32 and query rows 8*(i/4) + 4*hi + i%4;
+                        // the rows' lse read with the q fragments
                         const char LDS_AS *lt = lds + st_cur * 2 * kStatBytes;
+                        bf16x8 qa[8];
                         f32x4 l4s[4];
+#pragma unroll
+                        for (int sd = 0; sd < 8; ++sd)
+                            qa[sd] = lds_b128(lds + so_cur, rowb[sd]);
 #pragma unroll
                         for (int i4 = 0; i4 < 4; ++i4)
                             l4s[i4] = *(const f32x4 LDS_AS *)(lt + i4 * 32 + statb);
+                        issue_next();
                         __builtin_amdgcn_sched_barrier(0);
-                        bf16x8 pf[2];
+                        f32x16 sc = f32x16{};
 #pragma unroll
-                        for (int i4 = 0; i4 < 4; ++i4) {
-                            const f32x4 l4 = l4s[i4];
-                            f32x4 p4;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const int i = 4 * i4 + e;
-                                float p = __builtin_amdgcn_exp2f(
-                                    __builtin_fmaf(sc[i], c, -l4[e] * kLog2e));
-                                const int qi = 8 * i4 + 4 * hi + e;
-                                p = qi >= lim ? p : 0.f;
-                                p4[e] = p;
-                                pf[i >> 3][i & 7] = (__bf16)p;
-                            }
-                            *(f32x4 LDS_AS *)(pw + i4 * 1024 + pl) = p4;
-                        }
-                        // dV += P^T dO
+                        for (int sd = 0; sd < 8; ++sd)
+                            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[sd], kv[sd], sc, 0, 0,
+                                                                         0);
+                        // dout column fragments for dV, in flight during the softmax
                         bf16x8 dc[2][4];
 #pragma unroll
                         for (int kh = 0; kh < 2; ++kh)
@@ -699,36 +679,86 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
                             for (int db = 0; db < 4; ++db)
                                 dc[kh][db] = colf(so_cur, kh, db);
                         __builtin_amdgcn_sched_barrier(0);
+                        const int64_t qpos0 =
+                            b.q_offset +
+                            (int64_t)(down ? n_qt_all - 1 - cur_k : qt_begin + cur_k) * kTileRows;
+                        const bool need_mask = b.causal && first_key_pos + kKvRows - 1 > qpos0;
+                        // P, then to the pair's role-1 wavefront (lane to lane)
+                        const char LDS_AS *pw = lds + (it & 1) * (kKvPairs * kPBytes);
+                        bf16x8 pf[2];
+                        // the mask compares run only on tiles that cross the diagonal
+                        auto softmax = [&](auto masked_c) {
+                            constexpr bool kMasked = decltype(masked_c)::value;
+                            int lim = -1;
+                            if constexpr (kMasked) {
+                                // lane's key position minus the tile's first query position
+                                const int base = (int)min(
+                                    max(first_key_pos - qpos0, (int64_t)-1024), (int64_t)1024);
+                                lim = min(max(base + lane_key, -1), 64);
+                            }
+#pragma unroll
+                            for (int i4 = 0; i4 < 4; ++i4) {
+                                const f32x4 l4 = l4s[i4];
+                                f32x4 p4;
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const int i = 4 * i4 + e;
+                                    float p = __builtin_amdgcn_exp2f(
+                                        __builtin_fmaf(sc[i], c, -l4[e] * kLog2e));
+                                    if constexpr (kMasked) {
+                                        const int qi = 8 * i4 + 4 * hi + e;
+                                        p = qi >= lim ? p : 0.f;
+                                    }
+                                    p4[e] = p;
+                                    pf[i >> 3][i & 7] = (__bf16)p;
+                                }
+                                *(f32x4 LDS_AS *)(pw + i4 * 1024 + pl) = p4;
+                            }
+                        };
+                        if (need_mask)
+                            softmax(std::true_type{});
+                        else
+                            softmax(std::false_type{});
+                        // dV += P^T dO
 #pragma unroll
                         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                             for (int db = 0; db < 4; ++db)
                                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                                     pf[kh], dc[kh][db], acc[db], 0, 0, 0);
+                    } else {
+                        issue_next();
                     }
                 } else {
                     if (it > 0) {
-                        // dP = dO V^T (tile it - 1), same layout as S
-                        f32x16 dp = f32x16{};
-                        {
-                            bf16x8 da[8];
-#pragma unroll
-                            for (int sd = 0; sd < 8; ++sd)
-                                da[sd] = lds_b128(lds + so_prev, rowb[sd]);
-                            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                            for (int sd = 0; sd < 8; ++sd)
-                                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[sd], kv[sd], dp,
-                                                                             0, 0, 0);
-                        }
+                        // dP = dO V^T (tile it - 1), same layout as S; role 0's P
+                        // and the rows' dvec read with the dout fragments
                         const char LDS_AS *pr = lds + ((it - 1) & 1) * (kKvPairs * kPBytes);
                         const char LDS_AS *vt = lds + st_prev * 2 * kStatBytes;
+                        bf16x8 da[8];
                         f32x4 p4s[4], d4s[4];
+#pragma unroll
+                        for (int sd = 0; sd < 8; ++sd)
+                            da[sd] = lds_b128(lds + so_prev, rowb[sd]);
 #pragma unroll
                         for (int i4 = 0; i4 < 4; ++i4) {
                             p4s[i4] = *(const f32x4 LDS_AS *)(pr + i4 * 1024 + pl);
                             d4s[i4] = *(const f32x4 LDS_AS *)(vt + i4 * 32 + statb);
                         }
+                        issue_next();
+                        __builtin_amdgcn_sched_barrier(0);
+                        f32x16 dp = f32x16{};
+#pragma unroll
+                        for (int sd = 0; sd < 8; ++sd)
+                            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[sd], kv[sd], dp, 0, 0,
+                                                                         0);
+                        // q column fragments for dK, in flight during dS
+                        bf16x8 qc[2][4];
+#pragma unroll
+                        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                            for (int db = 0; db < 4; ++db)
+                                qc[kh][db] = colf(so_prev, kh, db);
                         __builtin_amdgcn_sched_barrier(0);
                         bf16x8 sf[2];
 #pragma unroll
@@ -742,20 +772,19 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
                             }
                         }
                         // dK += dS^T Q
-                        bf16x8 qc[2][4];
-#pragma unroll
-                        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                            for (int db = 0; db < 4; ++db)
-                                qc[kh][db] = colf(so_prev, kh, db);
-                        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                             for (int db = 0; db < 4; ++db)
                                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                                     sf[kh], qc[kh][db], acc[db], 0, 0, 0);
+                    } else {
+                        issue_next();
                     }
+                }
+                if (++cur_h == group) {
+                    cur_h = 0;
+                    ++cur_k;
                 }
                 so_prev = so_cur;
                 so_cur = so_cur == (kKvStages - 1) * kTileBytes ? 0 : so_cur + kTileBytes;
