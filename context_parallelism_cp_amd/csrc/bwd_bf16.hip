@@ -827,10 +827,14 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
                     pk[db * 32] = acc[db][i];
             }
         };
-        if (role == 0)
+        if (role == 0) {
+            // the exponentials' wavefront is the longer chain of the pair:
+            // it goes first when both can issue (+1% measured)
+            __builtin_amdgcn_s_setprio(1);
             steps(IC<0>{});
-        else
+        } else {
             steps(IC<1>{});
+        }
     }
 }
 
