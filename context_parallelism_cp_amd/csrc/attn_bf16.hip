@@ -314,6 +314,18 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
         seg_tiles[kv_i] = (int)((n_keys + BN - 1) / BN);
     }
     const int n_tiles = seg_tiles[0] + seg_tiles[1];
+    // Per segment, 32-bit bounds for the mask decisions (segments are
+    // shorter than 2^30 keys): key k of the segment is past its end iff
+    // k >= seg_len, and the workgroup's row at offset r sees k iff
+    // k <= seg_diag + r.  seg_diag is first_pos - pos0 clamped to
+    // [-512, len + 64], which changes no decision: rows are fewer than 512
+    // and no tile reaches past len.
+    int seg_len[2] = {0, 0}, seg_diag[2] = {0, 0};
+    for (int kv_i = 0; kv_i < qs.n_kv; ++kv_i) {
+        const KvSeg &kv = qs.kv[kv_i];
+        seg_len[kv_i] = (int)kv.len;
+        seg_diag[kv_i] = (int)min(max(first_pos - kv.pos0, (int64_t)-512), kv.len + 64);
+    }
 
     auto tile_ref = [&](int t) {
         TileRef r;
@@ -409,13 +421,9 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
         __syncthreads();
         issue(t + 2, std::integral_constant<int, (ST + 2) % 3>{});
         const TileRef r = tile_ref(t);
-        // The segment's length and position are read here, while no LDS read
-        // is in flight, and pinned in scalar registers: read at their first
-        // use (after the V fragment requests) the argument-block load's wait
-        // would also drain those LDS reads before the softmax.
-        int64_t kv_len = qs.kv[r.seg].len;
-        int64_t kv_pos0 = qs.kv[r.seg].pos0;
-        __asm__ volatile("" : "+s"(kv_len), "+s"(kv_pos0));
+        int len_c = r.seg == 0 ? seg_len[0] : seg_len[1];
+        int diag_c = r.seg == 0 ? seg_diag[0] : seg_diag[1];
+        __asm__ volatile("" : "+s"(len_c), "+s"(diag_c));
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             f32x16 cur[QB];
@@ -434,16 +442,14 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
             else if (t + 1 < n_tiles)
                 load_k(stage_base<(ST + 1) % 3>());
             __builtin_amdgcn_sched_barrier(0);
-            const int64_t key0 = r.key0 + half * 32;      // first key of the half tile
-            const bool need_mask = (key0 + 32 > kv_len) ||
-                                   (a.causal && kv_pos0 + key0 + 31 > first_pos);
+            const int key0 = (int)r.key0 + half * 32;     // first key of the half tile
+            const bool need_mask = (key0 + 32 > len_c) || (a.causal && key0 + 31 > diag_c);
             if (need_mask) {
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) {
                     // key k of the half tile (0..31) is visible iff k <= lim
-                    const int tail = (int)min(max(kv_len - 1 - key0, (int64_t)-1), (int64_t)64);
-                    const int base_c = (int)min(max(first_pos - kv_pos0 - key0, (int64_t)-512),
-                                                (int64_t)512);
+                    const int tail = min(max(len_c - 1 - key0, -1), 64);
+                    const int base_c = min(max(diag_c - key0, -512), 512);
                     const int lim = a.causal ? min(tail, base_c + row_off[qb]) : tail;
                     const int lim_l = max(lim, -1) - 4 * hi;
 #pragma unroll

@@ -141,6 +141,10 @@ int check_attn_common(const void *q, const void *k, const void *v, const float *
         // a 64-row K or V tile is addressed with 32-bit byte offsets
         if ((int64_t)Hkv * D >= ((int64_t)1 << 24))
             return fail(CP_ERR_UNSUPPORTED, "bf16 attention needs Hkv * D < 2^24 (Hkv=%d)", Hkv);
+        // the kernel takes its mask decisions on 32-bit in-segment key indices
+        if (Sq >= ((int64_t)1 << 30) || Sk >= ((int64_t)1 << 30))
+            return fail(CP_ERR_UNSUPPORTED, "bf16 attention needs Sq, Sk < 2^30 (Sq=%lld, Sk=%lld)",
+                        (long long)Sq, (long long)Sk);
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
             return fail(CP_ERR_ALIGN, "bf16 attention needs 16-byte aligned q, k, v and out");
     } else if (dtype == CP_F32) {

@@ -108,12 +108,13 @@ typedef struct {
  *   iff k_offset + j <= q_offset + i (the diagonal is visible);
  *   lse[h][i] = log sum_j exp(s[i][j]) over visible j;
  *   out[i][h] = sum_j exp(s[i][j] - lse[h][i]) v[j].
- * dtype CP_BF16 (q, k, v bf16; D must be 128, Hkv * D < 2^24) runs on bf16 MFMA with float32
+ * dtype CP_BF16 (q, k, v bf16; D must be 128, Hkv * D < 2^24, Sq and Sk below
+ * 2^30) runs on bf16 MFMA with float32
  * accumulation and the probabilities rounded to bf16 before the second
  * product; CP_F32 (1 <= D <= 128) runs in float32.
  * Sq == 0 is a no-op; Sk == 0 writes out = 0, lse = -inf.
  * Errors: CP_ERR_NULL, CP_ERR_SHAPE (negative sizes, Hq % Hkv != 0,
- * Hq or Hkv < 1), CP_ERR_UNSUPPORTED (D, or Hkv * D for bf16), CP_ERR_ALIGN,
+ * Hq or Hkv < 1), CP_ERR_UNSUPPORTED (D, or Hkv * D, Sq or Sk for bf16), CP_ERR_ALIGN,
  * CP_ERR_HIP.
  */
 int cp_attn_block_fwd(const void *q, const void *k, const void *v, float *out, float *lse,

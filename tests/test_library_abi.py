@@ -102,6 +102,10 @@ def test_block_fwd_argument_errors():
     # bf16 tiles are addressed with 32-bit byte offsets: Hkv * D < 2^24
     assert rc_block(Hq=1 << 17, Hkv=1 << 17) == cp.CP_ERR_UNSUPPORTED
     assert "2^24" in cp.cp_last_error()
+    # and takes its mask decisions on 32-bit key indices: Sq, Sk < 2^30
+    assert rc_block(Sk=1 << 30) == cp.CP_ERR_UNSUPPORTED
+    assert "2^30" in cp.cp_last_error()
+    assert rc_block(Sq=1 << 30) == cp.CP_ERR_UNSUPPORTED
     assert rc_block(q=FAKE + 2) == cp.CP_ERR_ALIGN
     assert rc_block(out=FAKE) == cp.CP_ERR_ALIGN          # out overlaps q
     assert "overlap" in cp.cp_last_error()
