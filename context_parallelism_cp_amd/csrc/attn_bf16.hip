@@ -144,36 +144,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, int
 
 constexpr int kLoadsPerLane = 16 / kWaves;  // 1 KiB blocks of a tile filled per wave
 
-// Issue the direct-to-LDS loads of one K tile and one V tile (keys
-// key0 .. key0+63 of a KV segment of `len` rows) into `stage`.  The buffer
-// resources end after the last row of the segment, so the chunks of rows
-// past it read as zeros (their scores are masked).  The tile's address
-// arithmetic is uniform (scalar unit); a lane adds only its fixed offset:
-// the chunk it copies sits in row blk*4 + lane/16 of the tile and lands in
-// the LDS slot the swizzle gives it.
+// Issue the direct-to-LDS loads of one K tile and one V tile (the `rows`
+// rows at kbase and vbase, rows <= 64, row_bytes apart) into `stage`.  The
+// buffer resources end after the last row, so the chunks of rows past it
+// read as zeros (their scores are masked).  The tile's address arithmetic
+// is uniform (scalar unit); a lane adds only its fixed offset off[i]: the
+// chunk it copies sits in row blk*4 + lane/16 of the tile and lands in the
+// LDS slot the swizzle gives it.
 __device__ __forceinline__ void load_tile(char LDS_AS *stage, const __bf16 *kbase,
-                                          const __bf16 *vbase, int64_t row_stride,
-                                          int64_t key0, int64_t len, int wave, int lane)
+                                          const __bf16 *vbase, int row_bytes, int rows,
+                                          const int (&off)[kLoadsPerLane], int wave)
 {
-    // The lane offsets are recomputed at every call (a few VALU operations
-    // per tile): the opaque copy of the lane index keeps the compiler from
-    // hoisting them out of the tile loop, which changes its register
-    // allocation of the loop for the worse.
-    __asm__ volatile("" : "+v"(lane));
-    const int64_t rows = min(len - key0, (int64_t)BN);   // >= 1 for an issued tile
-    const int row_bytes = (int)(row_stride * 2);
-    const int bytes = (int)(rows - 1) * row_bytes + HD * 2;
-    const auto rk = buffer_rsrc(kbase + key0 * row_stride, bytes);
-    const auto rv = buffer_rsrc(vbase + key0 * row_stride, bytes);
+    const int bytes = (rows - 1) * row_bytes + HD * 2;
+    const auto rk = buffer_rsrc(kbase, bytes);
+    const auto rv = buffer_rsrc(vbase, bytes);
 #pragma unroll
     for (int i = 0; i < kLoadsPerLane; ++i) {
         const int blk = wave * kLoadsPerLane + i;
-        const int r = blk * 4 + (lane >> 4);
-        const int off = r * row_bytes + (((lane & 15) ^ swz(r)) << 4);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (void LDS_AS *)(stage + blk * 1024), 16,
-                                                 off, 0, 0, 0);
+                                                 off[i], 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rv, (void LDS_AS *)(stage + kTileBytes + blk * 1024), 16, off, 0, 0, 0);
+            rv, (void LDS_AS *)(stage + kTileBytes + blk * 1024), 16, off[i], 0, 0, 0);
     }
 }
 
@@ -321,10 +312,14 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
     // [-512, len + 64], which changes no decision: rows are fewer than 512
     // and no tile reaches past len.
     int seg_len[2] = {0, 0}, seg_diag[2] = {0, 0};
-    for (int kv_i = 0; kv_i < qs.n_kv; ++kv_i) {
-        const KvSeg &kv = qs.kv[kv_i];
-        seg_len[kv_i] = (int)kv.len;
-        seg_diag[kv_i] = (int)min(max(first_pos - kv.pos0, (int64_t)-512), kv.len + 64);
+#pragma unroll
+    for (int kv_i = 0; kv_i < 2; ++kv_i) {
+        if (kv_i < qs.n_kv) {
+            const KvSeg &kv = qs.kv[kv_i];
+            seg_len[kv_i] = __builtin_amdgcn_readfirstlane((int)kv.len);
+            seg_diag[kv_i] = __builtin_amdgcn_readfirstlane(
+                (int)min(max(first_pos - kv.pos0, (int64_t)-512), kv.len + 64));
+        }
     }
 
     auto tile_ref = [&](int t) {
@@ -333,13 +328,24 @@ void attn_bf16_kernel(AttnLaunch a, TileMap tm, float scale_log2)
         r.key0 = (int64_t)(r.seg == 0 ? t : t - seg_tiles[0]) * BN;
         return r;
     };
+    // Each lane's byte offsets into a tile for its share of the loads (the
+    // same for every tile, kept in registers across the loop).
+    const int row_bytes = (int)(kv_stride * 2);
+    int dma_off[kLoadsPerLane];
+#pragma unroll
+    for (int i = 0; i < kLoadsPerLane; ++i) {
+        const int rr = (wave * kLoadsPerLane + i) * 4 + (lane >> 4);
+        dma_off[i] = rr * row_bytes + (((lane & 15) ^ swz(rr)) << 4);
+    }
     // loads of tile t into stage ST (ST == t % 3)
     auto issue = [&](int t, auto st) {
         if (t < n_tiles) {
             const TileRef r = tile_ref(t);
             const KvSeg &kv = qs.kv[r.seg];
-            load_tile(stage_base<decltype(st)::value>(), kg + kv.row0 * kv_stride,
-                      vg + kv.row0 * kv_stride, kv_stride, r.key0, kv.len, wave, lane);
+            const int rows = min((r.seg == 0 ? seg_len[0] : seg_len[1]) - (int)r.key0, BN);
+            const int64_t e0 = (kv.row0 + r.key0) * kv_stride;
+            load_tile(stage_base<decltype(st)::value>(), kg + e0, vg + e0, row_bytes, rows,
+                      dma_off, wave);
         }
     };
 
