@@ -153,35 +153,6 @@ __device__ __forceinline__ void dma4(uint32_t lds, int voff, const i32x4 &r)
                      : "memory", "m0");
 }
 
-// Rows row0 .. row0+kTileRows-1 (of `len`) of two bf16 tensors with
-// `row_stride` elements between rows (128 elements each) into the tiles at
-// LDS addresses ta and tb: lane l of a load fills 16 bytes of a 1-KiB block
-// (4 rows); rows past len read as zeros.  kWavesT wavefronts share the
-// blocks; each issues 2 * kTileRows / 4 / kWavesT loads.
-template <int kWavesT>
-__device__ __forceinline__ void load_two_tiles(uint32_t ta, uint32_t tb, const __bf16 *a,
-                                               const __bf16 *b, int64_t row_stride,
-                                               int64_t row0, int64_t len, int wave, int lane)
-{
-    constexpr int kBlocks = kTileRows / 4;
-    static_assert(kBlocks % kWavesT == 0, "blocks per wavefront");
-    constexpr int kPer = kBlocks / kWavesT;
-    __asm__ volatile("" : "+v"(lane));
-    const int64_t rows = min(len - row0, (int64_t)kTileRows);   // >= 1
-    const int row_bytes = (int)(row_stride * 2);
-    const int bytes = (int)(rows - 1) * row_bytes + HD * 2;
-    const i32x4 ra = rsrc(a + row0 * row_stride, bytes);
-    const i32x4 rb = rsrc(b + row0 * row_stride, bytes);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int blk = wave * kPer + i;
-        const int r = blk * 4 + (lane >> 4);
-        const int off = r * row_bytes + (((lane & 15) ^ swz(r)) << 4);
-        dma16(ta + blk * 1024, off, ra);
-        dma16(tb + blk * 1024, off, rb);
-    }
-}
-
 // s_waitcnt operand waiting for the vector-memory counter only (gfx9
 // encoding: vmcnt bits 3:0 and 15:14; expcnt 6:4, lgkmcnt 11:8 at maximum)
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
@@ -201,6 +172,7 @@ constexpr int kDqStage = 2 * kTileBytes;               // K then V
 // the ring's three stages, K then V in each
 __shared__ __attribute__((aligned(1024))) char g_dq[3 * kDqStage];
 constexpr int kDqLoads = 2 * (kTileRows / 4) / kDqWaves;   // tile loads per wavefront
+static_assert(kTileRows == 32 && kDqLoads == 2, "one K and one V block per wavefront and tile");
 
 // Order of the dq launch's (head, row tile) units over the XCDs (workgroup
 // b runs on XCD b % 8, as its slot b / 8):
@@ -291,11 +263,35 @@ void bwd_dq_kernel(BwdLaunch b, DqWork w)
     const __bf16 *kg = (const __bf16 *)b.k + g * HD;
     const __bf16 *vg = (const __bf16 *)b.v + g * HD;
     const uint32_t ring = (uint32_t)(uintptr_t)(char LDS_AS *)g_dq;
+    // 32-bit key bounds for the loads and the mask (Sk < 2^30): key k is past
+    // the block iff k >= sk32, and the wavefront's row at offset r sees k
+    // iff k <= diag32 + r (first_pos - k_offset clamped to [-512, Sk + 64],
+    // which changes no decision: rows are fewer than 512, keys end at Sk)
+    const int sk32 = (int)b.Sk;
+    const int diag32 = __builtin_amdgcn_readfirstlane(
+        (int)min(max(first_pos - b.k_offset, (int64_t)-512), b.Sk + 64));
+    // each lane's byte offsets into a tile for its share of the loads
+    const int row_bytes = (int)(kv_stride * 2);
+    int dma_off[kDqLoads / 2];
+#pragma unroll
+    for (int i = 0; i < kDqLoads / 2; ++i) {
+        const int rr = (wave * (kDqLoads / 2) + i) * 4 + (lane >> 4);
+        dma_off[i] = rr * row_bytes + (((lane & 15) ^ swz(rr)) << 4);
+    }
     auto issue = [&](int t) {
         if (t < n_tiles) {
             const uint32_t st = ring + (uint32_t)(t % 3) * kDqStage;
-            load_two_tiles<kDqWaves>(st, st + kTileBytes, kg, vg, kv_stride,
-                                     (int64_t)t * kTileRows, b.Sk, wave, lane);
+            const int key0 = t * kTileRows;
+            const int rows = min(sk32 - key0, kTileRows);
+            const int bytes = (rows - 1) * row_bytes + HD * 2;
+            const i32x4 ra = rsrc(kg + (int64_t)key0 * kv_stride, bytes);
+            const i32x4 rb = rsrc(vg + (int64_t)key0 * kv_stride, bytes);
+#pragma unroll
+            for (int i = 0; i < kDqLoads / 2; ++i) {
+                const int blk = wave * (kDqLoads / 2) + i;
+                dma16(st + blk * 1024, dma_off[i], ra);
+                dma16(st + kTileBytes + blk * 1024, dma_off[i], rb);
+            }
         }
     };
     const FragOffsets fo = frag_offsets(lane);
@@ -314,73 +310,85 @@ void bwd_dq_kernel(BwdLaunch b, DqWork w)
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         lds_barrier();
         issue(t + 2);
-        const char LDS_AS *kt = (const char LDS_AS *)g_dq + (t % 3) * kDqStage;
-        const char LDS_AS *vt = kt + kTileBytes;
+        // this step's per-lane LDS addresses: the stage offset added once to
+        // each fragment's lane offset, the K / V / row parts as immediates
+        int so = (t % 3) * kDqStage;
+        // opaque, so that the compiler adds it once per fragment instead of
+        // strength-reducing the modulo into extra per-read arithmetic
+        __asm__ volatile("" : "+s"(so));
+        int rowb[8], colb[2][4];
 #pragma unroll
-        for (int half = 0; half < kTileRows / 32; ++half) {
-            // S^T = K Q^T, then dP^T = V dO^T, for the 32 keys of this half;
-            // one set of eight fragments is live at a time
-            f32x16 s = f32x16{}, dp = f32x16{};
-            {
-                bf16x8 kf[8];
+        for (int sd = 0; sd < 8; ++sd)
+            rowb[sd] = fo.rowf[sd] + so;
 #pragma unroll
-                for (int sd = 0; sd < 8; ++sd)
-                    kf[sd] = lds_b128(kt + half * 32 * 256, fo.rowf[sd]);
-                __builtin_amdgcn_sched_barrier(0);
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int sd = 0; sd < 8; ++sd)
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sd], qf[sd], s, 0, 0, 0);
-            }
-            {
-                bf16x8 vf[8];
+            for (int db = 0; db < 4; ++db)
+                colb[x][db] = fo.col[x][db] + so;
+        const char LDS_AS *lds = (const char LDS_AS *)g_dq;
+        // S^T = K Q^T, then dP^T = V dO^T, for the tile's 32 keys; one set of
+        // eight fragments is live at a time
+        f32x16 s = f32x16{}, dp = f32x16{};
+        {
+            bf16x8 kf[8];
 #pragma unroll
-                for (int sd = 0; sd < 8; ++sd)
-                    vf[sd] = lds_b128(vt + half * 32 * 256, fo.rowf[sd]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int sd = 0; sd < 8; ++sd)
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sd], df[sd], dp, 0, 0, 0);
-            }
-            // K^T fragments for dQ^T, requested while the MFMAs run
-            bf16x8 kc[2][4];
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    kc[kh][db] = col_frag(kt, fo, 2 * half + kh, db);
+            for (int sd = 0; sd < 8; ++sd)
+                kf[sd] = lds_b128(lds, rowb[sd]);
             __builtin_amdgcn_sched_barrier(0);
-            const int64_t key0 = (int64_t)t * kTileRows + half * 32;
-            const bool need_mask = (key0 + 32 > b.Sk) ||
-                                   (b.causal && b.k_offset + key0 + 31 > first_pos);
-            if (need_mask) {
-                // key k (0..31) of the half is visible to this lane's row iff k <= lim
-                const int tail = (int)min(max(b.Sk - 1 - key0, (int64_t)-1), (int64_t)64);
-                const int base_c = (int)min(max(first_pos - b.k_offset - key0, (int64_t)-512),
-                                            (int64_t)512);
-                const int lim = b.causal ? min(tail, base_c + wave * 32 + l32) : tail;
-                const int lim_l = max(lim, -1) - 4 * hi;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int kc_i = 8 * (i >> 2) + (i & 3);   // key of register i
-                    s[i] = kc_i > lim_l ? -INFINITY : s[i];
-                }
+            for (int sd = 0; sd < 8; ++sd)
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[sd], qf[sd], s, 0, 0, 0);
+        }
+        {
+            bf16x8 vf[8];
+#pragma unroll
+            for (int sd = 0; sd < 8; ++sd)
+                vf[sd] = lds_b128(lds + kTileBytes, rowb[sd]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int sd = 0; sd < 8; ++sd)
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[sd], df[sd], dp, 0, 0, 0);
+        }
+        // K^T fragments for dQ^T, requested while the MFMAs run
+        bf16x8 kc[2][4];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const i16x4 lo = lds_tr(lds + kh * 16 * 256, colb[0][db]);
+                const i16x4 up = lds_tr(lds + kh * 16 * 256, colb[1][db]);
+                kc[kh][db] = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo),
+                                                     __builtin_bit_cast(bf16x4, up), 0, 1, 2, 3,
+                                                     4, 5, 6, 7);
             }
-            bf16x8 dsf[2];
+        __builtin_amdgcn_sched_barrier(0);
+        const int key0 = t * kTileRows;
+        const bool need_mask = (key0 + 32 > sk32) || (b.causal && key0 + 31 > diag32);
+        if (need_mask) {
+            // key k (0..31) of the tile is visible to this lane's row iff k <= lim
+            const int tail = min(max(sk32 - 1 - key0, -1), 64);
+            const int base_c = min(max(diag32 - key0, -512), 512);
+            const int lim = b.causal ? min(tail, base_c + wave * 32 + l32) : tail;
+            const int lim_l = max(lim, -1) - 4 * hi;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lse2));
-                dsf[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dvi));
+                const int kc_i = 8 * (i >> 2) + (i & 3);   // key of register i
+                s[i] = kc_i > lim_l ? -INFINITY : s[i];
             }
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[kh][db], dsf[kh],
-                                                                     acc[db], 0, 0, 0);
-            // the next half's fragments are not read ahead of these MFMAs
-            // (that would hold two halves' registers at once)
-            __builtin_amdgcn_sched_barrier(0);
         }
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lse2));
+            dsf[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dvi));
+        }
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[kh][db], dsf[kh], acc[db], 0,
+                                                                 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     issue(0);

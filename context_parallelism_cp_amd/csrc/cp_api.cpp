@@ -192,6 +192,10 @@ int check_bwd(const void *q, const void *k, const void *v, const void *dout, con
             return fail(CP_ERR_UNSUPPORTED, "bf16 backward supports D = 128 only (D=%d)", D);
         if ((int64_t)Hkv * D >= ((int64_t)1 << 24))
             return fail(CP_ERR_UNSUPPORTED, "bf16 backward needs Hkv * D < 2^24 (Hkv=%d)", Hkv);
+        // the kernels take their mask decisions on 32-bit key indices
+        if (Sq >= ((int64_t)1 << 30) || Sk >= ((int64_t)1 << 30))
+            return fail(CP_ERR_UNSUPPORTED, "bf16 backward needs Sq, Sk < 2^30 (Sq=%lld, Sk=%lld)",
+                        (long long)Sq, (long long)Sk);
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dout, 16) ||
             !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
             return fail(CP_ERR_ALIGN, "bf16 backward needs 16-byte aligned tensors");

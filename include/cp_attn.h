@@ -197,8 +197,8 @@ int cp_attn_bwd_dvec(const float *out, const void *dout, float *dvec, int64_t Sq
  * [Hq][Sq] float32 (the rows' final log-sum-exp, and cp_attn_bwd_dvec of
  * their final out); dq [Sq][Hq][D], dk and dv [Sk][Hkv][D] float32.
  * accumulate == 0 overwrites dq, dk and dv; accumulate != 0 adds into them.
- * dtype CP_BF16 (D = 128, Hkv * D < 2^24) runs on bf16 MFMA with float32
- * accumulation, P and ds rounded to bf16 before the products that take
+ * dtype CP_BF16 (D = 128, Hkv * D < 2^24, Sq and Sk below 2^30) runs on bf16
+ * MFMA with float32 accumulation, P and ds rounded to bf16 before the products that take
  * them; CP_F32 (1 <= D <= 128) runs in float32.  dq, dk and dv must not
  * overlap each other or any input.
  * Errors: CP_ERR_NULL, CP_ERR_SHAPE, CP_ERR_UNSUPPORTED, CP_ERR_ALIGN,

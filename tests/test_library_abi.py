@@ -209,6 +209,8 @@ def test_block_bwd_argument_errors():
     assert rc_block_bwd(D=129, dtype=cp.CP_F32) == cp.CP_ERR_UNSUPPORTED
     assert rc_block_bwd(dtype=5) == cp.CP_ERR_UNSUPPORTED
     assert rc_block_bwd(Hq=1 << 17, Hkv=1 << 17) == cp.CP_ERR_UNSUPPORTED
+    assert rc_block_bwd(Sk=1 << 30) == cp.CP_ERR_UNSUPPORTED and "2^30" in cp.cp_last_error()
+    assert rc_block_bwd(Sq=1 << 30) == cp.CP_ERR_UNSUPPORTED
     assert rc_block_bwd(dout=FAKE * 4 + 2) == cp.CP_ERR_ALIGN
     assert rc_block_bwd(dq=FAKE * 7 + 4) == cp.CP_ERR_ALIGN          # 16 B for bf16
     assert rc_block_bwd(dq=FAKE * 4) == cp.CP_ERR_ALIGN              # dq overlaps dout
