@@ -561,33 +561,42 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
         // it % kKvStages.  The loads walk the (query tile, head) pairs in step
         // order; the next pair to request is a cursor advanced by one per
         // call, so a request costs no division by the group size.
-        int c_it = 0, c_h = 0, c_k = 0, c_st = 0;
+        // The cursor also carries the pair's element offsets into q / dout
+        // and into the statistics (scalar adds per call, no 64-bit products).
+        int c_it = 0, c_h = 0, c_st = 0;
+        int c_q0 = down ? (n_qt_all - 1) * kTileRows : qt_begin * kTileRows;   // first row
+        const int q_step = down ? -kTileRows : kTileRows;
+        int64_t c_e0 = (int64_t)c_q0 * q_stride + (int64_t)g * group * HD;   // q / dout element
+        int64_t c_s0 = (int64_t)g * group * b.stat_ld + c_q0;                // lse / dvec element
+        const int64_t e_next_k = (int64_t)q_step * q_stride - (int64_t)(group - 1) * HD;
+        const int64_t s_next_k = (int64_t)q_step - (int64_t)(group - 1) * b.stat_ld;
+        const int sq32 = (int)b.Sq;
         auto issue_next = [&]() {
             if (c_it < n_iter) {
-                const int h = g * group + c_h;
-                const int64_t q0 =
-                    (int64_t)(down ? n_qt_all - 1 - c_k : qt_begin + c_k) * kTileRows;
-                const int64_t rows = min(b.Sq - q0, (int64_t)kTileRows);   // >= 1
-                const int bytes = (int)(rows - 1) * row_bytes + HD * 2;
-                const int64_t e0 = q0 * q_stride + h * HD;
+                const int rows = min(sq32 - c_q0, kTileRows);   // >= 1
+                const int bytes = (rows - 1) * row_bytes + HD * 2;
                 dma16(ring + kQOff + c_st * kTileBytes + wave * 1024, dma_off,
-                      rsrc((const __bf16 *)b.q + e0, bytes));
+                      rsrc((const __bf16 *)b.q + c_e0, bytes));
                 dma16(ring + kDOff + c_st * kTileBytes + wave * 1024, dma_off,
-                      rsrc((const __bf16 *)b.dout + e0, bytes));
+                      rsrc((const __bf16 *)b.dout + c_e0, bytes));
                 if (wave == 0) {
                     // lse and dvec of the tile's rows (rows past Sq read as zeros)
-                    const int sb = (int)rows * 4;
-                    dma4(ring + kSOff + c_st * 2 * kStatBytes, lane * 4,
-                         rsrc(b.lse + h * b.stat_ld + q0, sb));
+                    const int sb = rows * 4;
+                    dma4(ring + kSOff + c_st * 2 * kStatBytes, lane * 4, rsrc(b.lse + c_s0, sb));
                     dma4(ring + kSOff + c_st * 2 * kStatBytes + kStatBytes, lane * 4,
-                         rsrc(b.dvec + h * b.stat_ld + q0, sb));
+                         rsrc(b.dvec + c_s0, sb));
                 }
             }
             ++c_it;
             c_st = c_st == kKvStages - 1 ? 0 : c_st + 1;
             if (++c_h == group) {
                 c_h = 0;
-                ++c_k;
+                c_q0 += q_step;
+                c_e0 += e_next_k;
+                c_s0 += s_next_k;
+            } else {
+                c_e0 += HD;
+                c_s0 += b.stat_ld;
             }
         };
 
@@ -638,7 +647,14 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
             // byte offsets (uniform) of the stages of tiles it, it - 1 and
             // it + kKvAhead, advanced around the ring each step
             int so_cur = 0, so_prev = (kKvStages - 1) * kTileBytes;
-            int cur_h = 0, cur_k = 0;       // (head, query tile) of step it
+            int cur_h = 0;                  // head of step it within the group
+            // first query row of step it, and the key tile's first position
+            // minus the query block's, clamped to 32 bits: the mask decisions
+            // compare it with row offsets in [0, 2^30), so [-2^30, 2^30 + 4096]
+            // keeps every decision and the clamped window below
+            int cur_q0 = down ? (n_qt_all - 1) * kTileRows : qt_begin * kTileRows;
+            const int dk32 = (int)min(max(first_key_pos - b.q_offset, -((int64_t)1 << 30)),
+                                      ((int64_t)1 << 30) + 4096);
             for (int it = 0; n_iter > 0 && it <= n_iter; ++it) {
                 const int ahead = max(0, min(kKvAhead - 1, n_iter - 1 - it));
                 if (ahead == 2) {
@@ -687,10 +703,7 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
                             for (int db = 0; db < 4; ++db)
                                 dc[kh][db] = colf(so_cur, kh, db);
                         __builtin_amdgcn_sched_barrier(0);
-                        const int64_t qpos0 =
-                            b.q_offset +
-                            (int64_t)(down ? n_qt_all - 1 - cur_k : qt_begin + cur_k) * kTileRows;
-                        const bool need_mask = b.causal && first_key_pos + kKvRows - 1 > qpos0;
+                        const bool need_mask = b.causal && dk32 + kKvRows - 1 > cur_q0;
                         // P, then to the pair's role-1 wavefront (lane to lane)
                         const char LDS_AS *pw = lds + (it & 1) * (kKvPairs * kPBytes);
                         bf16x8 pf[2];
@@ -700,8 +713,7 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
                             int lim = -1;
                             if constexpr (kMasked) {
                                 // lane's key position minus the tile's first query position
-                                const int base = (int)min(
-                                    max(first_key_pos - qpos0, (int64_t)-1024), (int64_t)1024);
+                                const int base = min(max(dk32 - cur_q0, -1024), 1024);
                                 lim = min(max(base + lane_key, -1), 64);
                             }
 #pragma unroll
@@ -792,7 +804,7 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
                 }
                 if (++cur_h == group) {
                     cur_h = 0;
-                    ++cur_k;
+                    cur_q0 += down ? -kTileRows : kTileRows;
                 }
                 so_prev = so_cur;
                 so_cur = so_cur == (kKvStages - 1) * kTileBytes ? 0 : so_cur + kTileBytes;
