@@ -600,15 +600,48 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
             }
         };
 
-        // step it: every wavefront's loads of tile it have landed (later
-        // tiles may still be in flight), every wavefront has finished step
-        // it - 1, then tile it + kKvAhead is requested into the stage of
+        // step it: every wavefront's loads of tiles it and it + 1 have landed
+        // (tile it + 2 may still be in flight), every wavefront has finished
+        // step it - 1, then tile it + kKvAhead is requested into the stage of
         // tile it + kKvAhead - kKvStages = it - 2, whose last reader (role 1)
         // was in step it - 1.
         if (ph > 0)
             lds_barrier();      // the previous phase's stages are no longer read
         for (int t = 0; t < kKvAhead; ++t)
             issue_next();
+        // wait until at most `k` tiles' loads of this wavefront are in flight
+        // (wavefront 0 also loads the statistics)
+        auto wait_tiles = [&](int k) {
+            if (k >= 2) {
+                if (wave == 0)
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads0));
+                else
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads));
+            } else if (k == 1) {
+                if (wave == 0)
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads0));
+                else
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads));
+            } else {
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            }
+        };
+        // The rows' lse is used in log2 units (P = exp2(S c - lse log2 e)):
+        // one wavefront converts a tile's lse in LDS once, the step before
+        // the softmax role reads it (tile it + 1 during step it, tile 0
+        // here), instead of every softmax wavefront multiplying its 16 values
+        // every step.
+        auto lse_to_log2 = [&](int stage) {
+            float LDS_AS *lp =
+                (float LDS_AS *)((char LDS_AS *)g_kv + kSOff + stage * 2 * kStatBytes);
+            lp[lane] = lp[lane] * kLog2e;
+        };
+        if (n_iter > 0) {
+            wait_tiles(min(kKvAhead - 1, n_iter - 1));
+            lds_barrier();
+            if (wave == kKvPairs)
+                lse_to_log2(0);
+        }
 
         // the step loop, compiled once per role (separate register lifetimes)
         auto steps = [&](auto role_c) {
@@ -656,22 +689,13 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
             const int dk32 = (int)min(max(first_key_pos - b.q_offset, -((int64_t)1 << 30)),
                                       ((int64_t)1 << 30) + 4096);
             for (int it = 0; n_iter > 0 && it <= n_iter; ++it) {
-                const int ahead = max(0, min(kKvAhead - 1, n_iter - 1 - it));
-                if (ahead == 2) {
-                    if (wave == 0)
-                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads0));
-                    else
-                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kKvLoads));
-                } else if (ahead == 1) {
-                    if (wave == 0)
-                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads0));
-                    else
-                        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kKvLoads));
-                } else {
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-                }
+                // tiles it and it + 1 landed in every wavefront (tile it + 2
+                // may still be in flight)
+                wait_tiles(max(0, min(1, n_iter - 2 - it)));
                 lds_barrier();
                 const int st_cur = so_cur / kTileBytes, st_prev = so_prev / kTileBytes;
+                if (kRole == 1 && wave == kKvPairs && it + 1 < n_iter)
+                    lse_to_log2(st_cur == kKvStages - 1 ? 0 : st_cur + 1);
                 // The next tile's loads are requested after this step's first
                 // LDS reads, so that their scalar address work runs while
                 // those reads are in flight.
@@ -724,7 +748,7 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
                                 for (int e = 0; e < 4; ++e) {
                                     const int i = 4 * i4 + e;
                                     float p = __builtin_amdgcn_exp2f(
-                                        __builtin_fmaf(sc[i], c, -l4[e] * kLog2e));
+                                        __builtin_fmaf(sc[i], c, -l4[e]));
                                     if constexpr (kMasked) {
                                         const int qi = 8 * i4 + 4 * hi + e;
                                         p = qi >= lim ? p : 0.f;
