@@ -21,7 +21,8 @@
 //     row tiles are spread over the XCDs so that the workgroups an XCD holds
 //     at a time stream the same K/V tiles.  Per 32-key
 //     tile: S^T = K Q^T and dP^T = V dO^T (A = K or V fragments read from
-//     LDS, B = Q^T or dO^T kept in VGPRs), ds in registers, then
+//     LDS, B = Q^T or dO^T kept in VGPRs; the dP product starts from -dvec
+//     instead of zero, so it yields dP - dvec), ds in registers, then
 //     dQ^T += K^T ds^T with K^T from transpose reads of the same K tile.  The
 //     lane holds one query row, so lse and dvec are per-lane scalars.
 //   * bwd_dkdv_kernel: a workgroup of 8 wavefronts (two per SIMD) owns 128
@@ -295,6 +296,12 @@ void bwd_dq_kernel(BwdLaunch b, DqWork w)
         }
     };
     const FragOffsets fo = frag_offsets(lane);
+    // dP - dvec comes out of the dP product directly: its accumulator input
+    // is -dvec (the lane's row) instead of zero
+    f32x16 neg_dv;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        neg_dv[i] = -dvi;
     f32x16 acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -328,7 +335,7 @@ void bwd_dq_kernel(BwdLaunch b, DqWork w)
         const char LDS_AS *lds = (const char LDS_AS *)g_dq;
         // S^T = K Q^T, then dP^T = V dO^T, for the tile's 32 keys; one set of
         // eight fragments is live at a time
-        f32x16 s = f32x16{}, dp = f32x16{};
+        f32x16 s = f32x16{}, dp = neg_dv;
         {
             bf16x8 kf[8];
 #pragma unroll
@@ -380,7 +387,7 @@ void bwd_dq_kernel(BwdLaunch b, DqWork w)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lse2));
-            dsf[i >> 3][i & 7] = (__bf16)(p * (dp[i] - dvi));
+            dsf[i >> 3][i & 7] = (__bf16)(p * dp[i]);
         }
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
@@ -431,7 +438,8 @@ void bwd_dq_kernel(BwdLaunch b, DqWork w)
 // The pair splits the work of its keys by role:
 //   role 0 keeps K^T in registers: S = Q K^T, P = exp(S - lse) (masked),
 //          dV += P^T dO; it passes P (float32) to role 1 through LDS;
-//   role 1 keeps V^T in registers: dP = dO V^T, dS = P (dP - dvec),
+//   role 1 keeps V^T in registers: dP - dvec = dO V^T - dvec (the product
+//          starts from the rows' negated dvec), dS = P (dP - dvec),
 //          dK += dS^T Q, one query tile behind role 0 (it reads the P that
 //          role 0 wrote before the previous barrier).
 // Each wavefront then holds one key-side operand and one accumulator pair
@@ -635,6 +643,7 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
             float LDS_AS *lp =
                 (float LDS_AS *)((char LDS_AS *)g_kv + kSOff + stage * 2 * kStatBytes);
             lp[lane] = lp[lane] * kLog2e;
+            lp[64 + lane] = -lp[64 + lane];     // dvec negated: the dP product's input
         };
         if (n_iter > 0) {
             wait_tiles(min(kKvAhead - 1, n_iter - 1));
@@ -791,7 +800,12 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
                         }
                         issue_next();
                         __builtin_amdgcn_sched_barrier(0);
-                        f32x16 dp = f32x16{};
+                        // dP - dvec directly: the product's accumulator input is
+                        // the rows' negated dvec (negated in LDS with the lse)
+                        f32x16 dp;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            dp[i] = d4s[i >> 2][i & 3];
 #pragma unroll
                         for (int sd = 0; sd < 8; ++sd)
                             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[sd], kv[sd], dp, 0, 0,
@@ -808,11 +822,10 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
 #pragma unroll
                         for (int i4 = 0; i4 < 4; ++i4) {
                             const f32x4 p4 = p4s[i4];
-                            const f32x4 d4 = d4s[i4];
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
                                 const int i = 4 * i4 + e;
-                                sf[i >> 3][i & 7] = (__bf16)(p4[e] * (dp[i] - d4[e]));
+                                sf[i >> 3][i & 7] = (__bf16)(p4[e] * dp[i]);
                             }
                         }
                         // dK += dS^T Q
