@@ -790,14 +790,18 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
                         const char LDS_AS *vt = lds + st_prev * 2 * kStatBytes;
                         bf16x8 da[8];
                         f32x4 p4s[4], d4s[4];
+                        // in the order of use: the product's accumulator input,
+                        // its operands, then P, so the first product waits on
+                        // five reads rather than all sixteen
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4)
+                            d4s[i4] = *(const f32x4 LDS_AS *)(vt + i4 * 32 + statb);
 #pragma unroll
                         for (int sd = 0; sd < 8; ++sd)
                             da[sd] = lds_b128(lds + so_prev, rowb[sd]);
 #pragma unroll
-                        for (int i4 = 0; i4 < 4; ++i4) {
+                        for (int i4 = 0; i4 < 4; ++i4)
                             p4s[i4] = *(const f32x4 LDS_AS *)(pr + i4 * 1024 + pl);
-                            d4s[i4] = *(const f32x4 LDS_AS *)(vt + i4 * 32 + statb);
-                        }
                         issue_next();
                         __builtin_amdgcn_sched_barrier(0);
                         // dP - dvec directly: the product's accumulator input is
