@@ -479,16 +479,17 @@ constexpr int kKvLoads = 2 * (kTileRows / 4) / kKvWaves;   // tile loads per wav
 constexpr int kKvLoads0 = kKvLoads + 2;                     // wavefront 0 also loads lse, dvec
 static_assert(kKvLoads == 2, "one q and one dout block per wavefront and tile");
 
-// Work of the dk/dv launch: `units` per KV head, each one key tile or (under
-// the causal mask) the pair of key tiles t and n_key_tiles - 1 - t, whose
-// visible query rows add up to about the same count for every t.  The
-// units of all KV heads, head-major, are cut into 8 contiguous runs of
-// `per_xcd`, one per XCD (workgroup b runs on XCD b % 8), so the workgroups
-// an XCD holds at a time belong to one KV head and read the same query
-// tiles.
+// Work of one block's dk/dv: `units` per KV head, each one key tile or
+// (under the causal mask) the pair of key tiles t and n_key_tiles - 1 - t,
+// whose visible query rows add up to about the same count for every t.
+// A launch takes the units of all KV heads, head-major (with two blocks in
+// one launch, the first block's units, then the second's), cut into 8
+// contiguous runs of `per_xcd`, one per XCD (workgroup b runs on XCD b % 8),
+// so the workgroups an XCD holds at a time belong to one KV head and read
+// the same query tiles.
 struct KvWork {
     int units;        // units per KV head
-    int per_xcd;      // units per XCD
+    int per_xcd;      // units per XCD (of the launch)
     int paired;       // 1: a unit is a pair of key tiles
     int n_key_tiles;
 };
@@ -496,8 +497,12 @@ struct KvWork {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
+// kBlocks = 2: two blocks whose dk/dv rows are disjoint in one launch (a
+// causal block of few KV heads has fewer key-tile pairs than the chip has
+// CUs; two of them fill it); the second block's arguments are b1, w1.
+template <int kBlocks>
 __global__ __launch_bounds__(kKvThreads, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
+void bwd_dkdv_kernel(BwdLaunch b, KvWork w, BwdLaunch b1, KvWork w1)
 {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -507,8 +512,19 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
     int g, tiles[2], n_phase;
     {
         const int x = blockIdx.x % 8, slot = blockIdx.x / 8;
-        const int64_t lin = (int64_t)x * w.per_xcd + slot;
-        if (slot >= w.per_xcd || lin >= (int64_t)w.units * b.Hkv)
+        int64_t lin = (int64_t)x * w.per_xcd + slot;
+        int64_t n_units = (int64_t)w.units * b.Hkv;
+        if constexpr (kBlocks == 2) {
+            if (lin >= n_units) {
+                lin -= n_units;
+                const int per_xcd = w.per_xcd;
+                b = b1;
+                w = w1;
+                w.per_xcd = per_xcd;
+                n_units = (int64_t)w.units * b.Hkv;
+            }
+        }
+        if (slot >= w.per_xcd || lin >= n_units)
             return;
         g = (int)(lin / w.units);
         const int u = (int)(lin % w.units);
@@ -899,9 +915,18 @@ void bwd_dkdv_kernel(BwdLaunch b, KvWork w)
     }
 }
 
+KvWork kv_work(const BwdLaunch &b)
+{
+    KvWork w{};
+    w.n_key_tiles = (int)((b.Sk + kKvRows - 1) / kKvRows);
+    w.paired = b.causal && w.n_key_tiles > 1 ? 1 : 0;
+    w.units = w.paired ? (w.n_key_tiles + 1) / 2 : w.n_key_tiles;
+    return w;
+}
+
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdLaunch &b, hipStream_t stream)
+hipError_t launch_bwd_bf16_dq(const BwdLaunch &b, hipStream_t stream)
 {
     if (b.Sq > 0) {
         DqWork w{};
@@ -917,21 +942,50 @@ hipError_t launch_bwd_bf16(const BwdLaunch &b, hipStream_t stream)
         }
         hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)grid), dim3(kDqThreads), 0, stream, b,
                            w);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
-    if (b.Sk > 0) {
-        KvWork w{};
-        w.n_key_tiles = (int)((b.Sk + kKvRows - 1) / kKvRows);
-        w.paired = b.causal && w.n_key_tiles > 1 ? 1 : 0;
-        w.units = w.paired ? (w.n_key_tiles + 1) / 2 : w.n_key_tiles;
-        const int64_t total = (int64_t)w.units * b.Hkv;
-        w.per_xcd = (int)((total + 7) / 8);
-        hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)(8 * (int64_t)w.per_xcd)),
-                           dim3(kKvThreads), 0, stream, b, w);
     }
     return hipGetLastError();
+}
+
+int64_t bwd_bf16_dkdv_units(const BwdLaunch &b)
+{
+    if (b.Sk <= 0)
+        return 0;
+    return (int64_t)kv_work(b).units * b.Hkv;
+}
+
+hipError_t launch_bwd_bf16_dkdv(const BwdLaunch *bs, int n, hipStream_t stream)
+{
+    if (n < 1 || n > 2)
+        return hipErrorInvalidValue;
+    // blocks without key rows write nothing
+    const BwdLaunch *live[2];
+    int nl = 0;
+    for (int m = 0; m < n; ++m)
+        if (bs[m].Sk > 0)
+            live[nl++] = &bs[m];
+    if (nl == 0)
+        return hipGetLastError();
+    KvWork w0 = kv_work(*live[0]);
+    KvWork w1 = nl == 2 ? kv_work(*live[1]) : KvWork{};
+    const int64_t total = (int64_t)w0.units * live[0]->Hkv +
+                          (nl == 2 ? (int64_t)w1.units * live[1]->Hkv : 0);
+    w0.per_xcd = (int)((total + 7) / 8);
+    const dim3 grid((unsigned)(8 * (int64_t)w0.per_xcd));
+    if (nl == 1)
+        hipLaunchKernelGGL(bwd_dkdv_kernel<1>, grid, dim3(kKvThreads), 0, stream, *live[0], w0,
+                           BwdLaunch{}, KvWork{});
+    else
+        hipLaunchKernelGGL(bwd_dkdv_kernel<2>, grid, dim3(kKvThreads), 0, stream, *live[0], w0,
+                           *live[1], w1);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const BwdLaunch &b, hipStream_t stream)
+{
+    const hipError_t e = launch_bwd_bf16_dq(b, stream);
+    if (e != hipSuccess)
+        return e;
+    return launch_bwd_bf16_dkdv(&b, 1, stream);
 }
 
 }  // namespace cpattn

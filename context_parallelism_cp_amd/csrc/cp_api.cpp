@@ -719,8 +719,62 @@ int ring_bwd_check(const void *q, const void *k, const void *v, const float *out
     return CP_OK;
 }
 
+// The bf16 launches of one ring step's computed pairs: per pair its dq
+// launch, then its dk/dv launch, except that two pairs whose dk/dv launches
+// would each hold fewer workgroups than the chip has CUs (the causal
+// diagonal blocks of few KV heads) share one dk/dv launch when their dk/dv
+// rows are disjoint; that launch follows the second pair's dq launch.  A
+// pair goes into no dk/dv launch before one holding an earlier pair that
+// writes the same rows, so every row still accumulates its pairs in pair
+// order: the same sums, in the same order, as one launch per pair.
+constexpr int64_t kChipCUs = 256;
+int launch_bwd_bf16_step(const BwdLaunch *bl, int nb, int Hkv, int D, hipStream_t st)
+{
+    int rc;
+    int member[4][2], n_members[4], n_launch = 0, launch_of[4];
+    for (int i = 0; i < nb; ++i) {
+        int first = 0;      // launches before this one hold a pair writing its rows
+        const size_t bi = (size_t)bl[i].Sk * Hkv * D * 4;
+        for (int j = 0; j < i; ++j)
+            if (overlaps(bl[i].dk, bi, bl[j].dk, (size_t)bl[j].Sk * Hkv * D * 4))
+                first = std::max(first, launch_of[j] + 1);
+        int L = n_launch;
+        if (bwd_bf16_dkdv_units(bl[i]) < kChipCUs)
+            for (int l = first; l < n_launch; ++l)
+                if (n_members[l] == 1 && bwd_bf16_dkdv_units(bl[member[l][0]]) < kChipCUs) {
+                    L = l;
+                    break;
+                }
+        if (L == n_launch)
+            n_members[n_launch++] = 0;
+        member[L][n_members[L]++] = i;
+        launch_of[i] = L;
+    }
+    // per pair: its dq launch, then the dk/dv launches (in order) whose
+    // pairs have all had their dq launch
+    int next = 0;
+    for (int i = 0; i < nb; ++i) {
+        rc = timed_launch(CP_KERNEL_BWD_BF16, st, [&] {
+            hipError_t e = launch_bwd_bf16_dq(bl[i], st);
+            for (; e == hipSuccess && next < n_launch; ++next) {
+                if (member[next][n_members[next] - 1] > i)
+                    break;
+                BwdLaunch two[2];
+                for (int m = 0; m < n_members[next]; ++m)
+                    two[m] = bl[member[next][m]];
+                e = launch_bwd_bf16_dkdv(two, n_members[next], st);
+            }
+            return e;
+        });
+        if (rc)
+            return rc;
+    }
+    return CP_OK;
+}
+
 // The ring backward's launches, after ring_bwd_check: dvec of the output
-// rows, zeroed gradients, then one dq + dk/dv launch pair per computed pair.
+// rows, zeroed gradients, then per ring step the dq and dk/dv launches of
+// its computed pairs.
 int ring_bwd_run(const void *q, const void *k, const void *v, const float *out,
                  const float *lse, const void *dout, float *dq, float *dk, float *dv,
                  float *dvec, int64_t S, int Hq, int Hkv, int D, int P, cp_layout layout,
@@ -745,6 +799,8 @@ int ring_bwd_run(const void *q, const void *k, const void *v, const float *out,
             const int src = ((r - t) % P + P) % P;
             RingPair rp[4];
             const int m = ring_step_pairs(layout, S, P, r, src, causal, rp);
+            BwdLaunch bl[4];
+            int nb = 0;
             for (int i = 0; i < m; ++i) {
                 const RingPair &p = rp[i];
                 if (p.kind == CP_PAIR_SKIP)
@@ -770,9 +826,15 @@ int ring_bwd_run(const void *q, const void *k, const void *v, const float *out,
                 b.accumulate = 1;
                 b.q_offset = p.q_pos;
                 b.k_offset = p.k_pos;
-                if ((rc = launch_bwd(b, dtype, st)))
-                    return rc;
+                if (dtype != CP_BF16) {
+                    if ((rc = launch_bwd(b, dtype, st)))
+                        return rc;
+                    continue;
+                }
+                bl[nb++] = b;
             }
+            if ((rc = launch_bwd_bf16_step(bl, nb, Hkv, D, st)))
+                return rc;
         }
     return CP_OK;
 }

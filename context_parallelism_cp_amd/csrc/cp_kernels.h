@@ -104,6 +104,13 @@ hipError_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
 hipError_t launch_fill_2d(float *p, int64_t ld, int64_t n_rows, int64_t n_cols, float value,
                           hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdLaunch &b, hipStream_t stream);
+// The two halves of launch_bwd_bf16: dq of one block; dk/dv of n blocks
+// (n = 1 or 2) in one launch, which requires their dk and dv rows to be
+// disjoint (the blocks' units run concurrently).
+hipError_t launch_bwd_bf16_dq(const BwdLaunch &b, hipStream_t stream);
+hipError_t launch_bwd_bf16_dkdv(const BwdLaunch *bs, int n, hipStream_t stream);
+// Workgroups (key-tile units) of one block's dk/dv launch.
+int64_t bwd_bf16_dkdv_units(const BwdLaunch &b);
 
 // The library's device scratch array (16 MiB of floats per GPU, held from
 // the code object's load until the process ends): *ptr receives its address
