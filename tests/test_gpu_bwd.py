@@ -292,6 +292,50 @@ def test_bf16_ring_bwd_4k(layout):
                       rel=True)
 
 
+@pytest.mark.parametrize("rank", [0, 1])
+def test_bf16_ring_bwd_shared_launch_matches_per_pair(rank):
+    """Ring backward of a zigzag rank share whose diagonal blocks are small
+    (16384 tokens, P = 2, 4 query heads on 1 KV head: 16 key-tile pairs per
+    diagonal block, fewer than the chip's CUs), so their dk/dv work shares
+    one launch: the gradients must equal, bit for bit, those of one
+    cp_attn_block_bwd call per computed pair in the plan's order (each
+    accumulating into the same buffers)."""
+    S, Hq, Hkv, P, D = 16384, 4, 1, 2, 128
+    C = S // (2 * P)
+    announce(f"bf16 ring bwd shared dk/dv launch S={S} Hq={Hq} Hkv={Hkv} P={P} rank {rank}")
+    q, k, v = make_qkv(S=S, H=Hq, D=D, seed=31, dtype=torch.bfloat16, Hkv=Hkv)
+    dout, _, _ = make_qkv(S=S, H=Hq, D=D, seed=32, dtype=torch.bfloat16)
+    qd, kd, vd, dd = ring_inputs_for("zigzag", S, P, rank, q, k, v, dout)
+    out, lse = cp.cp_ring_fwd(qd, kd, vd, P, "zigzag", rank)
+    dq, dk, dv = cp.cp_ring_bwd(qd, kd, vd, out, lse, dd, P, "zigzag", rank)
+    # the same pairs, one block backward each, in the plan's order
+    dvec = cp.cp_attn_bwd_dvec(out, dd)
+    rows = S // P
+    pdq = torch.zeros(rows, Hq, D, device=DEV)
+    pdk = torch.zeros(S, Hkv, D, device=DEV)
+    pdv = torch.zeros(S, Hkv, D, device=DEV)
+    local = {rank: 0, 2 * P - 1 - rank: C}          # zigzag: chunk -> local row
+    n_diag = 0
+    for (_, _, qc, kc, q_off, k_off, len_q, len_k, kind) in cp.cp_ring_plan(S, P, "zigzag", rank):
+        if kind == cp.CP_PAIR_SKIP:
+            continue
+        n_diag += kind == cp.CP_PAIR_DIAG
+        o = local[qc]
+        cp.cp_attn_block_bwd(qd[q_off:q_off + len_q], kd[k_off:k_off + len_k],
+                             vd[k_off:k_off + len_k], dd[o:o + len_q],
+                             lse[:, o:o + len_q].contiguous(), dvec[:, o:o + len_q].contiguous(),
+                             pdq[o:o + len_q], pdk[k_off:k_off + len_k], pdv[k_off:k_off + len_k],
+                             q_offset=q_off, k_offset=k_off, causal=kind == cp.CP_PAIR_DIAG,
+                             accumulate=True)
+    torch.cuda.synchronize()
+    assert n_diag == 2
+    for name, a, b in (("dq", dq, pdq), ("dk", dk, pdk), ("dv", dv, pdv)):
+        assert not torch.isnan(a).any(), name
+        diff = (a != b).sum().item()
+        print(f"    {name}: {diff} elements differ", flush=True)
+        assert diff == 0, f"{name}: {diff} elements differ"
+
+
 def test_bf16_block_bwd_16k_sampled_rows():
     """16384 tokens, 8 query heads on 2 KV heads: sampled dq rows and dk/dv
     rows recomputed one by one by the C oracle."""
