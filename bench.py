@@ -23,12 +23,13 @@ The CPU oracle is timed on a bounded sample of the ring share's rows.
 instead (striped: q, k, v permuted to striped order once, before timing);
 ``--part ring|ulysses|bwd|usp|usp_bwd`` times one share, the backward pass,
 or one rank of the USP hybrid (8-way Ulysses x 2-way ring), forward or
-backward; ``--part merge|repack`` times the bandwidth-bound kernels alone
+backward; ``--part block`` the whole sequence as one causal block
+(``cp_attn_block_fwd`` on [131072, 32, 128]); ``--part merge|repack`` times the bandwidth-bound kernels alone
 (the log-sum-exp merges of a ring rank run as separate kernels, the Ulysses
 repacks of a rank) in GB/s against the HBM peak.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--part both|ring|ulysses|bwd|usp|usp_bwd|merge|repack]
+                    [--part both|ring|ulysses|bwd|usp|usp_bwd|merge|repack|block]
                     [--merge-in-place]
                     [--layout zigzag|striped|contiguous]
                     [--rank r]
@@ -485,6 +486,70 @@ def usp(args, cp, torch, dq, dku, dvu, stream):
     print(json.dumps(result))
 
 
+def block(args, cp, torch, dq, dk, dv, stream):
+    """The whole 128K-token layer as one causal block (one JSON line):
+    cp_attn_block_fwd of q, k, v bf16 [131072, 32, 128] (32 query heads on
+    32 KV heads) into float32 out and lse, the shape the single-GPU kernel
+    target names.  FLOP: 4*D*H per visible pair with the diagonal block
+    counted half, 2^47 per step."""
+    dev = "cuda:0"
+    out = torch.empty(S, HQ, D, device=dev, dtype=torch.float32)
+    lse = torch.empty(HQ, S, device=dev, dtype=torch.float32)
+
+    def step():
+        cp.cp_attn_block_fwd(dq, dk, dv, out, lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    cp.cp_timing_enable(True)
+    cp.cp_timing_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    attn_ms, attn_n = cp.cp_timing_read(cp.CP_KERNEL_ATTN_BF16)
+    cp.cp_timing_enable(False)
+    flop_step = 4.0 * D * HQ * S * S / 2.0
+    kern = flop_step * args.steps / (attn_ms * 1e-3) / 1e12 if attn_ms > 0 else None
+    result = {
+        "metric": "causal block-attn fwd TFLOP/s + % bf16 MFMA peak, one block S=128K H=32 D=128",
+        "value": round(flop_step * args.steps / elapsed / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("one causal block over the whole sequence: cp_attn_block_fwd of "
+                         "q, k, v bf16 [131072, 32, 128] (Hq=Hkv=32, D=128), fp32 out + lse"),
+            "parts": "block",
+            "S": S, "Hq": HQ, "Hkv": HQ, "D": D,
+            "flop_per_step": flop_step,
+            "flop_convention": "4*D*Hq per visible (q,k) pair, diagonal block counted half",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_bf16_kernel",
+            "achieved": round(kern, 2) if kern else None,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(kern / PEAK_BF16_TFLOPS, 4) if kern else None,
+            "traffic": None,
+            "launches": attn_n,
+            "avg_launch_ms": round(attn_ms / max(attn_n, 1), 4),
+        },
+    }
+    print(json.dumps(result))
+
+
 def rank_sweep(args, cp, torch, dq, dk, dv, stream, seq, RP):
     """Every rank's share of one ring, timed rank by rank (one JSON line):
     q, k, v bf16 [seq, 32, 128] (the first seq rows of the inputs; default
@@ -683,11 +748,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--part", choices=["both", "ring", "ulysses", "bwd", "usp", "usp_bwd",
-                                       "merge", "repack", "ranks"],
+                                       "merge", "repack", "ranks", "block"],
                     default="both",
                     help="bwd: time the backward pass of both shares instead; usp: one rank "
                          "of the 8-way Ulysses x 2-way ring hybrid; merge / repack: the "
-                         "bandwidth-bound kernels alone (GB/s against the HBM peak)")
+                         "bandwidth-bound kernels alone (GB/s against the HBM peak); block: "
+                         "the whole sequence as one causal block on one GPU")
     ap.add_argument("--merge-in-place", action="store_true",
                     help="--part merge: fold into the running output in place")
     ap.add_argument("--layout", choices=["zigzag", "striped", "contiguous"], default="zigzag",
@@ -794,6 +860,9 @@ def main():
 
     if args.part == "usp":
         usp(args, cp, torch, dq, dku, dvu, stream)
+        return
+    if args.part == "block":
+        block(args, cp, torch, dq, dk, dv, stream)
         return
     if args.part == "ranks":
         rank_sweep(args, cp, torch, dq, dk, dv, stream, args.seq, RP)

@@ -504,6 +504,25 @@ def test_full_ulysses_gqa_128k():
     np.testing.assert_allclose(ro_all[:, 4 * p:4 * p + 4], ro[:4], atol=1e-12)
 
 
+def test_full_block_128k_32_heads():
+    """The whole 131072-token sequence as one causal block on 32 heads (the
+    launch `bench.py --part block` times): sampled rows -- the edges of
+    every 16384-row stretch and random ones -- against the C oracle."""
+    S, H = 131072, 32
+    announce(f"one causal block S={S} H={H} (sampled rows)")
+    q, k, v = inputs_cached(S, H, H)
+    dq, dk, dv = dev(q, k, v)
+    out, lse = Guarded(S, H, 128), Guarded(H, S)
+    cp.cp_attn_block_fwd(dq, dk, dv, out.t, lse.t)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    rows = chunk_edge_rows(S, 16384, 16, seed=11)
+    ro, rl = oracle_rows(q, k, v, rows)
+    idx = torch.from_numpy(rows).to(DEV)
+    compare(out.t[idx].double().cpu().numpy(), lse.t[:, idx].double().cpu().numpy(), ro, rl,
+            BF16_OUT_TOL, BF16_LSE_TOL, "one causal block 128K x 32 heads")
+
+
 def test_ulysses_16way_with_kv_replication():
     """The handbook exercise's 16-way Ulysses on 32 query heads and 8 KV heads:
     KV heads copied to two ranks each (bit-exact), every rank's local
