@@ -727,7 +727,7 @@ int ring_bwd_check(const void *q, const void *k, const void *v, const float *out
 // pair goes into no dk/dv launch before one holding an earlier pair that
 // writes the same rows, so every row still accumulates its pairs in pair
 // order: the same sums, in the same order, as one launch per pair.
-constexpr int64_t kChipCUs = 256;
+constexpr int64_t kChipCUs = 256;   // MI355X: 8 XCDs x 32 CUs
 int launch_bwd_bf16_step(const BwdLaunch *bl, int nb, int Hkv, int D, hipStream_t st)
 {
     int rc;
