@@ -103,6 +103,8 @@ def ulysses_share_flop(S, H_local, D):
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_128k_rank_share_hbm_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "context_parallelism_cp_amd", "csrc", "attn_bf16.hip")
 BWD_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bwd_128k_rank_share_hbm_traffic.md")
+BLOCK_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
+                                     "attn_bf16_128k_single_block_32h_hbm_traffic.md")
 BWD_KERNEL_SOURCE = os.path.join(ROOT, "context_parallelism_cp_amd", "csrc", "bwd_bf16.hip")
 
 
@@ -542,7 +544,10 @@ def block(args, cp, torch, dq, dk, dv, stream):
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(kern / PEAK_BF16_TFLOPS, 4) if kern else None,
-            "traffic": None,
+            "traffic": recorded_traffic(BLOCK_TRAFFIC_PROFILE, KERNEL_SOURCE,
+                                        workload_key("block", args.layout, args.rank, args.seq,
+                                                     args.ring_p)),
+            "traffic_unit": "bytes per launch (HBM read + write, calibrated)",
             "launches": attn_n,
             "avg_launch_ms": round(attn_ms / max(attn_n, 1), 4),
         },
