@@ -31,12 +31,15 @@ pytestmark = pytest.mark.gpu
 F32_GRAD_TOL = 2e-5
 
 
-def grads_compare(got, want, tol, what, rel=False):
+def grads_compare(got, want, tol, what, rel=False, scale_floor=0.0):
+    """Max abs error of dq, dk, dv against the reference: at most tol, or
+    (rel) tol times the largest reference magnitude of the tensor, or of
+    scale_floor when that is larger."""
     for name, g, w in zip(("dq", "dk", "dv"), got, want):
         g = g.detach().double().cpu().numpy() if torch.is_tensor(g) else g
         assert not np.isnan(g).any(), f"{what} {name}: NaN"
         err = float(np.abs(g - w).max()) if g.size else 0.0
-        scale = float(np.abs(w).max()) if (rel and w.size) else 1.0
+        scale = max(float(np.abs(w).max()), scale_floor) if (rel and w.size) else 1.0
         print(f"    {what} {name}: max|err| = {err:.3e} (ref max {np.abs(w).max() if w.size else 0:.3e})",
               flush=True)
         assert err <= tol * max(scale, 1e-30), f"{what} {name}: error {err}"
@@ -230,6 +233,30 @@ def test_bf16_block_bwd(Sq, Sk, Hq, Hkv, qo, ko, causal):
     got = run_block_bwd(q, k, v, dout, qo, ko, causal)
     grads_compare(got, oracle_grads(q, k, v, dout, qo, ko, causal), BF16_GRAD_REL, "bf16 block",
                   rel=True)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_bf16_block_bwd_random_shapes(case):
+    """Seeded random block shapes (lengths off the tile sizes, GQA ratios
+    1, 2, 3, 4, 8, offsets in either order, causal or not) against the
+    float64 oracle backward.  A tensor whose exact value is zero (one
+    visible key per row: P = 1, so dP = Dv and dS = 0) comes out as the
+    rounding residue of dP - Dv, so the relative bound is taken against the
+    largest gradient magnitude of the block (dv = P^T dout is not zero)."""
+    rng = np.random.default_rng(5000 + case)
+    Hkv = int(rng.choice([1, 2]))
+    Hq = Hkv * int(rng.choice([1, 2, 3, 4, 8 // Hkv]))
+    Sq, Sk = int(rng.integers(1, 401)), int(rng.integers(1, 401))
+    qo, ko = int(rng.integers(0, 800)), int(rng.integers(0, 800))
+    causal = bool(rng.integers(0, 2))
+    announce(f"bf16 block bwd random case {case}: Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} "
+             f"qo={qo} ko={ko} causal={causal}")
+    q, k, v, dout = inputs(Sq, Sk, Hq, Hkv, 128, torch.bfloat16, 6000 + case)
+    got = run_block_bwd(q, k, v, dout, qo, ko, causal)
+    want = oracle_grads(q, k, v, dout, qo, ko, causal)
+    floor = max(float(np.abs(w).max()) if w.size else 0.0 for w in want)
+    grads_compare(got, want, BF16_GRAD_REL, f"bf16 block bwd random {case}", rel=True,
+                  scale_floor=floor)
 
 
 def test_bf16_block_bwd_accumulate_and_empty():

@@ -292,6 +292,33 @@ def test_bf16_block_small(Sq, Sk, Hq, Hkv, qo, ko, causal):
     compare(out.t, lse.t, ro, rl, BF16_OUT_TOL, BF16_LSE_TOL, "bf16 block")
 
 
+def random_block_case(case):
+    """Seeded random block shape: lengths that need not fill a tile, GQA
+    ratios that pack into a workgroup (1, 2, 4, 8) and ones that do not (3,
+    16), offsets in either order, causal or not."""
+    rng = np.random.default_rng(1000 + case)
+    Hkv = int(rng.choice([1, 2]))
+    group = int(rng.choice([1, 2, 3, 4, 8, 16 // Hkv]))
+    Sq, Sk = int(rng.integers(1, 521)), int(rng.integers(1, 601))
+    qo, ko = int(rng.integers(0, 1200)), int(rng.integers(0, 1200))
+    return Sq, Sk, Hkv * group, Hkv, qo, ko, bool(rng.integers(0, 2))
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_bf16_block_random_shapes(case):
+    Sq, Sk, Hq, Hkv, qo, ko, causal = random_block_case(case)
+    announce(f"bf16 block fwd random case {case}: Sq={Sq} Sk={Sk} Hq={Hq} Hkv={Hkv} "
+             f"qo={qo} ko={ko} causal={causal}")
+    q, _, _ = make_qkv(S=Sq, H=Hq, D=128, seed=2000 + case, dtype=torch.bfloat16)
+    _, k, v = make_qkv(S=Sk, H=Hkv, D=128, seed=3000 + case, dtype=torch.bfloat16)
+    out, lse = Guarded(Sq, Hq, 128), Guarded(Hq, Sq)
+    cp.cp_attn_block_fwd(*dev(q, k, v), out.t, lse.t, q_offset=qo, k_offset=ko, causal=causal)
+    torch.cuda.synchronize()
+    out.check(), lse.check()
+    ro, rl = oracle_rows(q, k, v, None, causal=causal, q_offset=qo, k_offset=ko)
+    compare(out.t, lse.t, ro, rl, BF16_OUT_TOL, BF16_LSE_TOL, f"bf16 block random {case}")
+
+
 def score_dynamics_inputs(kind, Sq, Sk, H, seed):
     """bf16 q, k, v whose scores stress the running max of the streaming
     softmax: "growing" -- key norms rise along the sequence, so a row's max
