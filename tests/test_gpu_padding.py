@@ -212,3 +212,39 @@ def test_bf16_padded_ring_bwd(layout):
         got = run_padded_bwd(q, k, v, dout, P, layout, rank, True, S)
         want = rank_bwd_oracle(q, k, v, dout, P, layout, rank, True)
         grads_compare(got, want, BF16_GRAD_REL, f"{layout} rank {rank}", rel=True)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_bf16_ring_random_shapes(case):
+    """Seeded random ring calls: 2-5 ranks, any layout, one rank's share or
+    every rank, lengths the split may or may not divide (200-3000 tokens),
+    GQA ratios 1, 2, 4, causal or not; the forward against the single pass
+    and the backward against the oracle's composition over the plan (the
+    relative bound as in the random block sweep: against the largest
+    gradient magnitude of the call when a tensor's own is smaller)."""
+    rng = np.random.default_rng(7000 + case)
+    P = int(rng.integers(2, 6))
+    layout = str(rng.choice(LAYOUTS))
+    S = int(rng.integers(200, 3001))
+    Hkv = int(rng.choice([1, 2]))
+    Hq = Hkv * int(rng.choice([1, 2, 4]))
+    rank = int(rng.integers(-1, P))
+    causal = bool(rng.integers(0, 2))
+    announce(f"bf16 ring random case {case}: S={S} Hq={Hq} Hkv={Hkv} P={P} {layout} "
+             f"rank {rank} causal={causal}")
+    q, k, v = make_qkv(S=S, H=Hq, D=128, seed=8000 + case, dtype=torch.bfloat16, Hkv=Hkv)
+    dout = make_qkv(S=S, H=Hq, D=128, seed=9000 + case, dtype=torch.bfloat16)[0]
+    ro, rl = oracle_rows(q, k, v, None, causal=causal)
+    ipos = input_positions(layout, S, P)
+    opos = out_positions(layout, S, P, rank)
+    qd, kd, vd = (to_input(x, ipos, S) for x in (q, k, v))
+    out, lse = cp.cp_ring_fwd(qd, kd, vd, P, layout, rank, causal=causal, seq_len=S)
+    torch.cuda.synchronize()
+    wo, wl = expected(ro, rl, opos, S)
+    compare(out, lse, wo, wl, BF16_OUT_TOL, BF16_LSE_TOL, f"ring random {case} fwd")
+    got = run_padded_bwd(q, k, v, dout, P, layout, rank, causal, S)
+    want = rank_bwd_oracle(q, k, v, dout, P, layout, rank, causal)
+    floor = max(float(np.abs(w).max()) if w.size else 0.0 for w in want)
+    grads_compare(got, want, BF16_GRAD_REL, f"ring random {case} bwd", rel=True,
+                  scale_floor=floor)
+
